@@ -1,0 +1,255 @@
+"""Seeded synthetic inputs for the table-batched embedding (TBE) workloads.
+
+This module only draws inputs. It holds none of the method's arithmetic: no
+pooling, no sort, no run-length encoding, no optimizer. Both the HIP path's
+tests/benchmark and the CPU oracle take their inputs from here, so the same
+seed gives the same batch on either side.
+
+Workload shapes follow the FBTriton TBE tutorial (page 1, "Notation": T tables,
+E rows, D columns, L bag size, B bags per table; the large-scenario statistics
+of about 83M lookups, 3M unique rows and a hottest row near 125K lookups at
+T*B = 4.2M, B = 128K) and the TorchEasyRec article (page 2, section 2: the
+three demo tables of 1,141,730 / 461,498 / 846,812 rows).
+
+Layout (the boundary's layout, table-major jagged like a KeyedJaggedTensor's
+values/lengths):
+  indices  int32 [N]        row index inside its own table
+  offsets  int32 [T*B + 1]  bag i = t*B + b covers indices[offsets[i]:offsets[i+1]]
+  psw      float32 [N] or None (per-sample weights)
+  grad     float32 [B, T*D] upstream gradient of the pooled output; table t
+           owns columns t*D .. t*D+D-1
+  W        [sum(E), D] weights, tables stacked in order; dtype f32/f16/bf16
+  m        float32 [sum(E)] row-wise Adagrad state
+
+Weights and optimizer state are not drawn from the numpy stream: every element
+comes from a counter-based integer hash of (seed, row key, column), so any row
+can be regenerated on the host or the device without materialising the table
+(the config with 64M rows holds 16 GiB of weights).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["Config", "CONFIGS", "Batch", "make_batch", "weight_rows",
+           "full_weights", "state_rows", "full_state", "table_offsets"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    T: int
+    B: int
+    D: int
+    rows: tuple            # E_t per table
+    dtype: str             # "f32" | "f16" | "bf16"
+    bag: tuple             # ("fixed", L) | ("uniform", lo, hi) per table | ("poisson", mean)
+    index: tuple           # ("uniform",) | ("zipf", alpha) | ("zipf_mandelbrot", alpha, q)
+    weighted: bool
+    preprocess_in_forward: bool
+    seed: int
+    lr: float = 0.01
+    eps: float = 1e-8
+    bag_per_table: Optional[tuple] = None   # overrides `bag` per table when set
+
+    @property
+    def sum_rows(self) -> int:
+        return int(sum(self.rows))
+
+
+# The five workloads. Shapes and distributions restate the benchmark's configs;
+# where they leave a detail open (weight init, lr/eps for configs 2-5, the
+# Zipf family for config 4) the choice is recorded in the design doc.
+CONFIGS = {
+    1: Config("tiny", T=2, B=64, D=16, rows=(1000, 1000), dtype="f32",
+              bag=("fixed", 4), index=("uniform",), weighted=False,
+              preprocess_in_forward=False, seed=1),
+    2: Config("demo3", T=3, B=4096, D=16, rows=(1141730, 461498, 846812),
+              dtype="f32", bag=("fixed", 1), index=("zipf", 1.1), weighted=False,
+              preprocess_in_forward=False, seed=2,
+              bag_per_table=(("fixed", 1), ("uniform", 1, 20), ("uniform", 1, 20))),
+    3: Config("t16_e1m_fp16", T=16, B=16384, D=128, rows=(1_000_000,) * 16,
+              dtype="f16", bag=("poisson", 20.0), index=("zipf", 1.05),
+              weighted=False, preprocess_in_forward=False, seed=3),
+    4: Config("t32_b128k_bf16", T=32, B=131072, D=128, rows=(2_000_000,) * 32,
+              dtype="bf16", bag=("poisson", 20.0),
+              index=("zipf_mandelbrot", 1.404, 7.32), weighted=True,
+              preprocess_in_forward=True, seed=4),
+    5: Config("small_table_fp16", T=64, B=32768, D=128, rows=(64,) * 64,
+              dtype="f16", bag=("fixed", 64), index=("uniform",), weighted=False,
+              preprocess_in_forward=False, seed=5),
+}
+
+
+@dataclasses.dataclass
+class Batch:
+    cfg: Config
+    indices: np.ndarray
+    offsets: np.ndarray
+    psw: Optional[np.ndarray]
+    grad: Optional[np.ndarray]
+
+    @property
+    def N(self) -> int:
+        return int(self.offsets[-1])
+
+
+def table_offsets(rows) -> np.ndarray:
+    """First stacked row of each table (int64 [T]); plain bookkeeping of the
+    stacked weight layout, shared by generator callers."""
+    r = np.asarray(rows, dtype=np.int64)
+    out = np.zeros(len(r), dtype=np.int64)
+    if len(r) > 1:
+        out[1:] = np.cumsum(r)[:-1]
+    return out
+
+
+def _bag_lengths(spec, B, rng) -> np.ndarray:
+    kind = spec[0]
+    if kind == "fixed":
+        return np.full(B, int(spec[1]), dtype=np.int64)
+    if kind == "uniform":
+        return rng.integers(int(spec[1]), int(spec[2]) + 1, size=B, dtype=np.int64)
+    if kind == "poisson":
+        return rng.poisson(float(spec[1]), size=B).astype(np.int64)
+    raise ValueError(f"unknown bag-length spec {spec!r}")
+
+
+def _rank_cdf(spec, E) -> Optional[np.ndarray]:
+    kind = spec[0]
+    if kind == "uniform":
+        return None
+    k = np.arange(1, E + 1, dtype=np.float64)
+    if kind == "zipf":
+        p = k ** (-float(spec[1]))
+    elif kind == "zipf_mandelbrot":
+        p = (k + float(spec[2])) ** (-float(spec[1]))
+    else:
+        raise ValueError(f"unknown index spec {spec!r}")
+    cdf = np.cumsum(p)
+    cdf /= cdf[-1]
+    return cdf
+
+
+def _draw_rows(spec, E, n, rng) -> np.ndarray:
+    """Rows of one table: uniform, or a truncated Zipf-family rank drawn by
+    inverse CDF on [1, E] and mapped to a row through a random permutation."""
+    if spec[0] == "uniform":
+        return rng.integers(0, E, size=n, dtype=np.int64)
+    perm = rng.permutation(E)
+    cdf = _rank_cdf(spec, E)
+    u = rng.random(n)
+    rank = np.searchsorted(cdf, u, side="right")        # 0-based rank
+    np.minimum(rank, E - 1, out=rank)                    # guards u == cdf[-1]
+    return perm[rank]
+
+
+def make_batch(cfg: Config, *, with_grad: bool = True, B: Optional[int] = None,
+               seed: Optional[int] = None) -> Batch:
+    """Draw one batch. Draw order: per table the bag lengths; then per table the
+    permutation and row draws; then per-sample weights; then the upstream
+    gradient. `B` shrinks the batch for quick tests (same distributions)."""
+    B = cfg.B if B is None else int(B)
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    T = cfg.T
+    specs = cfg.bag_per_table or (cfg.bag,) * T
+    lengths = np.empty(T * B, dtype=np.int64)
+    for t in range(T):
+        lengths[t * B:(t + 1) * B] = _bag_lengths(specs[t], B, rng)
+    offsets = np.zeros(T * B + 1, dtype=np.int64)
+    np.cumsum(lengths, out=offsets[1:])
+    N = int(offsets[-1])
+    if N >= 2 ** 31:
+        raise ValueError("batch exceeds int32 offsets")
+    indices = np.empty(N, dtype=np.int32)
+    for t in range(T):
+        a, b = int(offsets[t * B]), int(offsets[(t + 1) * B])
+        indices[a:b] = _draw_rows(cfg.index, int(cfg.rows[t]), b - a, rng)
+    psw = rng.random(N, dtype=np.float32) if cfg.weighted else None
+    grad = None
+    if with_grad:
+        grad = rng.standard_normal((B, T * cfg.D), dtype=np.float32)
+    return Batch(cfg=dataclasses.replace(cfg, B=B), indices=indices,
+                 offsets=offsets.astype(np.int32), psw=psw, grad=grad)
+
+
+# ---------------------------------------------------------------------------
+# Counter-based weights / state. Integer hashing is exact on every device; the
+# final affine map uses two IEEE float32 operations (multiply, subtract), each
+# correctly rounded on CPU and GPU alike, then a round-to-nearest-even cast.
+# ---------------------------------------------------------------------------
+_M32 = 0xFFFFFFFF
+
+
+def _mul32(x, c: int):
+    """(x * c) mod 2^32 for int64 tensors holding values < 2^32, without any
+    intermediate leaving int64 range (split into 16-bit halves)."""
+    lo = x & 0xFFFF
+    hi = x >> 16
+    return ((lo * c) + (((hi * c) & 0xFFFF) << 16)) & _M32
+
+
+def _mix32(x):
+    x = x ^ (x >> 16)
+    x = _mul32(x, 0x7FEB352D)
+    x = x ^ (x >> 15)
+    x = _mul32(x, 0x846CA68B)
+    x = x ^ (x >> 16)
+    return x
+
+
+def _uniform_rows(keys, D: int, salt: int, lo: float, hi: float):
+    import torch
+    keys = keys.to(torch.int64)
+    h1 = _mix32((keys ^ (salt & _M32)) & _M32)
+    cols = torch.arange(D, dtype=torch.int64, device=keys.device)
+    h = _mix32(h1[:, None] ^ _mul32(cols[None, :] + 1, 0x85EBCA6B))
+    u = (h >> 8).to(torch.float32) * (2.0 ** -24)          # exact, in [0, 1)
+    return u * (hi - lo) + lo   # two float32 ops: mul then add, each RNE
+
+
+_TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def weight_rows(cfg: Config, keys, device=None):
+    """Initial weights of the stacked rows `keys` (int tensor), dtype of cfg:
+    U(-0.01, 0.01) in float32, then cast (round to nearest even)."""
+    import torch
+    keys = torch.as_tensor(keys, device=device)
+    w = _uniform_rows(keys, cfg.D, 0x5EED0000 + cfg.seed, -0.01, 0.01)
+    return w.to(getattr(torch, _TORCH_DTYPES[cfg.dtype]))
+
+
+def full_weights(cfg: Config, device, chunk_rows: int = 1 << 20):
+    import torch
+    E = cfg.sum_rows
+    out = torch.empty((E, cfg.D), dtype=getattr(torch, _TORCH_DTYPES[cfg.dtype]),
+                      device=device)
+    for a in range(0, E, chunk_rows):
+        b = min(E, a + chunk_rows)
+        out[a:b] = weight_rows(cfg, torch.arange(a, b, device=device), device)
+    return out
+
+
+def state_rows(cfg: Config, keys, device=None, m0: str = "zeros"):
+    """Initial row-wise Adagrad state: zeros, or U(0, 1) when m0 == "uniform"."""
+    import torch
+    keys = torch.as_tensor(keys, device=device)
+    if m0 == "zeros":
+        return torch.zeros(keys.shape[0], dtype=torch.float32, device=keys.device)
+    u = _uniform_rows(keys, 1, 0xACC00000 + cfg.seed, 0.0, 1.0)
+    return u[:, 0].contiguous()
+
+
+def full_state(cfg: Config, device, m0: str = "zeros", chunk_rows: int = 1 << 22):
+    import torch
+    E = cfg.sum_rows
+    if m0 == "zeros":
+        return torch.zeros(E, dtype=torch.float32, device=device)
+    out = torch.empty(E, dtype=torch.float32, device=device)
+    for a in range(0, E, chunk_rows):
+        b = min(E, a + chunk_rows)
+        out[a:b] = state_rows(cfg, torch.arange(a, b, device=device), device, m0)
+    return out
