@@ -1,0 +1,237 @@
+"""Python binding of the MI355X table-batched embedding library (libtbe.so).
+
+Argument marshalling only: every step of the forward, the transpose (sort +
+run-length encoding + routing) and the backward with row-wise Adagrad runs in
+the library's HIP kernels. The functions carry the C ABI's names
+(include/tbe.h) and take torch tensors, passing their device pointers and the
+current HIP stream. There is no CPU fallback: importing this package fails if
+the library has not been built (python -m bwd_tbe_pooled_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtbe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bwd_tbe_pooled_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# --- C types ----------------------------------------------------------------
+TBE_OK, TBE_ERR_ARG, TBE_ERR_UNSUPPORTED, TBE_ERR_WORKSPACE, TBE_ERR_INDEX_RANGE, TBE_ERR_HIP = range(6)
+TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
+TBE_FLAG_VALIDATE, TBE_FLAG_FORCE_GENERIC = 0x1, 0x2
+TBE_PATH_GENERIC, TBE_PATH_SMALL_TABLE = 0, 1
+(TBE_OP_FORWARD, TBE_OP_FORWARD_PREPROCESS, TBE_OP_PREPROCESS, TBE_OP_BACKWARD,
+ TBE_OP_BACKWARD_SELF) = range(5)
+STAGES = ["fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "bwd_long", "bwd_apply",
+          "small_fwd", "small_bwd", "small_apply", "validate"]
+TBE_NUM_STAGES = len(STAGES)
+META_FIELDS = ["counts", "run_keys", "run_offsets", "sorted_pos", "sorted_bag", "sorted_psw",
+               "short_runs", "long_runs", "long_chunk_begin", "chunk_run", "chunk_start", "hist"]
+TBE_META_NUM_ARRAYS = len(META_FIELDS)
+DTYPE_CODES = {"f32": TBE_F32, "f16": TBE_F16, "bf16": TBE_BF16}
+
+
+class tbe_desc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("rows", ctypes.POINTER(ctypes.c_int64)), ("wdtype", ctypes.c_int),
+                ("short_max", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("flags", ctypes.c_uint32), ("timer", ctypes.c_void_p)]
+
+
+class tbe_meta(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in META_FIELDS]
+
+
+_P = ctypes.c_void_p
+_lib.tbe_status_str.restype = ctypes.c_char_p
+_lib.tbe_status_str.argtypes = [ctypes.c_int]
+_lib.tbe_select_path.restype = ctypes.c_int32
+_lib.tbe_select_path.argtypes = [ctypes.POINTER(tbe_desc), ctypes.c_int64, ctypes.c_int32]
+_lib.tbe_meta_capacity.restype = ctypes.c_int
+_lib.tbe_meta_capacity.argtypes = [ctypes.POINTER(tbe_desc), ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_int64)]
+_lib.tbe_workspace_bytes.restype = ctypes.c_size_t
+_lib.tbe_workspace_bytes.argtypes = [ctypes.POINTER(tbe_desc), ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.c_int]
+_lib.tbe_forward.restype = ctypes.c_int
+_lib.tbe_forward.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, ctypes.c_int64, _P, _P,
+                             ctypes.POINTER(tbe_meta), _P, ctypes.c_size_t, _P]
+_lib.tbe_preprocess.restype = ctypes.c_int
+_lib.tbe_preprocess.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, ctypes.c_int64, _P,
+                                ctypes.POINTER(tbe_meta), _P, ctypes.c_size_t, _P]
+_lib.tbe_backward_adagrad.restype = ctypes.c_int
+_lib.tbe_backward_adagrad.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, _P, _P,
+                                      ctypes.c_int64, _P, ctypes.POINTER(tbe_meta),
+                                      ctypes.c_double, ctypes.c_double, _P, ctypes.c_size_t, _P]
+_lib.tbe_timer_create.restype = ctypes.c_int
+_lib.tbe_timer_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+_lib.tbe_timer_reset.restype = ctypes.c_int
+_lib.tbe_timer_reset.argtypes = [_P]
+_lib.tbe_timer_read.restype = ctypes.c_int
+_lib.tbe_timer_read.argtypes = [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
+_lib.tbe_timer_destroy.restype = None
+_lib.tbe_timer_destroy.argtypes = [_P]
+
+
+class TbeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {tbe_status_str(status)} (status {status})")
+
+
+def tbe_status_str(status: int) -> str:
+    return _lib.tbe_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != TBE_OK:
+        raise TbeError(status, where)
+
+
+# --- description ----------------------------------------------------------------
+class Desc:
+    """Owns a tbe_desc and the host rows array it points to."""
+
+    def __init__(self, T: int, D: int, B: int, rows: Sequence[int], dtype: str,
+                 short_max: int = 0, chunk: int = 0, flags: int = 0, timer: "Timer" = None):
+        self._rows = (ctypes.c_int64 * len(rows))(*[int(r) for r in rows])
+        self.c = tbe_desc(T=int(T), D=int(D), B=int(B),
+                          rows=ctypes.cast(self._rows, ctypes.POINTER(ctypes.c_int64)),
+                          wdtype=DTYPE_CODES[dtype], short_max=int(short_max), chunk=int(chunk),
+                          flags=int(flags), timer=timer.handle if timer else None)
+        self.T, self.D, self.B, self.dtype = int(T), int(D), int(B), dtype
+        self.rows = [int(r) for r in rows]
+
+    def set_timer(self, timer: Optional["Timer"]):
+        self.c.timer = timer.handle if timer else None
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def tbe_select_path(desc: Desc, N: int, weighted: bool) -> int:
+    r = _lib.tbe_select_path(desc.ref, int(N), int(bool(weighted)))
+    if r < 0:
+        raise TbeError(-r, "tbe_select_path")
+    return r
+
+
+def tbe_meta_capacity(desc: Desc, N: int, weighted: bool) -> list:
+    caps = (ctypes.c_int64 * TBE_META_NUM_ARRAYS)()
+    _check(_lib.tbe_meta_capacity(desc.ref, int(N), int(bool(weighted)), caps), "tbe_meta_capacity")
+    return list(caps)
+
+
+def tbe_workspace_bytes(desc: Desc, N: int, weighted: bool, op: int) -> int:
+    return int(_lib.tbe_workspace_bytes(desc.ref, int(N), int(bool(weighted)), int(op)))
+
+
+class Meta:
+    """Device buffers of a tbe_meta, allocated to the library's capacities."""
+
+    def __init__(self, desc: Desc, N: int, weighted: bool, device="cuda"):
+        import torch
+        caps = tbe_meta_capacity(desc, N, weighted)
+        self.caps = dict(zip(META_FIELDS, caps))
+        self.path = tbe_select_path(desc, N, weighted)
+        if self.path == TBE_PATH_SMALL_TABLE:
+            used = {"counts", "hist"}
+        else:
+            used = set(META_FIELDS) - {"hist"} - (set() if weighted else {"sorted_psw"})
+        self.tensors = {}
+        for name in META_FIELDS:
+            if name not in used:
+                continue
+            dt = torch.uint8 if name == "hist" else (torch.float32 if name == "sorted_psw" else torch.int32)
+            # at least one element, so that every array the path uses is non-null
+            self.tensors[name] = torch.empty(max(int(self.caps[name]), 1), dtype=dt, device=device)
+        self.c = tbe_meta(**{n: (t.data_ptr() if t is not None else None)
+                             for n, t in ((n, self.tensors.get(n)) for n in META_FIELDS)})
+
+    def __getitem__(self, name):
+        return self.tensors[name]
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def workspace(desc: Desc, N: int, weighted: bool, op: int, device="cuda"):
+    import torch
+    nbytes = tbe_workspace_bytes(desc, N, weighted, op)
+    if nbytes == 0:
+        raise TbeError(TBE_ERR_ARG, "tbe_workspace_bytes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# --- the three calls ------------------------------------------------------------
+def tbe_forward(desc: Desc, W, indices, offsets, psw, out, meta: Optional[Meta], ws, stream=None):
+    N = indices.numel()
+    _check(_lib.tbe_forward(desc.ref, _ptr(W), _ptr(indices), _ptr(offsets), N, _ptr(psw),
+                            _ptr(out), meta.ref if meta is not None else None, _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream)), "tbe_forward")
+
+
+def tbe_preprocess(desc: Desc, indices, offsets, psw, meta: Meta, ws, stream=None):
+    N = indices.numel()
+    _check(_lib.tbe_preprocess(desc.ref, _ptr(indices), _ptr(offsets), N, _ptr(psw), meta.ref,
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "tbe_preprocess")
+
+
+def tbe_backward_adagrad(desc: Desc, W, momentum, grad_out, indices, offsets, psw,
+                         meta: Optional[Meta], lr: float, eps: float, ws, stream=None):
+    N = indices.numel()
+    _check(_lib.tbe_backward_adagrad(desc.ref, _ptr(W), _ptr(momentum), _ptr(grad_out),
+                                     _ptr(indices), _ptr(offsets), N, _ptr(psw),
+                                     meta.ref if meta is not None else None, float(lr),
+                                     float(eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)), "tbe_backward_adagrad")
+
+
+# --- stage timer -----------------------------------------------------------------
+class Timer:
+    def __init__(self, capacity: int = 256):
+        h = ctypes.c_void_p()
+        _check(_lib.tbe_timer_create(int(capacity), ctypes.byref(h)), "tbe_timer_create")
+        self.handle = h
+
+    def reset(self):
+        _check(_lib.tbe_timer_reset(self.handle), "tbe_timer_reset")
+
+    def read(self) -> dict:
+        ms = (ctypes.c_float * TBE_NUM_STAGES)()
+        n = (ctypes.c_int32 * TBE_NUM_STAGES)()
+        _check(_lib.tbe_timer_read(self.handle, ms, n), "tbe_timer_read")
+        return {STAGES[i]: (float(ms[i]), int(n[i])) for i in range(TBE_NUM_STAGES)}
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.tbe_timer_destroy(h)
+            self.handle = None
+
+
+def exported_symbols() -> list:
+    """Names the library exports from include/tbe.h (used by host tests)."""
+    return ["tbe_status_str", "tbe_select_path", "tbe_meta_capacity", "tbe_workspace_bytes",
+            "tbe_forward", "tbe_preprocess", "tbe_backward_adagrad", "tbe_timer_create",
+            "tbe_timer_reset", "tbe_timer_read", "tbe_timer_destroy"]

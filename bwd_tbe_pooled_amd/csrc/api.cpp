@@ -1,0 +1,491 @@
+// C ABI of the TBE library: argument validation (host, before any launch),
+// path selection, workspace carving and the launch sequence of each call on
+// the caller's stream. No allocation of device memory, no global state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "internal.h"
+
+namespace tbe {
+
+int small_splits_for(int32_t T, int32_t B);
+
+RowShape row_shape(int D, int max_v) {
+  RowShape r;
+  int V = max_v;
+  while (V > 1 && D % V != 0) V >>= 1;
+  const int per = (D + V - 1) / V;
+  int G = 1, lg = 0;
+  while (G < per && G < 64) { G <<= 1; ++lg; }
+  r.V = V;
+  r.G = G;
+  r.log2G = lg;
+  r.P = (D + G * V - 1) / (G * V);
+  return r;
+}
+
+static bool small_eligible(const tbe_desc* d, int64_t N, int weighted, int64_t max_rows) {
+  // Page 1, checklist item 2: E <= 64, 64 <= D <= 128, L >= 64, f16, unweighted.
+  if (d->flags & TBE_FLAG_FORCE_GENERIC) return false;
+  if (weighted || d->wdtype != TBE_F16) return false;
+  if (max_rows > kSmallE || d->D < 64 || d->D > 128) return false;
+  const int64_t nbags = (int64_t)d->T * d->B;
+  if (nbags == 0) return false;
+  return N >= 64 * nbags;  // average bag length N / (T*B) >= 64
+}
+
+tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) {
+  if (!d || !p || !d->rows) return TBE_ERR_ARG;
+  if (d->T < 1 || d->D < 1 || d->B < 0 || N < 0) return TBE_ERR_ARG;
+  if (d->wdtype != TBE_F32 && d->wdtype != TBE_F16 && d->wdtype != TBE_BF16) return TBE_ERR_UNSUPPORTED;
+  if (d->flags & ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC)) return TBE_ERR_ARG;
+  if (d->short_max < 0 || d->chunk < 0) return TBE_ERR_ARG;
+  int64_t sum = 0, mx = 0;
+  for (int32_t t = 0; t < d->T; ++t) {
+    if (d->rows[t] < 1) return TBE_ERR_ARG;
+    sum += d->rows[t];
+    mx = std::max<int64_t>(mx, d->rows[t]);
+    if (sum >= (int64_t(1) << 31)) return TBE_ERR_UNSUPPORTED;  // int32 keys (checklist item 6)
+  }
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  if (N >= lim || (int64_t)d->T * d->B >= lim) return TBE_ERR_UNSUPPORTED;
+  const RowShape rs = row_shape(d->D, 8);
+  if (rs.P > 4) return TBE_ERR_UNSUPPORTED;
+
+  p->T = d->T;
+  p->D = d->D;
+  p->B = d->B;
+  p->N = N;
+  p->nbags = (int64_t)d->T * d->B;
+  p->sum_rows = sum;
+  p->max_rows = mx;
+  p->wdtype = d->wdtype;
+  p->weighted = weighted != 0;
+  p->S = d->short_max ? d->short_max : kDefaultShortMax;
+  p->C = d->chunk ? d->chunk : kDefaultChunk;
+  p->path = small_eligible(d, N, weighted, mx) ? TBE_PATH_SMALL_TABLE : TBE_PATH_GENERIC;
+  int nbits = 0;
+  while ((int64_t(1) << nbits) < mx) ++nbits;
+  p->sort_passes = std::max(1, (nbits + 7) / 8);
+  p->sort_bits = std::max(1, (nbits + p->sort_passes - 1) / p->sort_passes);
+  p->sort_tiles_max = (N + kSortTile - 1) / kSortTile + d->T;
+  p->cap_runs = std::min<int64_t>(N, sum);
+  p->cap_long = N / p->S;
+  p->cap_chunks = p->cap_long ? N / p->C + p->cap_long : 0;
+  p->small_splits = small_splits_for(d->T, d->B);
+  return TBE_OK;
+}
+
+void meta_caps(const Problem& p, int64_t c[TBE_META_NUM_ARRAYS]) {
+  for (int i = 0; i < TBE_META_NUM_ARRAYS; ++i) c[i] = 0;
+  c[TBE_META_COUNTS] = 8;
+  if (p.path == TBE_PATH_SMALL_TABLE) {
+    c[TBE_META_HIST] = p.nbags * kSmallE;
+    return;
+  }
+  c[TBE_META_RUN_KEYS] = p.cap_runs;
+  c[TBE_META_RUN_OFFSETS] = p.cap_runs + 1;
+  c[TBE_META_SORTED_POS] = p.N;
+  c[TBE_META_SORTED_BAG] = p.N;
+  c[TBE_META_SORTED_PSW] = p.weighted ? p.N : 0;
+  c[TBE_META_SHORT_RUNS] = p.cap_runs;
+  c[TBE_META_LONG_RUNS] = p.cap_long;
+  c[TBE_META_LONG_CHUNK_BEGIN] = p.cap_long + 1;
+  c[TBE_META_CHUNK_RUN] = p.cap_chunks;
+  c[TBE_META_CHUNK_START] = p.cap_chunks;
+}
+
+static size_t meta_elem_bytes(int i) { return i == TBE_META_HIST ? 1 : 4; }
+
+WsLayout ws_layout(const Problem& p, tbe_op op) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  L.tinfo = take(sizeof(int32_t) * 2 * (size_t)p.T);
+  L.flags = take(sizeof(int32_t) * 16);
+  const bool generic = p.path == TBE_PATH_GENERIC;
+  const bool pre = (op == TBE_OP_FORWARD_PREPROCESS || op == TBE_OP_PREPROCESS ||
+                    op == TBE_OP_BACKWARD_SELF);
+  L.has_pre = pre && generic;
+  if (L.has_pre) {
+    const size_t n4 = sizeof(int32_t) * (size_t)p.N;
+    L.bag_of = take(n4);
+    const int sets = p.sort_passes >= 3 ? 2 : (p.sort_passes == 2 ? 1 : 0);
+    for (int k = 0; k < 4; ++k) {
+      const bool need = k < 3 || p.weighted;
+      L.sortA[k] = (sets >= 1 && need) ? take(n4) : 0;
+      L.sortB[k] = (sets >= 2 && need) ? take(n4) : 0;
+    }
+    L.sorted_keys = take(n4);
+    L.tile_base = take(sizeof(int32_t) * ((size_t)p.T + 1));
+    const int64_t radix = int64_t(1) << p.sort_bits;
+    L.digit_counts = take(sizeof(int32_t) * (size_t)(radix * p.sort_tiles_max));
+    L.digit_tot = take(sizeof(int32_t) * (size_t)(radix * p.T));
+    const int64_t nt = (p.N + kRleTile - 1) / kRleTile;
+    L.rle_tiles = take(sizeof(int32_t) * (size_t)(nt + 4));
+    const int64_t rt = (p.cap_runs + kRleTile - 1) / kRleTile;
+    L.route_tiles = take(sizeof(int32_t) * (size_t)(3 * rt + 4));
+  }
+  L.has_meta = op == TBE_OP_BACKWARD_SELF;
+  if (L.has_meta) {
+    int64_t caps[TBE_META_NUM_ARRAYS];
+    meta_caps(p, caps);
+    for (int i = 0; i < TBE_META_NUM_ARRAYS; ++i)
+      L.meta[i] = caps[i] ? take(meta_elem_bytes(i) * (size_t)caps[i]) : 0;
+  }
+  L.has_partials = op == TBE_OP_BACKWARD || op == TBE_OP_BACKWARD_SELF;
+  if (L.has_partials) {
+    if (generic) {
+      const size_t acc = p.wdtype == TBE_F32 ? 8 : 4;
+      L.partials = take(acc * (size_t)p.cap_chunks * (size_t)p.D);
+    } else {
+      const size_t parts = (size_t)p.T * (size_t)p.small_splits * kSmallE;
+      L.partials = take(sizeof(float) * parts * (size_t)p.D);
+      L.part_counts = take(sizeof(int32_t) * parts);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+// --- stage timer -------------------------------------------------------------
+
+struct StageTimer {
+  int32_t capacity;
+  std::vector<hipEvent_t> ev[TBE_NUM_STAGES];  // 2 per interval
+  int32_t used[TBE_NUM_STAGES];
+  bool open[TBE_NUM_STAGES];
+};
+
+}  // namespace tbe
+
+struct tbe_timer {
+  tbe::StageTimer st;
+};
+
+namespace tbe {
+
+void timer_begin(tbe_timer* t, int stage, hipStream_t s) {
+  if (!t) return;
+  StageTimer& st = t->st;
+  st.open[stage] = false;
+  if (st.used[stage] >= st.capacity) return;
+  (void)hipEventRecord(st.ev[stage][2 * st.used[stage]], s);
+  st.open[stage] = true;
+}
+
+void timer_end(tbe_timer* t, int stage, hipStream_t s) {
+  if (!t) return;
+  StageTimer& st = t->st;
+  if (!st.open[stage]) return;
+  (void)hipEventRecord(st.ev[stage][2 * st.used[stage] + 1], s);
+  st.used[stage] += 1;
+  st.open[stage] = false;
+}
+
+}  // namespace tbe
+
+using namespace tbe;
+
+namespace {
+
+#define TBE_TRY_HIP(expr)                                  \
+  do {                                                     \
+    if ((expr) != hipSuccess) return TBE_ERR_HIP;          \
+  } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool meta_ok_generic(const tbe_meta* m, bool weighted) {
+  return m && m->counts && m->run_keys && m->run_offsets && m->sorted_pos && m->sorted_bag &&
+         (!weighted || m->sorted_psw) && m->short_runs && m->long_runs && m->long_chunk_begin &&
+         m->chunk_run && m->chunk_start;
+}
+
+bool meta_ok_small(const tbe_meta* m) { return m && m->counts && m->hist; }
+
+tbe_meta carve_meta(void* ws, const WsLayout& L) {
+  tbe_meta m{};
+  auto ptr = [&](int i) -> void* { return L.meta[i] ? at<char>(ws, L.meta[i]) : nullptr; };
+  m.counts = (int32_t*)ptr(TBE_META_COUNTS);
+  m.run_keys = (int32_t*)ptr(TBE_META_RUN_KEYS);
+  m.run_offsets = (int32_t*)ptr(TBE_META_RUN_OFFSETS);
+  m.sorted_pos = (int32_t*)ptr(TBE_META_SORTED_POS);
+  m.sorted_bag = (int32_t*)ptr(TBE_META_SORTED_BAG);
+  m.sorted_psw = (float*)ptr(TBE_META_SORTED_PSW);
+  m.short_runs = (int32_t*)ptr(TBE_META_SHORT_RUNS);
+  m.long_runs = (int32_t*)ptr(TBE_META_LONG_RUNS);
+  m.long_chunk_begin = (int32_t*)ptr(TBE_META_LONG_CHUNK_BEGIN);
+  m.chunk_run = (int32_t*)ptr(TBE_META_CHUNK_RUN);
+  m.chunk_start = (int32_t*)ptr(TBE_META_CHUNK_START);
+  m.hist = (uint8_t*)ptr(TBE_META_HIST);
+  // Unused psw slot on unweighted problems still needs a non-null pointer for
+  // nothing; leave NULL.
+  return m;
+}
+
+// Common prologue: table info upload and optional validation.
+tbe_status prologue(const tbe_desc* d, const Problem& p, const int32_t* indices,
+                    const int32_t* offsets, void* ws, const WsLayout& L, hipStream_t s) {
+  int32_t* tinfo = at<int32_t>(ws, L.tinfo);
+  TBE_TRY_HIP(launch_fill_tinfo(p, d->rows, tinfo, s));
+  if (d->flags & TBE_FLAG_VALIDATE) {
+    int32_t* flag = at<int32_t>(ws, L.flags);
+    timer_begin(d->timer, TBE_STAGE_VALIDATE, s);
+    TBE_TRY_HIP(launch_validate(p, indices, offsets, tinfo, flag, s));
+    timer_end(d->timer, TBE_STAGE_VALIDATE, s);
+    int32_t host_flag = 0;
+    TBE_TRY_HIP(hipMemcpyAsync(&host_flag, flag, sizeof host_flag, hipMemcpyDeviceToHost, s));
+    TBE_TRY_HIP(hipStreamSynchronize(s));
+    if (host_flag) return TBE_ERR_INDEX_RANGE;
+  }
+  return TBE_OK;
+}
+
+tbe_status run_preprocess(const tbe_desc* d, const Problem& p, const int32_t* indices,
+                          const int32_t* offsets, const float* psw, const tbe_meta& meta,
+                          void* ws, const WsLayout& L, hipStream_t s) {
+  const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
+  SortBuffers b{};
+  b.bag_of = at<int32_t>(ws, L.bag_of);
+  for (int k = 0; k < 4; ++k) {
+    b.A[k] = L.sortA[k] ? at<int32_t>(ws, L.sortA[k]) : nullptr;
+    b.B[k] = L.sortB[k] ? at<int32_t>(ws, L.sortB[k]) : nullptr;
+  }
+  b.sorted_keys = at<int32_t>(ws, L.sorted_keys);
+  b.tile_base = at<int32_t>(ws, L.tile_base);
+  b.digit_counts = at<int32_t>(ws, L.digit_counts);
+  b.digit_tot = at<int32_t>(ws, L.digit_tot);
+  timer_begin(d->timer, TBE_STAGE_LINEARIZE, s);
+  TBE_TRY_HIP(launch_linearize(p, offsets, b.bag_of, s));
+  timer_end(d->timer, TBE_STAGE_LINEARIZE, s);
+  timer_begin(d->timer, TBE_STAGE_SORT, s);
+  TBE_TRY_HIP(launch_sort(p, indices, offsets, psw, tinfo, b, meta, d->timer, s));
+  timer_end(d->timer, TBE_STAGE_SORT, s);
+  timer_begin(d->timer, TBE_STAGE_RLE_ROUTE, s);
+  TBE_TRY_HIP(launch_rle_route(p, b.sorted_keys, at<int32_t>(ws, L.rle_tiles),
+                               at<int32_t>(ws, L.route_tiles), meta, s));
+  timer_end(d->timer, TBE_STAGE_RLE_ROUTE, s);
+  return TBE_OK;
+}
+
+tbe_status check_ws(const Problem& p, tbe_op op, void* ws, size_t ws_bytes, WsLayout* L) {
+  *L = ws_layout(p, op);
+  if (!ws || ws_bytes < L->total) return TBE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return TBE_ERR_ARG;
+  return TBE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tbe_status_str(tbe_status s) {
+  switch (s) {
+    case TBE_OK: return "ok";
+    case TBE_ERR_ARG: return "invalid argument";
+    case TBE_ERR_UNSUPPORTED: return "unsupported problem shape or type";
+    case TBE_ERR_WORKSPACE: return "workspace missing or too small";
+    case TBE_ERR_INDEX_RANGE: return "offsets or indices out of range";
+    case TBE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t tbe_select_path(const tbe_desc* desc, int64_t N, int32_t weighted) {
+  Problem p;
+  const tbe_status st = make_problem(desc, N, weighted, &p);
+  if (st != TBE_OK) return -(int32_t)st;
+  return p.path;
+}
+
+tbe_status tbe_meta_capacity(const tbe_desc* desc, int64_t N, int32_t weighted, int64_t* caps) {
+  if (!caps) return TBE_ERR_ARG;
+  Problem p;
+  const tbe_status st = make_problem(desc, N, weighted, &p);
+  if (st != TBE_OK) return st;
+  meta_caps(p, caps);
+  return TBE_OK;
+}
+
+size_t tbe_workspace_bytes(const tbe_desc* desc, int64_t N, int32_t weighted, tbe_op op) {
+  Problem p;
+  if (make_problem(desc, N, weighted, &p) != TBE_OK) return 0;
+  if (op < TBE_OP_FORWARD || op > TBE_OP_BACKWARD_SELF) return 0;
+  return ws_layout(p, op).total;
+}
+
+tbe_status tbe_forward(const tbe_desc* desc, const void* W, const int32_t* indices,
+                       const int32_t* offsets, int64_t N, const float* psw, float* out,
+                       tbe_meta* meta, void* ws, size_t ws_bytes, void* stream) {
+  Problem p;
+  tbe_status st = make_problem(desc, N, psw != nullptr, &p);
+  if (st != TBE_OK) return st;
+  if (!W || !offsets || (!indices && N > 0) || (!out && p.nbags > 0)) return TBE_ERR_ARG;
+  const tbe_op op = meta ? TBE_OP_FORWARD_PREPROCESS : TBE_OP_FORWARD;
+  if (meta && !(p.path == TBE_PATH_SMALL_TABLE ? meta_ok_small(meta) : meta_ok_generic(meta, p.weighted)))
+    return TBE_ERR_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, op, ws, ws_bytes, &L)) != TBE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
+  const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
+  if (p.path == TBE_PATH_SMALL_TABLE) {
+    int32_t* counts = meta ? meta->counts : at<int32_t>(ws, L.flags) + 8;
+    timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    TBE_TRY_HIP(launch_small_forward(p, W, indices, offsets, tinfo, out, meta ? meta->hist : nullptr,
+                                     counts, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    return TBE_OK;
+  }
+  timer_begin(desc->timer, TBE_STAGE_FWD_POOL, s);
+  TBE_TRY_HIP(launch_forward_pool(p, W, indices, offsets, psw, tinfo, out, s));
+  timer_end(desc->timer, TBE_STAGE_FWD_POOL, s);
+  if (meta) return run_preprocess(desc, p, indices, offsets, psw, *meta, ws, L, s);
+  return TBE_OK;
+}
+
+tbe_status tbe_preprocess(const tbe_desc* desc, const int32_t* indices, const int32_t* offsets,
+                          int64_t N, const float* psw, tbe_meta* meta, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Problem p;
+  tbe_status st = make_problem(desc, N, psw != nullptr, &p);
+  if (st != TBE_OK) return st;
+  if (!offsets || (!indices && N > 0)) return TBE_ERR_ARG;
+  if (!(p.path == TBE_PATH_SMALL_TABLE ? meta_ok_small(meta) : meta_ok_generic(meta, p.weighted)))
+    return TBE_ERR_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, TBE_OP_PREPROCESS, ws, ws_bytes, &L)) != TBE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
+  if (p.path == TBE_PATH_SMALL_TABLE) {
+    timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    TBE_TRY_HIP(launch_small_forward(p, nullptr, indices, offsets, at<int32_t>(ws, L.tinfo), nullptr,
+                                     meta->hist, meta->counts, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    return TBE_OK;
+  }
+  return run_preprocess(desc, p, indices, offsets, psw, *meta, ws, L, s);
+}
+
+tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
+                                const float* grad_out, const int32_t* indices,
+                                const int32_t* offsets, int64_t N, const float* psw,
+                                const tbe_meta* meta, double lr, double eps, void* ws,
+                                size_t ws_bytes, void* stream) {
+  Problem p;
+  tbe_status st = make_problem(desc, N, psw != nullptr, &p);
+  if (st != TBE_OK) return st;
+  if (!W || !momentum || (!grad_out && p.nbags > 0) || !offsets || (!indices && N > 0))
+    return TBE_ERR_ARG;
+  if (!(lr >= 0.0) || !(eps >= 0.0)) return TBE_ERR_ARG;
+  const tbe_op op = meta ? TBE_OP_BACKWARD : TBE_OP_BACKWARD_SELF;
+  if (meta && !(p.path == TBE_PATH_SMALL_TABLE ? meta_ok_small(meta) : meta_ok_generic(meta, p.weighted)))
+    return TBE_ERR_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, op, ws, ws_bytes, &L)) != TBE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
+  const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
+  tbe_meta m = meta ? *meta : carve_meta(ws, L);
+
+  if (p.path == TBE_PATH_SMALL_TABLE) {
+    if (!meta) {
+      timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
+      TBE_TRY_HIP(launch_small_forward(p, nullptr, indices, offsets, tinfo, nullptr, m.hist,
+                                       m.counts, s));
+      timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    }
+    float* parts = at<float>(ws, L.partials);
+    int32_t* pcounts = at<int32_t>(ws, L.part_counts);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_BWD, s);
+    TBE_TRY_HIP(launch_small_backward(p, grad_out, m.hist, m.counts, indices, offsets, parts,
+                                      pcounts, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_BWD, s);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_APPLY, s);
+    TBE_TRY_HIP(launch_small_apply(p, W, momentum, tinfo, parts, pcounts, lr, eps, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_APPLY, s);
+    return TBE_OK;
+  }
+
+  if (!meta) {
+    if ((st = run_preprocess(desc, p, indices, offsets, psw, m, ws, L, s)) != TBE_OK) return st;
+  }
+  void* parts = at<void>(ws, L.partials);
+  timer_begin(desc->timer, TBE_STAGE_BWD_SHORT, s);
+  TBE_TRY_HIP(launch_bwd_short(p, W, momentum, grad_out, m, tinfo, lr, eps, s));
+  timer_end(desc->timer, TBE_STAGE_BWD_SHORT, s);
+  timer_begin(desc->timer, TBE_STAGE_BWD_LONG, s);
+  TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, s));
+  timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
+  timer_begin(desc->timer, TBE_STAGE_BWD_APPLY, s);
+  TBE_TRY_HIP(launch_bwd_apply(p, W, momentum, m, parts, lr, eps, s));
+  timer_end(desc->timer, TBE_STAGE_BWD_APPLY, s);
+  return TBE_OK;
+}
+
+tbe_status tbe_timer_create(int32_t capacity, tbe_timer** out) {
+  if (!out || capacity < 1) return TBE_ERR_ARG;
+  tbe_timer* t = new (std::nothrow) tbe_timer;
+  if (!t) return TBE_ERR_ARG;
+  t->st.capacity = capacity;
+  for (int s = 0; s < TBE_NUM_STAGES; ++s) {
+    t->st.used[s] = 0;
+    t->st.open[s] = false;
+    t->st.ev[s].assign(2 * (size_t)capacity, nullptr);
+    for (auto& e : t->st.ev[s]) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        tbe_timer_destroy(t);
+        return TBE_ERR_HIP;
+      }
+    }
+  }
+  *out = t;
+  return TBE_OK;
+}
+
+tbe_status tbe_timer_reset(tbe_timer* t) {
+  if (!t) return TBE_ERR_ARG;
+  for (int s = 0; s < TBE_NUM_STAGES; ++s) {
+    t->st.used[s] = 0;
+    t->st.open[s] = false;
+  }
+  return TBE_OK;
+}
+
+tbe_status tbe_timer_read(tbe_timer* t, float* ms, int32_t* intervals) {
+  if (!t || !ms || !intervals) return TBE_ERR_ARG;
+  for (int s = 0; s < TBE_NUM_STAGES; ++s) {
+    float total = 0.f;
+    for (int32_t i = 0; i < t->st.used[s]; ++i) {
+      hipEvent_t a = t->st.ev[s][2 * i], b = t->st.ev[s][2 * i + 1];
+      if (hipEventSynchronize(b) != hipSuccess) return TBE_ERR_HIP;
+      float x = 0.f;
+      if (hipEventElapsedTime(&x, a, b) != hipSuccess) return TBE_ERR_HIP;
+      total += x;
+    }
+    ms[s] = total;
+    intervals[s] = t->st.used[s];
+  }
+  return TBE_OK;
+}
+
+void tbe_timer_destroy(tbe_timer* t) {
+  if (!t) return;
+  for (int s = 0; s < TBE_NUM_STAGES; ++s)
+    for (auto& e : t->st.ev[s])
+      if (e) (void)hipEventDestroy(e);
+  delete t;
+}
+
+}  // extern "C"

@@ -1,0 +1,358 @@
+// Backward with the optimizer applied in place (page 1, backward section): for
+// each run (unique (table,row)), sum the upstream gradient rows of all its
+// lookups, each scaled by the lookup's per-sample weight on weighted tables,
+// then apply exactly one row-wise Adagrad step to the row:
+//     m' = m + mean_d(g_d^2),   w' = w - lr * g / (sqrt(m') + eps).
+//
+// Three kernels, following the page's routing by segment length:
+//   short  (SL < S): one row slot (G lanes of a wave) owns a whole run: it
+//          gathers the run's gradient rows, accumulates in registers, applies
+//          Adagrad and stores the row with plain stores; no atomics, since no
+//          other slot touches the row.
+//   long   (SL >= S): one wave per chunk of C lookups writes the chunk's
+//          partial sum to the workspace.
+//   apply  one wave per long run reduces its chunk partials in a fixed order
+//          and applies Adagrad.
+// Accumulation is float for f16/bf16 weights and double for f32 weights (page
+// 1, checklist item 1); nothing is accumulated with atomics, so results are
+// deterministic run to run.
+//
+// The gradient row of lookup k is grad[b, t*D .. t*D+D-1] where sorted_bag[k]
+// = t*B + b; every lookup of a run shares its table t.
+#include "adagrad.h"
+#include "device.h"
+#include "internal.h"
+
+namespace tbe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <typename ACC, int V, int PMAX>
+__device__ __forceinline__ void zero_acc(ACC (&acc)[PMAX][V]) {
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[p][v] = (ACC)0;
+}
+
+template <typename WT, int V, int PMAX, bool WEIGHTED>
+__global__ __launch_bounds__(kThreads) void bwd_short_kernel(
+    WT* __restrict__ W, float* __restrict__ mom, const float* __restrict__ grad,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ short_runs,
+    const int32_t* __restrict__ run_keys, const int32_t* __restrict__ run_offsets,
+    const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw, int32_t T,
+    int32_t B, int32_t D, int32_t G, int32_t log2G, int32_t P,
+    typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
+  using ACC = typename acc_of<WT>::type;
+  using GRAW = typename raw_vec<float, V>::type;
+  constexpr int UNROLL = PMAX == 1 ? 4 : 1;
+  const int lane = lane_id();
+  const int slot = lane >> log2G;
+  const int col = lane & (G - 1);
+  const int NS = kWave >> log2G;
+  const int64_t n_short = counts[1];
+  const int64_t gwave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+
+  for (int64_t grp = gwave; grp * NS < n_short; grp += nwaves) {
+    const int64_t i = grp * NS + slot;
+    const bool active = i < n_short;
+    const int32_t u = active ? short_runs[i] : 0;
+    const int32_t k0 = active ? run_offsets[u] : 0;
+    const int32_t k1 = active ? run_offsets[u + 1] : 0;
+    const int32_t t = active ? sorted_bag[k0] / B : 0;
+    const float* __restrict__ gt = grad + (int64_t)t * D;
+    ACC acc[PMAX][V];
+    zero_acc<ACC, V, PMAX>(acc);
+    for (int32_t k = k0; k < k1; k += UNROLL) {
+      GRAW buf[UNROLL][PMAX];
+      float sc[UNROLL];
+#pragma unroll
+      for (int uu = 0; uu < UNROLL; ++uu) {
+        const int32_t kk = k + uu;
+        const bool ok = kk < k1;
+        const int32_t bag = ok ? sorted_bag[kk] : 0;
+        if constexpr (WEIGHTED) sc[uu] = ok ? sorted_psw[kk] : 0.f;
+        else sc[uu] = ok ? 1.f : 0.f;
+        const float* row = gt + (int64_t)(bag - t * B) * T * D;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+          const int e = (p * G + col) * V;
+          if (ok && p < P && e < D) buf[uu][p] = load_vec<float, V>(row + e);
+          else buf[uu][p] = GRAW{};
+        }
+      }
+#pragma unroll
+      for (int uu = 0; uu < UNROLL; ++uu) {
+        const ACC s = (ACC)sc[uu];
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+          const float* x = reinterpret_cast<const float*>(&buf[uu][p]);
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[p][v] += s * (ACC)x[v];
+        }
+      }
+    }
+    if (active) {  // whole slots are active or not, so the slot's reductions stay within it
+      const int32_t key = run_keys[u];
+      adagrad_row<WT, ACC, V, PMAX>(W + (int64_t)key * D, mom + key, acc, col, G, P, D, lr, eps);
+    }
+  }
+}
+
+template <int V, int PMAX, typename ACC, bool WEIGHTED>
+__global__ __launch_bounds__(kThreads) void bwd_long_kernel(
+    const float* __restrict__ grad, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ chunk_run, const int32_t* __restrict__ chunk_start,
+    const int32_t* __restrict__ run_offsets, const int32_t* __restrict__ sorted_bag,
+    const float* __restrict__ sorted_psw, ACC* __restrict__ partials, int32_t T, int32_t B,
+    int32_t D, int32_t C, int32_t G, int32_t log2G, int32_t P) {
+  using GRAW = typename raw_vec<float, V>::type;
+  constexpr int UNROLL = PMAX == 1 ? 4 : 1;
+  const int lane = lane_id();
+  const int slot = lane >> log2G;
+  const int col = lane & (G - 1);
+  const int NS = kWave >> log2G;
+  const int64_t n_chunks = counts[3];
+  const int64_t gwave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+
+  for (int64_t c = gwave; c < n_chunks; c += nwaves) {
+    const int32_t u = chunk_run[c];
+    const int32_t k0 = chunk_start[c];
+    const int32_t kend = run_offsets[u + 1];
+    const int32_t k1 = k0 + C < kend ? k0 + C : kend;
+    const int32_t t = sorted_bag[k0] / B;
+    const float* __restrict__ gt = grad + (int64_t)t * D;
+    ACC acc[PMAX][V];
+    zero_acc<ACC, V, PMAX>(acc);
+    for (int32_t base = k0; base < k1; base += kWave) {
+      const int n = k1 - base < kWave ? k1 - base : kWave;
+      const int32_t my_bag = lane < n ? sorted_bag[base + lane] : 0;
+      float my_s = 0.f;
+      if constexpr (WEIGHTED) my_s = lane < n ? sorted_psw[base + lane] : 0.f;
+      for (int r0 = 0; r0 < n; r0 += NS * UNROLL) {
+        GRAW buf[UNROLL][PMAX];
+        float sc[UNROLL];
+#pragma unroll
+        for (int uu = 0; uu < UNROLL; ++uu) {
+          const int r = r0 + uu * NS + slot;
+          const bool ok = r < n;
+          const int32_t bag = __shfl(my_bag, r & (kWave - 1));
+          if constexpr (WEIGHTED) {
+            const float sv = __shfl(my_s, r & (kWave - 1));
+            sc[uu] = ok ? sv : 0.f;
+          } else {
+            sc[uu] = ok ? 1.f : 0.f;
+          }
+          const float* row = gt + (int64_t)(bag - t * B) * T * D;
+#pragma unroll
+          for (int p = 0; p < PMAX; ++p) {
+            const int e = (p * G + col) * V;
+            if (ok && p < P && e < D) buf[uu][p] = load_vec<float, V>(row + e);
+            else buf[uu][p] = GRAW{};
+          }
+        }
+#pragma unroll
+        for (int uu = 0; uu < UNROLL; ++uu) {
+          const ACC s = (ACC)sc[uu];
+#pragma unroll
+          for (int p = 0; p < PMAX; ++p) {
+            const float* x = reinterpret_cast<const float*>(&buf[uu][p]);
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[p][v] += s * (ACC)x[v];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[p][v] = across_slots_sum<ACC>(acc[p][v], G);
+    if (slot == 0) {
+      ACC* out = partials + c * D;
+#pragma unroll
+      for (int p = 0; p < PMAX; ++p) {
+        const int e = (p * G + col) * V;
+        if (p < P && e < D) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) out[e + v] = acc[p][v];
+        }
+      }
+    }
+  }
+}
+
+template <typename WT, int V, int PMAX>
+__global__ __launch_bounds__(kThreads) void bwd_apply_kernel(
+    WT* __restrict__ W, float* __restrict__ mom, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ long_runs, const int32_t* __restrict__ long_chunk_begin,
+    const int32_t* __restrict__ run_keys, const typename acc_of<WT>::type* __restrict__ partials,
+    int32_t D, int32_t G, int32_t log2G, int32_t P, typename acc_of<WT>::type lr,
+    typename acc_of<WT>::type eps) {
+  using ACC = typename acc_of<WT>::type;
+  const int lane = lane_id();
+  const int slot = lane >> log2G;
+  const int col = lane & (G - 1);
+  const int NS = kWave >> log2G;
+  const int64_t n_long = counts[2];
+  const int64_t gwave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  for (int64_t l = gwave; l < n_long; l += nwaves) {
+    const int32_t c0 = long_chunk_begin[l];
+    const int32_t c1 = long_chunk_begin[l + 1];
+    ACC acc[PMAX][V];
+    zero_acc<ACC, V, PMAX>(acc);
+    // slot s sums chunks c0+s, c0+s+NS, ... in ascending order; the slots are
+    // then combined by a fixed butterfly, so the order is the same every run.
+    for (int32_t c = c0 + slot; c < c1; c += NS) {
+      const ACC* src = partials + (int64_t)c * D;
+#pragma unroll
+      for (int p = 0; p < PMAX; ++p) {
+        const int e = (p * G + col) * V;
+        if (p < P && e < D) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[p][v] += src[e + v];
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[p][v] = across_slots_sum<ACC>(acc[p][v], G);
+    if (slot == 0) {
+      const int32_t key = run_keys[long_runs[l]];
+      adagrad_row<WT, ACC, V, PMAX>(W + (int64_t)key * D, mom + key, acc, col, G, P, D, lr, eps);
+    }
+  }
+}
+
+inline int64_t persistent_blocks(int64_t work_waves) {
+  // Enough workgroups to fill 256 CUs several times over; the kernels stride.
+  int64_t cap = 256 * 16;
+  int64_t need = (work_waves + kWaves - 1) / kWaves;
+  if (need < 1) need = 1;
+  return need < cap ? need : cap;
+}
+
+template <typename WT, int V, int PMAX>
+hipError_t short_typed(const Problem& p, const RowShape& rs, void* W, float* m, const float* grad,
+                       const tbe_meta& meta, double lr, double eps, hipStream_t s) {
+  using ACC = typename acc_of<WT>::type;
+  const int NS = kWave / rs.G;
+  const dim3 grid((unsigned)persistent_blocks((p.cap_runs + NS - 1) / NS));
+  if (p.weighted)
+    hipLaunchKernelGGL((bwd_short_kernel<WT, V, PMAX, true>), grid, dim3(kThreads), 0, s, (WT*)W, m,
+                       grad, meta.counts, meta.short_runs, meta.run_keys, meta.run_offsets,
+                       meta.sorted_bag, meta.sorted_psw, p.T, p.B, p.D, rs.G, rs.log2G, rs.P,
+                       (ACC)lr, (ACC)eps);
+  else
+    hipLaunchKernelGGL((bwd_short_kernel<WT, V, PMAX, false>), grid, dim3(kThreads), 0, s, (WT*)W,
+                       m, grad, meta.counts, meta.short_runs, meta.run_keys, meta.run_offsets,
+                       meta.sorted_bag, meta.sorted_psw, p.T, p.B, p.D, rs.G, rs.log2G, rs.P,
+                       (ACC)lr, (ACC)eps);
+  return hipGetLastError();
+}
+
+template <typename ACC, int V, int PMAX>
+hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, const tbe_meta& meta,
+                      void* partials, hipStream_t s) {
+  const dim3 grid((unsigned)persistent_blocks(p.cap_chunks));
+  if (p.weighted)
+    hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, true>), grid, dim3(kThreads), 0, s, grad,
+                       meta.counts, meta.chunk_run, meta.chunk_start, meta.run_offsets,
+                       meta.sorted_bag, meta.sorted_psw, (ACC*)partials, p.T, p.B, p.D, p.C, rs.G,
+                       rs.log2G, rs.P);
+  else
+    hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, false>), grid, dim3(kThreads), 0, s, grad,
+                       meta.counts, meta.chunk_run, meta.chunk_start, meta.run_offsets,
+                       meta.sorted_bag, meta.sorted_psw, (ACC*)partials, p.T, p.B, p.D, p.C, rs.G,
+                       rs.log2G, rs.P);
+  return hipGetLastError();
+}
+
+template <typename WT, int V, int PMAX>
+hipError_t apply_typed(const Problem& p, const RowShape& rs, void* W, float* m,
+                       const tbe_meta& meta, const void* partials, double lr, double eps,
+                       hipStream_t s) {
+  using ACC = typename acc_of<WT>::type;
+  const dim3 grid((unsigned)persistent_blocks(p.cap_long));
+  hipLaunchKernelGGL((bwd_apply_kernel<WT, V, PMAX>), grid, dim3(kThreads), 0, s, (WT*)W, m,
+                     meta.counts, meta.long_runs, meta.long_chunk_begin, meta.run_keys,
+                     (const ACC*)partials, p.D, rs.G, rs.log2G, rs.P, (ACC)lr, (ACC)eps);
+  return hipGetLastError();
+}
+
+#define TBE_DISPATCH_V(RS, CALL_V)                              \
+  do {                                                          \
+    if ((RS).V == 8) { if ((RS).P == 1) return CALL_V(8, 1); return CALL_V(8, 4); } \
+    if ((RS).V == 4) { if ((RS).P == 1) return CALL_V(4, 1); return CALL_V(4, 4); } \
+    if ((RS).V == 2) { if ((RS).P == 1) return CALL_V(2, 1); return CALL_V(2, 4); } \
+    if ((RS).P == 1) return CALL_V(1, 1);                      \
+    return CALL_V(1, 4);                                        \
+  } while (0)
+
+template <typename WT>
+hipError_t short_for(const Problem& p, void* W, float* m, const float* grad, const tbe_meta& meta,
+                     double lr, double eps, hipStream_t s) {
+  const RowShape rs = row_shape(p.D, 8);
+#define CALL(VV, PP) short_typed<WT, VV, PP>(p, rs, W, m, grad, meta, lr, eps, s)
+  TBE_DISPATCH_V(rs, CALL);
+#undef CALL
+}
+
+template <typename ACC>
+hipError_t long_for(const Problem& p, const float* grad, const tbe_meta& meta, void* partials,
+                    hipStream_t s) {
+  const RowShape rs = row_shape(p.D, 8);
+#define CALL(VV, PP) long_typed<ACC, VV, PP>(p, rs, grad, meta, partials, s)
+  TBE_DISPATCH_V(rs, CALL);
+#undef CALL
+}
+
+template <typename WT>
+hipError_t apply_for(const Problem& p, void* W, float* m, const tbe_meta& meta,
+                     const void* partials, double lr, double eps, hipStream_t s) {
+  const RowShape rs = row_shape(p.D, 8);
+#define CALL(VV, PP) apply_typed<WT, VV, PP>(p, rs, W, m, meta, partials, lr, eps, s)
+  TBE_DISPATCH_V(rs, CALL);
+#undef CALL
+}
+
+}  // namespace
+
+hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* grad,
+                            const tbe_meta& meta, const int32_t* tinfo, double lr, double eps,
+                            hipStream_t s) {
+  (void)tinfo;
+  if (p.cap_runs == 0) return hipSuccess;
+  switch (p.wdtype) {
+    case TBE_F32: return short_for<float>(p, W, m, grad, meta, lr, eps, s);
+    case TBE_F16: return short_for<f16_t>(p, W, m, grad, meta, lr, eps, s);
+    case TBE_BF16: return short_for<bf16_t>(p, W, m, grad, meta, lr, eps, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
+                           void* partials, hipStream_t s) {
+  if (p.cap_chunks == 0) return hipSuccess;
+  if (p.wdtype == TBE_F32) return long_for<double>(p, grad, meta, partials, s);
+  return long_for<float>(p, grad, meta, partials, s);
+}
+
+hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
+                            const void* partials, double lr, double eps, hipStream_t s) {
+  if (p.cap_long == 0) return hipSuccess;
+  switch (p.wdtype) {
+    case TBE_F32: return apply_for<float>(p, W, m, meta, partials, lr, eps, s);
+    case TBE_F16: return apply_for<f16_t>(p, W, m, meta, partials, lr, eps, s);
+    case TBE_BF16: return apply_for<bf16_t>(p, W, m, meta, partials, lr, eps, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tbe

@@ -1,0 +1,130 @@
+// Host-side internals shared by the API layer and the kernel launchers:
+// problem geometry, the row decomposition of a D-wide row over wave lanes,
+// workspace carving, and the launcher entry points of each kernel file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tbe.h"
+
+namespace tbe {
+
+constexpr int kDefaultShortMax = 256;  // SL < 256 is short (page 1, routing)
+constexpr int kDefaultChunk = 256;     // 256-lookup chunks (page 1, routing)
+constexpr int kSmallE = 64;            // small-table path row limit and hist stride
+
+// Sort geometry.
+constexpr int kSortTile = 4096;        // elements per radix tile (256 threads x 16)
+constexpr int kRleTile = 4096;         // elements per RLE / routing tile
+
+// How one D-wide row maps onto the lanes of a wave: V consecutive elements
+// per lane per pass, G lanes per row (power of two), P passes; 64/G rows are
+// in flight per wave ("row slots").
+struct RowShape {
+  int V, G, P, log2G;
+};
+RowShape row_shape(int D, int max_v);
+
+// Everything the launchers need, derived once per call on the host.
+struct Problem {
+  int32_t T, D, B;
+  int64_t N;
+  int64_t nbags;       // T*B
+  int64_t sum_rows;    // sum(E_t)
+  int64_t max_rows;    // max(E_t)
+  tbe_dtype wdtype;
+  bool weighted;
+  int32_t S, C;        // short/long threshold and chunk length
+  int path;            // TBE_PATH_*
+  // radix sort
+  int sort_passes, sort_bits;   // bits per pass
+  int64_t sort_tiles_max;       // upper bound of tiles over all table segments
+  // capacities
+  int64_t cap_runs, cap_long, cap_chunks;
+  // small-table backward split
+  int small_splits;
+};
+
+tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p);
+
+// Workspace carving: every region 256-byte aligned.
+struct WsLayout {
+  size_t total;
+  // common
+  size_t tinfo;        // int32 toff[T], int32 rows[T]
+  size_t flags;        // int32[16]
+  // generic preprocessing
+  size_t bag_of;       // int32[N]
+  size_t sortA[4];     // key, pos, bag, psw  (int32/float [N] each)
+  size_t sortB[4];
+  size_t sorted_keys;  // int32[N]
+  size_t tile_base;    // int32[T+1]
+  size_t digit_counts; // int32[radix * sort_tiles_max]
+  size_t digit_tot;    // int32[T * radix]
+  size_t rle_tiles;    // int32[2 * n_rle_tiles]
+  size_t route_tiles;  // int32[6 * n_route_tiles]
+  // carved metadata (backward without a caller meta)
+  size_t meta[TBE_META_NUM_ARRAYS];
+  // backward
+  size_t partials;     // long-run chunk partials / small-table partials
+  size_t part_counts;  // small-table per-split row counts
+  bool has_pre, has_meta, has_partials;
+};
+
+WsLayout ws_layout(const Problem& p, tbe_op op);
+void meta_caps(const Problem& p, int64_t caps[TBE_META_NUM_ARRAYS]);
+
+// Stage timer (opaque to callers).
+struct StageTimer;
+void timer_begin(tbe_timer* t, int stage, hipStream_t s);
+void timer_end(tbe_timer* t, int stage, hipStream_t s);
+
+// --- launchers (return hipSuccess or the first launch error) ----------------
+hipError_t launch_fill_tinfo(const Problem& p, const int64_t* rows_host, int32_t* tinfo,
+                             hipStream_t s);
+hipError_t launch_validate(const Problem& p, const int32_t* indices, const int32_t* offsets,
+                           const int32_t* tinfo, int32_t* flag, hipStream_t s);
+
+hipError_t launch_forward_pool(const Problem& p, const void* W, const int32_t* indices,
+                               const int32_t* offsets, const float* psw, const int32_t* tinfo,
+                               float* out, hipStream_t s);
+
+struct SortBuffers {
+  int32_t* bag_of;
+  int32_t* A[4];
+  int32_t* B[4];
+  int32_t* sorted_keys;
+  int32_t* tile_base;
+  int32_t* digit_counts;
+  int32_t* digit_tot;
+};
+hipError_t launch_linearize(const Problem& p, const int32_t* offsets, int32_t* bag_of,
+                            hipStream_t s);
+hipError_t launch_sort(const Problem& p, const int32_t* indices, const int32_t* offsets,
+                       const float* psw, const int32_t* tinfo, const SortBuffers& b,
+                       const tbe_meta& meta, tbe_timer* timer, hipStream_t s);
+hipError_t launch_rle_route(const Problem& p, const int32_t* sorted_keys, int32_t* rle_tiles,
+                            int32_t* route_tiles, const tbe_meta& meta, hipStream_t s);
+
+hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* grad,
+                            const tbe_meta& meta, const int32_t* tinfo, double lr, double eps,
+                            hipStream_t s);
+hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
+                           void* partials, hipStream_t s);
+hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
+                            const void* partials, double lr, double eps, hipStream_t s);
+
+hipError_t launch_small_forward(const Problem& p, const void* W, const int32_t* indices,
+                                const int32_t* offsets, const int32_t* tinfo, float* out,
+                                uint8_t* hist, int32_t* counts, hipStream_t s);
+hipError_t launch_small_backward(const Problem& p, const float* grad, const uint8_t* hist,
+                                 const int32_t* counts, const int32_t* indices,
+                                 const int32_t* offsets, float* partials, int32_t* part_counts,
+                                 hipStream_t s);
+hipError_t launch_small_apply(const Problem& p, void* W, float* m, const int32_t* tinfo,
+                              const float* partials, const int32_t* part_counts, double lr,
+                              double eps, hipStream_t s);
+
+}  // namespace tbe

@@ -1,0 +1,80 @@
+// Small utility kernels: table-info upload through kernel arguments (no host
+// memory copy, so callers may free their host array right after the call),
+// and the opt-in validation of offsets and index ranges (page 1, checklist
+// item 5 makes the bounds check optional and off by default).
+#include <algorithm>
+
+#include "device.h"
+#include "internal.h"
+
+namespace tbe {
+
+struct TinfoChunk {
+  int32_t toff[256];
+  int32_t rows[256];
+};
+
+__global__ void fill_tinfo_kernel2(int32_t* tinfo, int32_t T, int32_t t0, int32_t n, TinfoChunk c) {
+  const int i = threadIdx.x;
+  if (i < n) {
+    tinfo[t0 + i] = c.toff[i];
+    tinfo[T + t0 + i] = c.rows[i];
+  }
+}
+
+hipError_t launch_fill_tinfo(const Problem& p, const int64_t* rows_host, int32_t* tinfo,
+                             hipStream_t s) {
+  int64_t acc = 0;
+  for (int32_t t0 = 0; t0 < p.T; t0 += 256) {
+    TinfoChunk c;
+    const int32_t n = std::min<int32_t>(256, p.T - t0);
+    for (int32_t i = 0; i < n; ++i) {
+      c.toff[i] = (int32_t)acc;
+      c.rows[i] = (int32_t)rows_host[t0 + i];
+      acc += rows_host[t0 + i];
+    }
+    hipLaunchKernelGGL(fill_tinfo_kernel2, dim3(1), dim3(256), 0, s, tinfo, p.T, t0, n, c);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// flag[0] = 1 if offsets are not a valid table-major partition of [0, N) or an
+// index lies outside its table.
+__global__ __launch_bounds__(256) void validate_kernel(const int32_t* __restrict__ indices,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ trows,
+                                                       int32_t B, int64_t nbags, int64_t N,
+                                                       int32_t* __restrict__ flag) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0 && (offsets[0] != 0 || offsets[nbags] != N)) atomicOr(flag, 1);
+  if (i >= nbags) return;
+  const int32_t a = offsets[i], e = offsets[i + 1];
+  if (a < 0 || e > N || a > e) {
+    atomicOr(flag, 1);
+    return;
+  }
+  const int32_t rows = trows[i / B];
+  bool bad = false;
+  for (int32_t j = a; j < e; ++j) bad |= (indices[j] < 0) | (indices[j] >= rows);
+  if (bad) atomicOr(flag, 1);
+}
+
+hipError_t launch_validate(const Problem& p, const int32_t* indices, const int32_t* offsets,
+                           const int32_t* tinfo, int32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, s, flag, 1);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t blocks = std::max<int64_t>(1, (p.nbags + 255) / 256);
+  hipLaunchKernelGGL(validate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, indices, offsets,
+                     tinfo + p.T, p.B, p.nbags, p.N, flag);
+  return hipGetLastError();
+}
+
+}  // namespace tbe

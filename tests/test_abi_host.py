@@ -1,0 +1,146 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/tbe.h declares, validates arguments on the host before any launch, and
+sizes metadata/workspace consistently. No compute call is made here."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+tbe = pytest.importorskip("bwd_tbe_pooled_amd", reason="libtbe.so not built")
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "tbe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(tbe_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_function():
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    lib = ctypes.CDLL(tbe.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in tbe.h but not exported"
+    assert sorted(tbe.exported_symbols()) == declared
+
+
+def test_status_strings():
+    for s in range(6):
+        assert tbe.tbe_status_str(s) and tbe.tbe_status_str(s) != "unknown status"
+    assert tbe.tbe_status_str(99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(T=2, D=16, B=8, rows=[100, 50], dtype="f32")
+    base.update(kw)
+    return tbe.Desc(**base)
+
+
+def test_small_table_eligibility_follows_the_page():
+    g = json.load(open(os.path.join(GOLDEN, "page1_thresholds.json")))["small_table"]
+    T, B = 4, 32
+    ok = dict(T=T, D=128, B=B, rows=[g["E_max"]] * T, dtype="f16")
+    N_ok = g["L_min"] * T * B
+    assert tbe.tbe_select_path(tbe.Desc(**ok), N_ok, False) == tbe.TBE_PATH_SMALL_TABLE
+    # each violated condition falls back to the generic path
+    cases = [
+        (dict(ok, rows=[g["E_max"] + 1] + [g["E_max"]] * (T - 1)), N_ok, False),
+        (dict(ok, D=g["D_min"] - 1), N_ok, False),
+        (dict(ok, D=g["D_max"] + 1), N_ok, False),
+        (ok, N_ok - 1, False),                                  # average L just below 64
+        (dict(ok, dtype="bf16"), N_ok, False),
+        (dict(ok, dtype="f32"), N_ok, False),
+        (ok, N_ok, True),                                       # per-sample weights
+        (dict(ok, flags=tbe.TBE_FLAG_FORCE_GENERIC), N_ok, False),
+    ]
+    for kw, N, w in cases:
+        assert tbe.tbe_select_path(tbe.Desc(**kw), N, w) == tbe.TBE_PATH_GENERIC, (kw, N, w)
+    assert tbe.tbe_select_path(tbe.Desc(**dict(ok, D=g["D_min"])), N_ok, False) == 1
+    assert tbe.tbe_select_path(tbe.Desc(**dict(ok, rows=[1] * T)), N_ok, False) == 1
+
+
+def test_bad_descriptions_are_rejected():
+    assert tbe.tbe_select_path(_desc(), 10, False) == tbe.TBE_PATH_GENERIC
+    for kw in [dict(T=0, rows=[]), dict(D=0), dict(B=-1), dict(rows=[100, 0]),
+               dict(flags=0x80), dict(short_max=-1), dict(chunk=-3)]:
+        with pytest.raises(tbe.TbeError) as e:
+            tbe.tbe_select_path(_desc(**kw), 10, False)
+        assert e.value.status == tbe.TBE_ERR_ARG, kw
+    # int32 limits (page 1, checklist item 6): sum of rows and N below 2^31
+    with pytest.raises(tbe.TbeError) as e:
+        tbe.tbe_select_path(_desc(rows=[2 ** 30, 2 ** 30]), 10, False)
+    assert e.value.status == tbe.TBE_ERR_UNSUPPORTED
+    with pytest.raises(tbe.TbeError) as e:
+        tbe.tbe_select_path(_desc(), 2 ** 31, False)
+    assert e.value.status == tbe.TBE_ERR_UNSUPPORTED
+    with pytest.raises(tbe.TbeError) as e:
+        tbe.tbe_select_path(_desc(D=4099), 10, False)   # odd D beyond 4 passes of 64 lanes
+    assert e.value.status == tbe.TBE_ERR_UNSUPPORTED
+
+
+def test_meta_capacities_bound_the_run_structure():
+    N = 100_000
+    caps = dict(zip(tbe.META_FIELDS, tbe.tbe_meta_capacity(_desc(), N, True)))
+    assert caps["counts"] == 8
+    assert caps["run_keys"] == min(N, 150) and caps["run_offsets"] == caps["run_keys"] + 1
+    assert caps["sorted_pos"] == caps["sorted_bag"] == caps["sorted_psw"] == N
+    assert caps["long_runs"] == N // 256 and caps["long_chunk_begin"] == N // 256 + 1
+    # sum of ceil(SL/C) over long runs <= N/C + number of long runs
+    assert caps["chunk_run"] == caps["chunk_start"] == N // 256 + N // 256
+    assert caps["hist"] == 0
+    unw = dict(zip(tbe.META_FIELDS, tbe.tbe_meta_capacity(_desc(), N, False)))
+    assert unw["sorted_psw"] == 0
+    small = tbe.Desc(T=3, D=128, B=10, rows=[64] * 3, dtype="f16")
+    sc = dict(zip(tbe.META_FIELDS, tbe.tbe_meta_capacity(small, 64 * 30, False)))
+    assert sc["hist"] == 3 * 10 * 64 and sc["sorted_pos"] == 0
+
+
+def test_workspace_sizes_grow_with_the_operation():
+    d = _desc()
+    N = 50_000
+    f = tbe.tbe_workspace_bytes(d, N, False, tbe.TBE_OP_FORWARD)
+    fp = tbe.tbe_workspace_bytes(d, N, False, tbe.TBE_OP_FORWARD_PREPROCESS)
+    b = tbe.tbe_workspace_bytes(d, N, False, tbe.TBE_OP_BACKWARD)
+    bs = tbe.tbe_workspace_bytes(d, N, False, tbe.TBE_OP_BACKWARD_SELF)
+    assert 0 < f < fp and 0 < b < bs and fp < bs
+    assert tbe.tbe_workspace_bytes(d, N, False, 17) == 0
+    assert tbe.tbe_workspace_bytes(_desc(D=0), N, False, tbe.TBE_OP_FORWARD) == 0
+
+
+def test_calls_reject_bad_arguments_before_any_launch():
+    """Every error here is found on the host; no HIP call is reached (this
+    container has no GPU, so a launch would fail with TBE_ERR_HIP instead)."""
+    lib = tbe._lib
+    d = _desc()
+    fake = ctypes.c_void_p(256)      # never dereferenced on these paths
+    ws_small = ctypes.c_void_p(4096)
+    st = lib.tbe_forward(d.ref, fake, fake, fake, 10, None, fake, None, ws_small, 1, None)
+    assert st == tbe.TBE_ERR_WORKSPACE
+    st = lib.tbe_forward(d.ref, None, fake, fake, 10, None, fake, None, ws_small, 1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG
+    st = lib.tbe_forward(None, fake, fake, fake, 10, None, fake, None, ws_small, 1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG
+    bad = _desc(flags=0x100)
+    st = lib.tbe_forward(bad.ref, fake, fake, fake, 10, None, fake, None, ws_small, 1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG
+    # meta with missing arrays
+    empty_meta = tbe.tbe_meta()
+    st = lib.tbe_preprocess(d.ref, fake, fake, 10, None, ctypes.byref(empty_meta), ws_small,
+                            1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG
+    st = lib.tbe_backward_adagrad(d.ref, fake, None, fake, fake, fake, 10, None, None, 0.01,
+                                  1e-8, ws_small, 1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG
+    st = lib.tbe_backward_adagrad(d.ref, fake, fake, fake, fake, fake, 10, None, None, -1.0,
+                                  1e-8, ws_small, 1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG
+    # misaligned workspace
+    st = lib.tbe_forward(d.ref, fake, fake, fake, 10, None, fake, None, ctypes.c_void_p(4100),
+                         1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG

@@ -1,0 +1,141 @@
+"""Parity at the full sizes of the two large workloads, in the launch
+configuration the benchmark times: T=32, E=2M, D=128 bf16, B=131072 weighted
+with preprocessing in the forward (about 84M lookups); and the small-table
+workload T=64, E=64, D=128 f16, B=32768, L=64 (134M lookups).
+
+The oracle cannot redo 84M lookups in seconds, so:
+- the sort / RLE / routing metadata is checked by properties that define the
+  stable sort uniquely (permutation; keys non-decreasing; equal keys in
+  increasing position), exact RLE of the sorted keys, and the oracle's routing
+  of the GPU's run lengths compared element by element;
+- outputs and updated rows are checked on samples the oracle computes one by
+  one: random bags (forward) and the hottest plus random rows (backward, with
+  every lookup of each sampled row)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_common import (TOL, assert_rows_match, assert_untouched_unchanged, fresh_params,
+                              host_rows, meta_host, rel_err, run_library)
+from workloads import CONFIGS, make_batch
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bwd_tbe_pooled_amd  # noqa: F401
+
+
+def _mask(n, members):
+    mk = np.zeros(n, dtype=bool)
+    mk[members] = True
+    return mk
+
+
+def _sampled_backward(cfg, batch, keys, bags, W, m, Wrows_all, mrows_all, uk, sample_keys):
+    sel = _mask(cfg.sum_rows, sample_keys)[keys]
+    pos = np.nonzero(sel)[0]
+    sk = keys[pos]
+    order = np.argsort(sk, kind="stable")          # stable: positions stay ascending
+    pos = pos[order]
+    sub_keys = keys[pos]
+    sub_bags = bags[pos]
+    sub_psw = None if batch.psw is None else batch.psw[pos]
+    r = oracle.rle(sub_keys, np.arange(pos.size, dtype=np.int32), sub_bags, sub_psw)
+    at = np.searchsorted(uk, r["run_keys"])
+    bw = oracle.backward_adagrad(cfg.T, cfg.B, cfg.D, cfg.dtype, r["run_keys"], r["run_offsets"],
+                                 r["sorted_bag"], r["sorted_psw"], batch.grad, Wrows_all[at],
+                                 mrows_all[at], cfg.lr, cfg.eps, wkeys=r["run_keys"])
+    assert_rows_match(cfg, W, m, r["run_keys"], bw["w_new"], bw["m_new"], "sampled rows")
+
+
+def test_large_skewed_workload_full_size():
+    cfg = CONFIGS[4]
+    print("\n[full] generating the T=32 B=131072 workload", flush=True)
+    batch = make_batch(cfg)
+    keys, bags = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
+    counts_all = np.bincount(keys, minlength=cfg.sum_rows)
+    uk = np.nonzero(counts_all)[0].astype(np.int32)
+    counts = counts_all[uk]
+    W, m = fresh_params(cfg)
+    W0, m0 = W.clone(), m.clone()
+    rng = np.random.default_rng(123)
+    hot = uk[np.argsort(counts)[-12:]]
+    sample_keys = np.unique(np.concatenate([hot, rng.choice(uk, 300, replace=False)]))
+    sample_bags = rng.choice(cfg.T * cfg.B, 3000, replace=False).astype(np.int32)
+    need = np.unique(np.concatenate([sample_keys, keys[_mask(cfg.T * cfg.B, sample_bags)[bags]]]))
+    Wrows, mrows = host_rows(W0, m0, need)
+    print("[full] running the library", flush=True)
+    r = run_library(cfg, batch, W, m, meta_in_forward=True, backward_meta=True)
+
+    # forward on sampled bags
+    ob = oracle.forward_bags(cfg.D, cfg.dtype, batch.offsets, keys, batch.psw, Wrows, sample_bags,
+                             wkeys=need)
+    t, b = sample_bags // cfg.B, sample_bags % cfg.B
+    out = r["out"].view(cfg.B, cfg.T, cfg.D)
+    got = out[torch.from_numpy(b.astype(np.int64)).cuda(),
+              torch.from_numpy(t.astype(np.int64)).cuda()].cpu().numpy()
+    err = rel_err(got, ob)
+    assert err <= TOL[cfg.dtype], f"forward rel err {err:.3g}"
+
+    # metadata by defining properties and the oracle's routing
+    print("[full] checking metadata", flush=True)
+    h = meta_host(r["meta"], 0)
+    N = keys.size
+    sp = h["sorted_pos"]
+    seen = np.zeros(N, dtype=bool)
+    seen[sp] = True
+    assert seen.all()                                             # a permutation
+    ks = keys[sp]
+    d = np.diff(ks)
+    assert (d >= 0).all()                                         # sorted by key
+    assert (np.diff(sp)[d == 0] > 0).all()                        # ties keep position order
+    np.testing.assert_array_equal(h["sorted_bag"], bags[sp])
+    np.testing.assert_array_equal(h["sorted_psw"].view(np.uint32), batch.psw[sp].view(np.uint32))
+    heads = np.concatenate([[0], np.nonzero(d)[0] + 1])
+    np.testing.assert_array_equal(h["run_offsets"], np.concatenate([heads, [N]]))
+    np.testing.assert_array_equal(h["run_keys"], ks[heads])
+    np.testing.assert_array_equal(h["run_keys"], uk)
+    route = oracle.route(h["run_offsets"], 256, 256)
+    for name in ("short_runs", "long_runs", "long_chunk_begin", "chunk_run", "chunk_start"):
+        np.testing.assert_array_equal(h[name], route[name], err_msg=name)
+    print(f"[full] U={uk.size} long={route['long_runs'].size} chunks={route['chunk_run'].size}",
+          flush=True)
+
+    # backward on sampled rows, then untouched rows
+    _sampled_backward(cfg, batch, keys, bags, W, m, Wrows, mrows, need, sample_keys)
+    assert_untouched_unchanged(W0, W, m0, m, uk)
+
+
+def test_small_table_workload_full_size():
+    cfg = CONFIGS[5]
+    print("\n[full] generating the T=64 B=32768 small-table workload", flush=True)
+    batch = make_batch(cfg)
+    W, m = fresh_params(cfg)
+    W0, m0 = W.clone(), m.clone()
+    allk = np.arange(cfg.sum_rows, dtype=np.int32)
+    Wrows, mrows = host_rows(W0, m0, allk)
+    r = run_library(cfg, batch, W, m, meta_in_forward=True, backward_meta=True)
+    assert r["path"] == 1
+    rng = np.random.default_rng(5)
+    sample_bags = rng.choice(cfg.T * cfg.B, 2000, replace=False).astype(np.int32)
+    keys, bags = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
+    ob = oracle.forward_bags(cfg.D, cfg.dtype, batch.offsets, keys, None, Wrows, sample_bags,
+                             wkeys=allk)
+    t, b = sample_bags // cfg.B, sample_bags % cfg.B
+    out = r["out"].view(cfg.B, cfg.T, cfg.D)
+    got = out[torch.from_numpy(b.astype(np.int64)).cuda(),
+              torch.from_numpy(t.astype(np.int64)).cuda()].cpu().numpy()
+    assert rel_err(got, ob) <= TOL[cfg.dtype]
+    hist = r["meta"]["hist"].cpu().numpy().reshape(cfg.T * cfg.B, 64)
+    for i in sample_bags[:500]:
+        ref = np.bincount(batch.indices[batch.offsets[i]:batch.offsets[i + 1]], minlength=64)
+        np.testing.assert_array_equal(hist[i], ref)
+    assert int(r["meta"]["counts"][4]) == 0
+    sample_keys = np.sort(rng.choice(cfg.sum_rows, 48, replace=False)).astype(np.int32)
+    _sampled_backward(cfg, batch, keys, bags, W, m, Wrows, mrows, allk, sample_keys)
+    assert_untouched_unchanged(W0, W, m0, m, allk)

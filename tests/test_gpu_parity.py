@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs. Metadata must match bit for bit; pooled outputs and
+updated weights within the dtype's tolerance (1e-5 f32, 2e-3 f16, 1e-2 bf16,
+max relative error floored at the row rms); optimizer state within 1e-5;
+untouched rows bitwise unchanged."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_common import (TOL, assert_meta_equal, assert_rows_match,
+                              assert_untouched_unchanged, fresh_params, host_rows,
+                              make_desc, meta_host, oracle_all, rel_err, run_library)
+from tests.helpers import TOL as _TOL  # noqa: F401
+from workloads import CONFIGS, Config, make_batch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bwd_tbe_pooled_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _full_check(cfg, batch, *, meta_in_forward, backward_meta=True, S=0, C=0, m0="zeros"):
+    print(f"\n[parity] {cfg.name} T={cfg.T} B={cfg.B} D={cfg.D} {cfg.dtype} N={batch.indices.size} "
+          f"S={S or 256} C={C or 256} meta_fwd={meta_in_forward} meta_bwd={backward_meta}",
+          flush=True)
+    W, m = fresh_params(cfg, m0)
+    W0, m0t = W.clone(), m.clone()
+    keys_all, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
+    uk = np.unique(keys_all)
+    Wrows, mrows = host_rows(W0, m0t, uk)
+    r = run_library(cfg, batch, W, m, meta_in_forward=meta_in_forward,
+                    backward_meta=backward_meta, S=S, C=C)
+    pre, out, bw = oracle_all(cfg, batch, Wrows, mrows, uk, S or 256, C or 256)
+    err = rel_err(r["out"].cpu().numpy(), out)
+    assert err <= TOL[cfg.dtype], f"forward rel err {err:.3g}"
+    if r["path"] == 0:
+        assert_meta_equal(meta_host(r["meta"], 0), pre)
+    assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], cfg.name)
+    assert_untouched_unchanged(W0, W, m0t, m, uk)
+    return r, pre
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_config_generic_full(k):
+    cfg = CONFIGS[k]
+    batch = make_batch(cfg)
+    _full_check(cfg, batch, meta_in_forward=False, backward_meta=False)
+
+
+def test_config1_metadata_reused_from_preprocess():
+    cfg = CONFIGS[1]
+    _full_check(cfg, make_batch(cfg), meta_in_forward=False, backward_meta=True)
+
+
+def test_config4_reduced_batch_full_compare():
+    cfg = CONFIGS[4]
+    batch = make_batch(cfg, B=2048)
+    _full_check(batch.cfg, batch, meta_in_forward=True, backward_meta=True)
+
+
+def test_config2_fp64_partials_with_small_chunks():
+    """f32 weights accumulate and keep chunk partials in f64; small S/C put
+    many runs on the chunked path."""
+    cfg = CONFIGS[2]
+    batch = make_batch(cfg, B=1024)
+    _full_check(batch.cfg, batch, meta_in_forward=True, S=4, C=3)
+
+
+def test_nonzero_initial_state():
+    cfg = CONFIGS[3]
+    batch = make_batch(cfg, B=256)
+    _full_check(batch.cfg, batch, meta_in_forward=True, m0="uniform")
+
+
+# --- edge cases ---------------------------------------------------------------
+
+def _custom(T, B, D, rows, dtype, lengths, indices, psw=None, seed=0):
+    rng = np.random.default_rng(seed)
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    cfg = Config("edge", T=T, B=B, D=D, rows=tuple(rows), dtype=dtype, bag=("fixed", 0),
+                 index=("uniform",), weighted=psw is not None, preprocess_in_forward=True,
+                 seed=seed)
+    from workloads import Batch
+    grad = rng.standard_normal((B, T * D)).astype(np.float32)
+    return cfg, Batch(cfg=cfg, indices=np.asarray(indices, dtype=np.int32), offsets=offsets,
+                      psw=None if psw is None else np.asarray(psw, dtype=np.float32), grad=grad)
+
+
+@pytest.mark.parametrize("sl", [255, 256, 257, 511, 512, 513])
+def test_segment_lengths_around_the_threshold(sl):
+    """One hot row hit exactly sl times, spread over bags, among cold rows."""
+    rng = np.random.default_rng(sl)
+    T, B, D = 2, 600, 16
+    rows = [5000, 3000]
+    lengths = rng.integers(1, 4, size=T * B)
+    N = int(lengths.sum())
+    idx = rng.integers(0, 3000, size=N)
+    hot = rng.choice(int(lengths[:B].sum()), size=sl, replace=False)
+    idx[hot] = 4242
+    cfg, batch = _custom(T, B, D, rows, "f16" if sl % 2 else "bf16", lengths, idx,
+                         psw=rng.random(N), seed=sl)
+    r, pre = _full_check(cfg, batch, meta_in_forward=True)
+    u = int(np.searchsorted(pre["run_keys"], 4242))
+    assert pre["run_keys"][u] == 4242 and np.diff(pre["run_offsets"])[u] == sl
+    assert (u in pre["long_runs"]) == (sl >= 256)
+
+
+def test_every_lookup_on_one_row():
+    T, B, D = 1, 4000, 128
+    lengths = np.full(B, 7)
+    cfg, batch = _custom(T, B, D, [100], "bf16", lengths, np.full(lengths.sum(), 17),
+                         psw=np.random.default_rng(1).random(lengths.sum()))
+    r, pre = _full_check(cfg, batch, meta_in_forward=True)
+    assert pre["U"] == 1 and pre["chunk_run"].size == -(-lengths.sum() // 256)
+
+
+def test_empty_bags_and_all_empty_batch():
+    rng = np.random.default_rng(3)
+    T, B, D = 3, 500, 3
+    lengths = rng.integers(0, 5, size=T * B)
+    lengths[rng.random(T * B) < 0.6] = 0
+    idx = rng.integers(0, 40, size=lengths.sum())
+    cfg, batch = _custom(T, B, D, [40, 41, 42], "f32", lengths, idx)
+    r, _ = _full_check(cfg, batch, meta_in_forward=True)
+    out = r["out"].cpu().numpy().reshape(B, T, D)
+    L = lengths.reshape(T, B)
+    for t in range(T):
+        assert not out[L[t] == 0, t].any()
+    cfg0, batch0 = _custom(2, 64, 16, [10, 10], "f32", np.zeros(128, dtype=np.int64), [])
+    r0, pre0 = _full_check(cfg0, batch0, meta_in_forward=True)
+    assert pre0["U"] == 0 and not r0["out"].any()
+
+
+@pytest.mark.parametrize("D", [1, 3, 24, 256, 1000])
+def test_odd_dimensions(D):
+    rng = np.random.default_rng(D)
+    T, B = 2, 300
+    lengths = rng.poisson(6, size=T * B)
+    idx = rng.integers(0, 30, size=lengths.sum())
+    cfg, batch = _custom(T, B, D, [30, 50], "f16" if D % 2 == 0 else "f32", lengths, idx,
+                         psw=rng.random(lengths.sum()), seed=D)
+    _full_check(cfg, batch, meta_in_forward=True, S=8, C=5)
+
+
+def test_unit_weights_equal_unweighted_bitwise():
+    cfg = CONFIGS[3]
+    batch = make_batch(cfg, B=512)
+    outs = []
+    for psw in (None, np.ones(batch.indices.size, dtype=np.float32)):
+        b = make_batch(cfg, B=512)
+        b.psw = psw
+        W, m = fresh_params(batch.cfg)
+        r = run_library(batch.cfg, b, W, m, meta_in_forward=True)
+        outs.append((r["out"].clone(), W.clone(), m.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.float16 else a,
+                           b.view(torch.int16) if b.dtype == torch.float16 else b)
+
+
+def test_runs_are_deterministic():
+    cfg = CONFIGS[4]
+    batch = make_batch(cfg, B=4096)
+    res = []
+    for _ in range(2):
+        W, m = fresh_params(batch.cfg)
+        r = run_library(batch.cfg, batch, W, m, meta_in_forward=True)
+        res.append((r["out"], W.view(torch.int16), m))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
+
+
+def test_validate_flag_reports_bad_input_before_other_work():
+    import bwd_tbe_pooled_amd as tbe
+    cfg = CONFIGS[1]
+    batch = make_batch(cfg)
+    desc = make_desc(cfg, flags=tbe.TBE_FLAG_VALIDATE)
+    W, m = fresh_params(cfg)
+    out = torch.zeros((cfg.B, cfg.T * cfg.D), device="cuda")
+    ws = tbe.workspace(desc, batch.indices.size, False, tbe.TBE_OP_FORWARD)
+    off = torch.from_numpy(batch.offsets).cuda()
+    good = torch.from_numpy(batch.indices).cuda()
+    tbe.tbe_forward(desc, W, good, off, None, out, None, ws)      # valid input passes
+    bad = good.clone()
+    bad[5] = cfg.rows[0]                                            # one past the table
+    out2 = torch.zeros_like(out)
+    with pytest.raises(tbe.TbeError) as e:
+        tbe.tbe_forward(desc, W, bad, off, None, out2, None, ws)
+    assert e.value.status == tbe.TBE_ERR_INDEX_RANGE
+    assert not out2.any()                                           # nothing else ran
+    bad_off = off.clone()
+    bad_off[3] = bad_off[4] + 1                                     # decreasing offsets
+    with pytest.raises(tbe.TbeError) as e:
+        tbe.tbe_forward(desc, W, good, bad_off, None, out2, None, ws)
+    assert e.value.status == tbe.TBE_ERR_INDEX_RANGE
+
+
+def test_stage_timer_counts_each_stage():
+    import bwd_tbe_pooled_amd as tbe
+    cfg = CONFIGS[3]
+    batch = make_batch(cfg, B=1024)
+    timer = tbe.Timer(8)
+    desc = make_desc(batch.cfg, timer=timer)
+    W, m = fresh_params(batch.cfg)
+    from tests.gpu_common import device_batch
+    dev = device_batch(batch)
+    N = batch.indices.size
+    meta = tbe.Meta(desc, N, False)
+    out = torch.empty((batch.cfg.B, cfg.T * cfg.D), device="cuda")
+    ws = tbe.workspace(desc, N, False, tbe.TBE_OP_FORWARD_PREPROCESS)
+    tbe.tbe_forward(desc, W, dev["indices"], dev["offsets"], None, out, meta, ws)
+    wsb = tbe.workspace(desc, N, False, tbe.TBE_OP_BACKWARD)
+    tbe.tbe_backward_adagrad(desc, W, m, dev["grad"], dev["indices"], dev["offsets"], None, meta,
+                             0.01, 1e-8, wsb)
+    t = timer.read()
+    for st in ("fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "bwd_long", "bwd_apply"):
+        assert t[st][1] == 1 and t[st][0] > 0, st
+    assert t["small_fwd"][1] == 0

@@ -1,0 +1,85 @@
+"""GPU parity of the small-table histogram path (E <= 64, 64 <= D <= 128,
+L >= 64, f16, unweighted): per-bag counts bit-exact against the oracle's
+histogram; outputs and updated rows against the oracle's plain definition."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_common import (TOL, assert_rows_match, assert_untouched_unchanged, fresh_params,
+                              host_rows, oracle_all, rel_err, run_library)
+from workloads import CONFIGS, Batch, Config, make_batch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bwd_tbe_pooled_amd  # noqa: F401
+
+
+def _check(cfg, batch, meta_in_forward=True, backward_meta=True, expect_saturated=False):
+    print(f"\n[small-table] T={cfg.T} B={cfg.B} D={cfg.D} E={max(cfg.rows)} N={batch.indices.size} "
+          f"meta_fwd={meta_in_forward} meta_bwd={backward_meta}", flush=True)
+    W, m = fresh_params(cfg)
+    W0, m0 = W.clone(), m.clone()
+    keys, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
+    uk = np.unique(keys)
+    Wrows, mrows = host_rows(W0, m0, uk)
+    r = run_library(cfg, batch, W, m, meta_in_forward=meta_in_forward, backward_meta=backward_meta)
+    assert r["path"] == 1
+    pre, out, bw = oracle_all(cfg, batch, Wrows, mrows, uk)
+    err = rel_err(r["out"].cpu().numpy(), out)
+    assert err <= TOL[cfg.dtype], f"forward rel err {err:.3g}"
+    H = oracle.histogram(cfg.T, cfg.B, 64, cfg.rows, batch.indices, batch.offsets)
+    hist = r["meta"]["hist"].cpu().numpy().reshape(cfg.T, cfg.B, 64)
+    np.testing.assert_array_equal(hist, np.minimum(H, 255))
+    assert int(r["meta"]["counts"][4]) == int(expect_saturated)
+    assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], "small-table")
+    assert_untouched_unchanged(W0, W, m0, m, uk)
+    return r
+
+
+def _cfg(T, B, D, E, L, seed):
+    return Config("small", T=T, B=B, D=D, rows=(E,) * T if isinstance(E, int) else tuple(E),
+                  dtype="f16", bag=("fixed", L), index=("uniform",), weighted=False,
+                  preprocess_in_forward=False, seed=seed)
+
+
+def test_config5_reduced_batch():
+    cfg = CONFIGS[5]
+    batch = make_batch(cfg, B=512)
+    _check(batch.cfg, batch)
+
+
+def test_backward_without_saved_counts():
+    cfg = CONFIGS[5]
+    batch = make_batch(cfg, B=300)
+    _check(batch.cfg, batch, meta_in_forward=True, backward_meta=False)
+
+
+@pytest.mark.parametrize("D,E", [(64, 64), (96, 40), (128, 1), (100, 64)])
+def test_shapes(D, E):
+    cfg = _cfg(3, 200, D, E, 70, seed=D + E)
+    batch = make_batch(cfg)
+    _check(cfg, batch)
+
+
+def test_saturated_counts_are_recounted():
+    """Bags with more than 255 lookups of one row: the saved uint8 counts
+    saturate, the flag is raised, and the backward recounts from indices."""
+    rng = np.random.default_rng(7)
+    T, B, D, E = 2, 96, 128, 64
+    lengths = np.full(T * B, 80)
+    lengths[5] = 300
+    lengths[B + 7] = 2500                      # > 2048: beyond f16-exact counts
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    idx = rng.integers(0, E, size=offsets[-1]).astype(np.int32)
+    idx[offsets[5]:offsets[6]] = 3
+    idx[offsets[B + 7]:offsets[B + 8]] = 9
+    cfg = _cfg(T, B, D, E, 80, seed=11)
+    grad = rng.standard_normal((B, T * D)).astype(np.float32)
+    batch = Batch(cfg=cfg, indices=idx, offsets=offsets, psw=None, grad=grad)
+    _check(cfg, batch, expect_saturated=True)

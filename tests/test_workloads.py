@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from workloads import CONFIGS, make_batch, weight_rows, full_weights, state_rows
+from workloads import CONFIGS, init_state, init_weights, make_batch
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -51,17 +51,14 @@ def test_bag_length_distributions():
     assert np.all(np.diff(b5.offsets) == 64)
 
 
-def test_weight_rows_are_counter_based():
-    cfg = CONFIGS[3]
-    keys = torch.tensor([0, 5, 999_999, 15_999_999])
-    w = weight_rows(cfg, keys)
-    assert w.dtype == torch.float16 and w.shape == (4, 128)
-    w2 = weight_rows(cfg, keys[[2, 0]])
-    assert torch.equal(w[[2, 0]], w2)
-    wf = w.float()
-    assert wf.abs().max() <= 0.01 and wf.std() > 0.004
-    small = CONFIGS[1]
-    full = full_weights(small, "cpu", chunk_rows=300)
-    assert torch.equal(full[[3, 1500]], weight_rows(small, torch.tensor([3, 1500])))
-    m = state_rows(small, torch.arange(10), m0="uniform")
-    assert m.min() >= 0 and m.max() < 1 and m.unique().numel() == 10
+def test_weights_and_state_are_seeded_and_in_range():
+    cfg = CONFIGS[1]
+    w1 = init_weights(cfg, "cpu", chunk_rows=300)
+    w2 = init_weights(cfg, "cpu", chunk_rows=300)
+    assert w1.dtype == torch.float32 and w1.shape == (2000, 16) and torch.equal(w1, w2)
+    assert w1.abs().max() <= 0.01 and w1.std() > 0.004
+    w16 = init_weights(CONFIGS[5], "cpu")
+    assert w16.dtype == torch.float16 and w16.shape == (64 * 64, 128)
+    m = init_state(cfg, "cpu", m0="uniform")
+    assert m.min() >= 0 and m.max() < 1 and m.unique().numel() > 1900
+    assert not init_state(cfg, "cpu").any()

@@ -21,10 +21,8 @@ values/lengths):
   W        [sum(E), D] weights, tables stacked in order; dtype f32/f16/bf16
   m        float32 [sum(E)] row-wise Adagrad state
 
-Weights and optimizer state are not drawn from the numpy stream: every element
-comes from a counter-based integer hash of (seed, row key, column), so any row
-can be regenerated on the host or the device without materialising the table
-(the config with 64M rows holds 16 GiB of weights).
+Weights and optimizer state are drawn on the device that holds them (the
+table of the largest workload is 16 GiB), with torch's seeded generator.
 """
 from __future__ import annotations
 
@@ -33,8 +31,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Config", "CONFIGS", "Batch", "make_batch", "weight_rows",
-           "full_weights", "state_rows", "full_state", "table_offsets"]
+__all__ = ["Config", "CONFIGS", "Batch", "make_batch", "init_weights", "init_state",
+           "torch_dtype", "table_offsets"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -176,80 +174,41 @@ def make_batch(cfg: Config, *, with_grad: bool = True, B: Optional[int] = None,
 
 
 # ---------------------------------------------------------------------------
-# Counter-based weights / state. Integer hashing is exact on every device; the
-# final affine map uses two IEEE float32 operations (multiply, subtract), each
-# correctly rounded on CPU and GPU alike, then a round-to-nearest-even cast.
+# Weights and optimizer state: drawn on the target device with torch's seeded
+# generator (uniform in float32, then rounded to nearest even into the weight
+# type). Large tables (16 GiB at 64M rows) are filled in slices of rows so the
+# float32 staging stays small. Callers that need the initial values of some
+# rows on the host (the oracle) copy them from the tensor before any update.
 # ---------------------------------------------------------------------------
-_M32 = 0xFFFFFFFF
-
-
-def _mul32(x, c: int):
-    """(x * c) mod 2^32 for int64 tensors holding values < 2^32, without any
-    intermediate leaving int64 range (split into 16-bit halves)."""
-    lo = x & 0xFFFF
-    hi = x >> 16
-    return ((lo * c) + (((hi * c) & 0xFFFF) << 16)) & _M32
-
-
-def _mix32(x):
-    x = x ^ (x >> 16)
-    x = _mul32(x, 0x7FEB352D)
-    x = x ^ (x >> 15)
-    x = _mul32(x, 0x846CA68B)
-    x = x ^ (x >> 16)
-    return x
-
-
-def _uniform_rows(keys, D: int, salt: int, lo: float, hi: float):
-    import torch
-    keys = keys.to(torch.int64)
-    h1 = _mix32((keys ^ (salt & _M32)) & _M32)
-    cols = torch.arange(D, dtype=torch.int64, device=keys.device)
-    h = _mix32(h1[:, None] ^ _mul32(cols[None, :] + 1, 0x85EBCA6B))
-    u = (h >> 8).to(torch.float32) * (2.0 ** -24)          # exact, in [0, 1)
-    return u * (hi - lo) + lo   # two float32 ops: mul then add, each RNE
-
-
 _TORCH_DTYPES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 
 
-def weight_rows(cfg: Config, keys, device=None):
-    """Initial weights of the stacked rows `keys` (int tensor), dtype of cfg:
-    U(-0.01, 0.01) in float32, then cast (round to nearest even)."""
+def torch_dtype(cfg: Config):
     import torch
-    keys = torch.as_tensor(keys, device=device)
-    w = _uniform_rows(keys, cfg.D, 0x5EED0000 + cfg.seed, -0.01, 0.01)
-    return w.to(getattr(torch, _TORCH_DTYPES[cfg.dtype]))
+    return getattr(torch, _TORCH_DTYPES[cfg.dtype])
 
 
-def full_weights(cfg: Config, device, chunk_rows: int = 1 << 20):
+def init_weights(cfg: Config, device, chunk_rows: int = 1 << 20):
+    """W [sum(E), D] ~ U(-0.01, 0.01), deterministic for a device and seed."""
     import torch
     E = cfg.sum_rows
-    out = torch.empty((E, cfg.D), dtype=getattr(torch, _TORCH_DTYPES[cfg.dtype]),
-                      device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(0x5EED0000 + cfg.seed)
+    out = torch.empty((E, cfg.D), dtype=torch_dtype(cfg), device=device)
     for a in range(0, E, chunk_rows):
         b = min(E, a + chunk_rows)
-        out[a:b] = weight_rows(cfg, torch.arange(a, b, device=device), device)
+        tmp = torch.empty((b - a, cfg.D), dtype=torch.float32, device=device)
+        tmp.uniform_(-0.01, 0.01, generator=gen)
+        out[a:b] = tmp
     return out
 
 
-def state_rows(cfg: Config, keys, device=None, m0: str = "zeros"):
-    """Initial row-wise Adagrad state: zeros, or U(0, 1) when m0 == "uniform"."""
-    import torch
-    keys = torch.as_tensor(keys, device=device)
-    if m0 == "zeros":
-        return torch.zeros(keys.shape[0], dtype=torch.float32, device=keys.device)
-    u = _uniform_rows(keys, 1, 0xACC00000 + cfg.seed, 0.0, 1.0)
-    return u[:, 0].contiguous()
-
-
-def full_state(cfg: Config, device, m0: str = "zeros", chunk_rows: int = 1 << 22):
+def init_state(cfg: Config, device, m0: str = "zeros"):
+    """Row-wise Adagrad state [sum(E)]: zeros, or U(0, 1) when m0 == "uniform"."""
     import torch
     E = cfg.sum_rows
     if m0 == "zeros":
         return torch.zeros(E, dtype=torch.float32, device=device)
-    out = torch.empty(E, dtype=torch.float32, device=device)
-    for a in range(0, E, chunk_rows):
-        b = min(E, a + chunk_rows)
-        out[a:b] = state_rows(cfg, torch.arange(a, b, device=device), device, m0)
-    return out
+    gen = torch.Generator(device=device)
+    gen.manual_seed(0xACC00000 + cfg.seed)
+    return torch.empty(E, dtype=torch.float32, device=device).uniform_(0.0, 1.0, generator=gen)
