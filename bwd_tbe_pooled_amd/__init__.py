@@ -14,7 +14,8 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtbe.so")
+# TBE_LIBRARY may name another build of the same library (development builds).
+LIB_PATH = os.environ.get("TBE_LIBRARY") or os.path.join(_HERE, "libtbe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bwd_tbe_pooled_amd.build`")

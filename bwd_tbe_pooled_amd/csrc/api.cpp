@@ -145,6 +145,7 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
     if (generic) {
       const size_t acc = p.wdtype == TBE_F32 ? 8 : 4;
       L.partials = take(acc * (size_t)p.cap_chunks * (size_t)p.D);
+      L.sched = take(sizeof(int32_t) * long_schedule_ints(p));
     } else {
       const size_t parts = (size_t)p.T * (size_t)p.small_splits * kSmallE;
       L.partials = take(sizeof(float) * parts * (size_t)p.D);
@@ -426,7 +427,7 @@ tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
   TBE_TRY_HIP(launch_bwd_short(p, W, momentum, grad_out, m, tinfo, lr, eps, s));
   timer_end(desc->timer, TBE_STAGE_BWD_SHORT, s);
   timer_begin(desc->timer, TBE_STAGE_BWD_LONG, s);
-  TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, s));
+  TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, at<int32_t>(ws, L.sched), s));
   timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
   timer_begin(desc->timer, TBE_STAGE_BWD_APPLY, s);
   TBE_TRY_HIP(launch_bwd_apply(p, W, momentum, m, parts, lr, eps, s));

@@ -19,6 +19,19 @@
 //
 // The gradient row of lookup k is grad[b, t*D .. t*D+D-1] where sorted_bag[k]
 // = t*B + b; every lookup of a run shares its table t.
+//
+// Memory access on gfx950:
+// - Gradient rows are f32 and read at random; a lane reads 16 contiguous bytes
+//   and consecutive lanes read consecutive bytes, so each load instruction
+//   covers whole 128-byte lines (D = 128: 16 lanes x 16 B x 2 passes per row).
+//   Random 512-byte rows served from L2 move about twice as fast this way as
+//   with 32 bytes per lane split over two instructions.
+// - Long-run chunks are executed in a schedule, not in chunk order: chunks are
+//   bucketed per XCD (a contiguous block of tables per XCD) and ordered by the
+//   batch position of their first lookup. Lookups of a run are in batch order,
+//   so concurrent chunks on one XCD read gradient rows of nearby bags, which
+//   its L2 keeps. Each chunk still writes its own partial, so the result does
+//   not depend on the schedule.
 #include "adagrad.h"
 #include "device.h"
 #include "internal.h"
@@ -48,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
     typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
   using ACC = typename acc_of<WT>::type;
   using GRAW = typename raw_vec<float, V>::type;
-  constexpr int UNROLL = PMAX == 1 ? 4 : 1;
+  constexpr int UNROLL = PMAX <= 2 ? 4 : 1;
   const int lane = lane_id();
   const int slot = lane >> log2G;
   const int col = lane & (G - 1);
@@ -103,24 +116,30 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
   }
 }
 
+// Workgroup w serves the schedule list of XCD (w mod 8); the grid is a
+// multiple of 8, so every list is served whatever the dispatch order.
 template <int V, int PMAX, typename ACC, bool WEIGHTED>
 __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
-    const float* __restrict__ grad, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ chunk_run, const int32_t* __restrict__ chunk_start,
-    const int32_t* __restrict__ run_offsets, const int32_t* __restrict__ sorted_bag,
-    const float* __restrict__ sorted_psw, ACC* __restrict__ partials, int32_t T, int32_t B,
-    int32_t D, int32_t C, int32_t G, int32_t log2G, int32_t P) {
+    const float* __restrict__ grad, const int32_t* __restrict__ chunk_run,
+    const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ run_offsets,
+    const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ list_begin,
+    ACC* __restrict__ partials, int32_t T, int32_t B, int32_t D, int32_t C, int32_t G,
+    int32_t log2G, int32_t P) {
   using GRAW = typename raw_vec<float, V>::type;
-  constexpr int UNROLL = PMAX == 1 ? 4 : 1;
+  constexpr int UNROLL = PMAX <= 2 ? 4 : 1;
   const int lane = lane_id();
   const int slot = lane >> log2G;
   const int col = lane & (G - 1);
   const int NS = kWave >> log2G;
-  const int64_t n_chunks = counts[3];
-  const int64_t gwave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+  const int x = blockIdx.x % kXcds;
+  const int64_t first = list_begin[x];
+  const int64_t n_items = list_begin[x + 1] - first;
+  const int64_t gwave = (int64_t)(blockIdx.x / kXcds) * kWaves + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)(gridDim.x / kXcds) * kWaves;
 
-  for (int64_t c = gwave; c < n_chunks; c += nwaves) {
+  for (int64_t it = gwave; it < n_items; it += nwaves) {
+    const int32_t c = order[first + it];
     const int32_t u = chunk_run[c];
     const int32_t k0 = chunk_start[c];
     const int32_t kend = run_offsets[u + 1];
@@ -173,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
 #pragma unroll
       for (int v = 0; v < V; ++v) acc[p][v] = across_slots_sum<ACC>(acc[p][v], G);
     if (slot == 0) {
-      ACC* out = partials + c * D;
+      ACC* out = partials + (int64_t)c * D;
 #pragma unroll
       for (int p = 0; p < PMAX; ++p) {
         const int e = (p * G + col) * V;
@@ -230,6 +249,74 @@ __global__ __launch_bounds__(kThreads) void bwd_apply_kernel(
   }
 }
 
+// --- long-chunk schedule: bucket = (XCD of the chunk's table block, first
+// bag / 2^shift); counting sort of chunk ids into buckets. ----------------------
+constexpr int kSchedBuckets = 4096;  // per XCD
+
+__global__ void sched_zero_kernel(int32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void sched_count_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ chunk_start,
+    const int32_t* __restrict__ sorted_bag, int32_t B, int32_t T, int shift,
+    int32_t* __restrict__ hist, int32_t* __restrict__ bucket_of) {
+  const int64_t n = counts[3];
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t bag = sorted_bag[chunk_start[c]];
+    const int32_t t = bag / B, b = bag - t * B;
+    const int x = (int)(((int64_t)t * kXcds) / T);
+    const int bk = x * kSchedBuckets + (b >> shift);
+    bucket_of[c] = bk;
+    atomicAdd(&hist[bk], 1);
+  }
+}
+
+// Single workgroup: exclusive scan of the bucket counts in place; list_begin[x]
+// = first slot of XCD x's list, list_begin[8] = number of chunks.
+__global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ list_begin) {
+  __shared__ int32_t wsum[16];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  constexpr int n = kXcds * kSchedBuckets;
+  int32_t carry = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int32_t v = hist[i];
+    int32_t inc = v;
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t y = __shfl_up(inc, d);
+      if (lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = inc;
+    __syncthreads();
+    int32_t pre = 0, tot = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wave) pre += wsum[w];
+      tot += wsum[w];
+    }
+    const int32_t ex = carry + pre + inc - v;
+    hist[i] = ex;
+    if (i % kSchedBuckets == 0) list_begin[i / kSchedBuckets] = ex;
+    carry += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) list_begin[kXcds] = carry;
+}
+
+__global__ __launch_bounds__(256) void sched_scatter_kernel(const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ bucket_of,
+                                                            int32_t* __restrict__ cursor,
+                                                            int32_t* __restrict__ order) {
+  const int64_t n = counts[3];
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t pos = atomicAdd(&cursor[bucket_of[c]], 1);
+    order[pos] = (int32_t)c;
+  }
+}
+
 inline int64_t persistent_blocks(int64_t work_waves) {
   // Enough workgroups to fill 256 CUs several times over; the kernels stride.
   int64_t cap = 256 * 16;
@@ -259,18 +346,33 @@ hipError_t short_typed(const Problem& p, const RowShape& rs, void* W, float* m, 
 
 template <typename ACC, int V, int PMAX>
 hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, const tbe_meta& meta,
-                      void* partials, hipStream_t s) {
-  const dim3 grid((unsigned)persistent_blocks(p.cap_chunks));
+                      void* partials, int32_t* sched, hipStream_t s) {
+  int shift = 0;
+  while (((int64_t)(p.B - 1) >> shift) >= kSchedBuckets) ++shift;
+  int32_t* order = sched;
+  int32_t* bucket_of = order + p.cap_chunks;
+  int32_t* hist = bucket_of + p.cap_chunks;
+  int32_t* list_begin = hist + kXcds * kSchedBuckets;
+  hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, hist, kXcds * kSchedBuckets);
+  hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
+                     meta.sorted_bag, p.B, p.T, shift, hist, bucket_of);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, hist, list_begin);
+  hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, bucket_of,
+                     hist, order);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t blocks = (persistent_blocks(p.cap_chunks) + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid((unsigned)blocks);
   if (p.weighted)
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, true>), grid, dim3(kThreads), 0, s, grad,
-                       meta.counts, meta.chunk_run, meta.chunk_start, meta.run_offsets,
-                       meta.sorted_bag, meta.sorted_psw, (ACC*)partials, p.T, p.B, p.D, p.C, rs.G,
-                       rs.log2G, rs.P);
+                       meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
+                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.T, p.B, p.D, p.C,
+                       rs.G, rs.log2G, rs.P);
   else
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, false>), grid, dim3(kThreads), 0, s, grad,
-                       meta.counts, meta.chunk_run, meta.chunk_start, meta.run_offsets,
-                       meta.sorted_bag, meta.sorted_psw, (ACC*)partials, p.T, p.B, p.D, p.C, rs.G,
-                       rs.log2G, rs.P);
+                       meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
+                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.T, p.B, p.D, p.C,
+                       rs.G, rs.log2G, rs.P);
   return hipGetLastError();
 }
 
@@ -286,19 +388,44 @@ hipError_t apply_typed(const Problem& p, const RowShape& rs, void* W, float* m,
   return hipGetLastError();
 }
 
-#define TBE_DISPATCH_V(RS, CALL_V)                              \
-  do {                                                          \
-    if ((RS).V == 8) { if ((RS).P == 1) return CALL_V(8, 1); return CALL_V(8, 4); } \
-    if ((RS).V == 4) { if ((RS).P == 1) return CALL_V(4, 1); return CALL_V(4, 4); } \
-    if ((RS).V == 2) { if ((RS).P == 1) return CALL_V(2, 1); return CALL_V(2, 4); } \
-    if ((RS).P == 1) return CALL_V(1, 1);                      \
-    return CALL_V(1, 4);                                        \
+#define TBE_DISPATCH_P(VV, RS, CALL_V)          \
+  do {                                           \
+    if ((RS).P == 1) return CALL_V(VV, 1);       \
+    if ((RS).P == 2) return CALL_V(VV, 2);       \
+    return CALL_V(VV, 4);                        \
   } while (0)
+#define TBE_DISPATCH_V(RS, CALL_V)                           \
+  do {                                                       \
+    if ((RS).V == 8) TBE_DISPATCH_P(8, RS, CALL_V);          \
+    if ((RS).V == 4) TBE_DISPATCH_P(4, RS, CALL_V);          \
+    if ((RS).V == 2) TBE_DISPATCH_P(2, RS, CALL_V);          \
+    TBE_DISPATCH_P(1, RS, CALL_V);                           \
+  } while (0)
+
+// Row shape for f32 gradient rows: 16 bytes per lane, consecutive lanes on
+// consecutive bytes (whole lines per load instruction), at most 16 lanes per
+// row so that four rows are in flight per wave; wider rows take more passes.
+inline RowShape grad_row_shape(int D) {
+  int V = 4;
+  while (V > 1 && D % V != 0) V >>= 1;
+  const int per = (D + V - 1) / V;
+  int G = 1, lg = 0;
+  while (G < per && G < 16) { G <<= 1; ++lg; }
+  int P = (D + G * V - 1) / (G * V);
+  while (P > 4 && G < 64) { G <<= 1; ++lg; P = (D + G * V - 1) / (G * V); }
+  if (P > 4) return row_shape(D, 8);
+  RowShape r;
+  r.V = V;
+  r.G = G;
+  r.log2G = lg;
+  r.P = P;
+  return r;
+}
 
 template <typename WT>
 hipError_t short_for(const Problem& p, void* W, float* m, const float* grad, const tbe_meta& meta,
                      double lr, double eps, hipStream_t s) {
-  const RowShape rs = row_shape(p.D, 8);
+  const RowShape rs = grad_row_shape(p.D);
 #define CALL(VV, PP) short_typed<WT, VV, PP>(p, rs, W, m, grad, meta, lr, eps, s)
   TBE_DISPATCH_V(rs, CALL);
 #undef CALL
@@ -306,9 +433,9 @@ hipError_t short_for(const Problem& p, void* W, float* m, const float* grad, con
 
 template <typename ACC>
 hipError_t long_for(const Problem& p, const float* grad, const tbe_meta& meta, void* partials,
-                    hipStream_t s) {
-  const RowShape rs = row_shape(p.D, 8);
-#define CALL(VV, PP) long_typed<ACC, VV, PP>(p, rs, grad, meta, partials, s)
+                    int32_t* sched, hipStream_t s) {
+  const RowShape rs = grad_row_shape(p.D);
+#define CALL(VV, PP) long_typed<ACC, VV, PP>(p, rs, grad, meta, partials, sched, s)
   TBE_DISPATCH_V(rs, CALL);
 #undef CALL
 }
@@ -338,10 +465,14 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
 }
 
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
-                           void* partials, hipStream_t s) {
+                           void* partials, int32_t* sched, hipStream_t s) {
   if (p.cap_chunks == 0) return hipSuccess;
-  if (p.wdtype == TBE_F32) return long_for<double>(p, grad, meta, partials, s);
-  return long_for<float>(p, grad, meta, partials, s);
+  if (p.wdtype == TBE_F32) return long_for<double>(p, grad, meta, partials, sched, s);
+  return long_for<float>(p, grad, meta, partials, sched, s);
+}
+
+size_t long_schedule_ints(const Problem& p) {
+  return 2 * (size_t)p.cap_chunks + kXcds * kSchedBuckets + kXcds + 1;
 }
 
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,

@@ -7,7 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/tbe.h"
+#include "tbe.h"
 
 namespace tbe {
 
@@ -70,6 +70,7 @@ struct WsLayout {
   // backward
   size_t partials;     // long-run chunk partials / small-table partials
   size_t part_counts;  // small-table per-split row counts
+  size_t sched;        // long-chunk schedule (order, buckets, list bounds)
   bool has_pre, has_meta, has_partials;
 };
 
@@ -112,7 +113,8 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
                             const tbe_meta& meta, const int32_t* tinfo, double lr, double eps,
                             hipStream_t s);
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
-                           void* partials, hipStream_t s);
+                           void* partials, int32_t* sched, hipStream_t s);
+size_t long_schedule_ints(const Problem& p);  // workspace ints of the chunk schedule
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
                             const void* partials, double lr, double eps, hipStream_t s);
 
