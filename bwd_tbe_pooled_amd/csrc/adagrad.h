@@ -40,4 +40,55 @@ __device__ __forceinline__ void adagrad_row(WT* __restrict__ wrow, float* __rest
   if (col == 0) *mrow = (float)m1;
 }
 
+// The same step split in two, so that the row's weights and state can be
+// loaded before its gradient is complete (their latency then overlaps the
+// gradient gather).
+template <typename WT, int V, int PMAX>
+struct RowState {
+  typename raw_vec<WT, V>::type w[PMAX];
+  float m;
+};
+
+template <typename WT, int V, int PMAX>
+__device__ __forceinline__ void load_row_state(const WT* __restrict__ wrow,
+                                               const float* __restrict__ mrow, int col, int G,
+                                               int P, int D, RowState<WT, V, PMAX>& st) {
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+    const int e = (p * G + col) * V;
+    if (p < P && e < D) st.w[p] = load_vec<WT, V>(wrow + e);
+  }
+  st.m = *mrow;
+}
+
+template <typename WT, typename ACC, int V, int PMAX>
+__device__ __forceinline__ void apply_row_state(WT* __restrict__ wrow, float* __restrict__ mrow,
+                                                const RowState<WT, V, PMAX>& st,
+                                                ACC (&g)[PMAX][V], int col, int G, int P, int D,
+                                                ACC lr, ACC eps) {
+  using RAW = typename raw_vec<WT, V>::type;
+  ACC sq = (ACC)0;
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+    for (int v = 0; v < V; ++v) sq += g[p][v] * g[p][v];
+  sq = group_sum<ACC>(sq, G);
+  const ACC m1 = (ACC)st.m + sq / (ACC)D;
+  const ACC scale = lr / (sqrt(m1) + eps);
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p) {
+    const int e = (p * G + col) * V;
+    if (p < P && e < D) {
+      ACC w[V];
+      unpack<WT, V, ACC>(st.w[p], w);
+      RAW outv;
+      WT* o = reinterpret_cast<WT*>(&outv);
+#pragma unroll
+      for (int v = 0; v < V; ++v) store_w(&o[v], w[v] - g[p][v] * scale);
+      *reinterpret_cast<RAW*>(wrow + e) = outv;
+    }
+  }
+  if (col == 0) *mrow = (float)m1;
+}
+
 }  // namespace tbe

@@ -51,50 +51,56 @@ __device__ __forceinline__ void zero_acc(ACC (&acc)[PMAX][V]) {
     for (int v = 0; v < V; ++v) acc[p][v] = (ACC)0;
 }
 
-template <typename WT, int V, int PMAX, bool WEIGHTED>
-__global__ __launch_bounds__(kThreads) void bwd_short_kernel(
-    WT* __restrict__ W, float* __restrict__ mom, const float* __restrict__ grad,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ short_runs,
-    const int32_t* __restrict__ run_keys, const int32_t* __restrict__ run_offsets,
-    const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw, int32_t T,
-    int32_t B, int32_t D, int32_t G, int32_t log2G, int32_t P,
-    typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
-  using ACC = typename acc_of<WT>::type;
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// All row slots of a wave accumulate sorted slots [k0, k1) of one run of table
+// t: slot s takes k0+s, k0+s+NS, ...; bag ids and weights of 64 slots at a
+// time are loaded coalesced and handed to the slots with shuffles. On return
+// every slot holds the wave's sum (fixed butterfly over the slots).
+template <int V, int PMAX, typename ACC, bool WEIGHTED>
+__device__ __forceinline__ void wave_accumulate(const float* __restrict__ grad,
+                                                const int32_t* __restrict__ sorted_bag,
+                                                const float* __restrict__ sorted_psw, int32_t k0,
+                                                int32_t k1, int32_t T, int32_t B, int32_t D,
+                                                int G, int log2G, int P, ACC (&acc)[PMAX][V]) {
   using GRAW = typename raw_vec<float, V>::type;
   constexpr int UNROLL = PMAX <= 2 ? 4 : 1;
   const int lane = lane_id();
   const int slot = lane >> log2G;
   const int col = lane & (G - 1);
   const int NS = kWave >> log2G;
-  const int64_t n_short = counts[1];
-  const int64_t gwave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
-  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
-
-  for (int64_t grp = gwave; grp * NS < n_short; grp += nwaves) {
-    const int64_t i = grp * NS + slot;
-    const bool active = i < n_short;
-    const int32_t u = active ? short_runs[i] : 0;
-    const int32_t k0 = active ? run_offsets[u] : 0;
-    const int32_t k1 = active ? run_offsets[u + 1] : 0;
-    const int32_t t = active ? sorted_bag[k0] / B : 0;
-    const float* __restrict__ gt = grad + (int64_t)t * D;
-    ACC acc[PMAX][V];
-    zero_acc<ACC, V, PMAX>(acc);
-    for (int32_t k = k0; k < k1; k += UNROLL) {
+  const int32_t t = sorted_bag[k0] / B;
+  const float* __restrict__ gt = grad + (int64_t)t * D;
+  const int32_t tB = t * B;
+  zero_acc<ACC, V, PMAX>(acc);
+  for (int32_t base = k0; base < k1; base += kWave) {
+    const int n = k1 - base < kWave ? k1 - base : kWave;
+    const int32_t my_bag = lane < n ? sorted_bag[base + lane] : tB;
+    float my_s = 0.f;
+    if constexpr (WEIGHTED) my_s = lane < n ? sorted_psw[base + lane] : 0.f;
+    for (int r0 = 0; r0 < n; r0 += NS * UNROLL) {
       GRAW buf[UNROLL][PMAX];
       float sc[UNROLL];
 #pragma unroll
       for (int uu = 0; uu < UNROLL; ++uu) {
-        const int32_t kk = k + uu;
-        const bool ok = kk < k1;
-        const int32_t bag = ok ? sorted_bag[kk] : 0;
-        if constexpr (WEIGHTED) sc[uu] = ok ? sorted_psw[kk] : 0.f;
-        else sc[uu] = ok ? 1.f : 0.f;
-        const float* row = gt + (int64_t)(bag - t * B) * T * D;
+        const int r = r0 + uu * NS + slot;
+        const bool ok = r < n;
+        const int32_t bag = __shfl(my_bag, r & (kWave - 1));
+        if constexpr (WEIGHTED) {
+          const float sv = __shfl(my_s, r & (kWave - 1));
+          sc[uu] = ok ? sv : 0.f;
+        } else {
+          sc[uu] = ok ? 1.f : 0.f;
+        }
+        const float* row = gt + (int64_t)(ok ? bag - tB : 0) * T * D;
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
           const int e = (p * G + col) * V;
-          if (ok && p < P && e < D) buf[uu][p] = load_vec<float, V>(row + e);
+          if (p < P && e < D) buf[uu][p] = load_vec<float, V>(row + e);
           else buf[uu][p] = GRAW{};
         }
       }
@@ -109,9 +115,117 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
         }
       }
     }
-    if (active) {  // whole slots are active or not, so the slot's reductions stay within it
-      const int32_t key = run_keys[u];
-      adagrad_row<WT, ACC, V, PMAX>(W + (int64_t)key * D, mom + key, acc, col, G, P, D, lr, eps);
+  }
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[p][v] = across_slots_sum<ACC>(acc[p][v], G);
+}
+
+// Short runs. A wave takes 64 entries of the short-run list at a time:
+// - runs of at most kTinyMax lookups are owned by one row slot each (four runs
+//   in flight per wave, all their rows loaded at once);
+// - longer short runs are owned by the whole wave in turn, four slots sharing
+//   the rows, so a run of a few hundred lookups does not hold three idle slots.
+// Either way one owner updates the row, with plain stores. The row's weights
+// and state are loaded before its gradient gather completes.
+constexpr int kTinyMax = 4;
+
+template <typename WT, int V, int PMAX, bool WEIGHTED>
+__global__ __launch_bounds__(kThreads) void bwd_short_kernel(
+    WT* __restrict__ W, float* __restrict__ mom, const float* __restrict__ grad,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ short_runs,
+    const int32_t* __restrict__ run_keys, const int32_t* __restrict__ run_offsets,
+    const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw, int32_t T,
+    int32_t B, int32_t D, int32_t G, int32_t log2G, int32_t P,
+    typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
+  using ACC = typename acc_of<WT>::type;
+  using GRAW = typename raw_vec<float, V>::type;
+  __shared__ int32_t s_src[kWaves][kWave];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int slot = lane >> log2G;
+  const int col = lane & (G - 1);
+  const int NS = kWave >> log2G;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+  const int64_t n_short = counts[1];
+  const int64_t gwave = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+
+  for (int64_t tile = gwave * kWave; tile < n_short; tile += nwaves * kWave) {
+    const int64_t i = tile + lane;
+    const bool valid = i < n_short;
+    const int32_t u = valid ? short_runs[i] : 0;
+    const int32_t k0 = valid ? run_offsets[u] : 0;
+    const int32_t k1 = valid ? run_offsets[u + 1] : 0;
+    const int32_t key = valid ? run_keys[u] : 0;
+    const bool tiny = valid && k1 - k0 <= kTinyMax;
+    const uint64_t tmask = __ballot(tiny);
+    uint64_t mmask = __ballot(valid && !tiny);
+    wave_lds_sync();
+    if (tiny) s_src[wave][__popcll(tmask & lt)] = lane;
+    wave_lds_sync();
+
+    // tiny runs, one per slot
+    const int ntiny = __popcll(tmask);
+    for (int q = 0; q < ntiny; q += NS) {
+      const bool act = q + slot < ntiny;
+      const int src = act ? s_src[wave][q + slot] : 0;
+      const int32_t a = __shfl(k0, src), e = __shfl(k1, src), rkey = __shfl(key, src);
+      RowState<WT, V, PMAX> st;
+      if (act) load_row_state<WT, V, PMAX>(W + (int64_t)rkey * D, mom + rkey, col, G, P, D, st);
+      int32_t bag[kTinyMax];
+      float sc[kTinyMax];
+#pragma unroll
+      for (int r = 0; r < kTinyMax; ++r) {
+        const bool ok = act && a + r < e;
+        bag[r] = act ? sorted_bag[ok ? a + r : a] : 0;
+        if constexpr (WEIGHTED) sc[r] = ok ? sorted_psw[a + r] : 0.f;
+        else sc[r] = ok ? 1.f : 0.f;
+      }
+      const int32_t t = bag[0] / (B > 0 ? B : 1);
+      const float* __restrict__ gt = grad + (int64_t)t * D;
+      GRAW buf[kTinyMax][PMAX];
+#pragma unroll
+      for (int r = 0; r < kTinyMax; ++r) {
+        const float* row = gt + (int64_t)(bag[r] - t * B) * T * D;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+          const int ee = (p * G + col) * V;
+          if (act && p < P && ee < D) buf[r][p] = load_vec<float, V>(row + ee);
+          else buf[r][p] = GRAW{};
+        }
+      }
+      ACC acc[PMAX][V];
+      zero_acc<ACC, V, PMAX>(acc);
+#pragma unroll
+      for (int r = 0; r < kTinyMax; ++r) {
+        const ACC sv = (ACC)sc[r];
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+          const float* x = reinterpret_cast<const float*>(&buf[r][p]);
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[p][v] += sv * (ACC)x[v];
+        }
+      }
+      if (act)  // whole slots are active or not, so the slot's reductions stay within it
+        apply_row_state<WT, ACC, V, PMAX>(W + (int64_t)rkey * D, mom + rkey, st, acc, col, G, P,
+                                          D, lr, eps);
+    }
+
+    // longer short runs, one per wave
+    while (mmask) {
+      const int src = __ffsll((unsigned long long)mmask) - 1;
+      mmask &= mmask - 1;
+      const int32_t a = __shfl(k0, src), e = __shfl(k1, src), rkey = __shfl(key, src);
+      RowState<WT, V, PMAX> st;
+      if (slot == 0) load_row_state<WT, V, PMAX>(W + (int64_t)rkey * D, mom + rkey, col, G, P, D, st);
+      ACC acc[PMAX][V];
+      wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, a, e, T, B, D, G,
+                                              log2G, P, acc);
+      if (slot == 0)
+        apply_row_state<WT, ACC, V, PMAX>(W + (int64_t)rkey * D, mom + rkey, st, acc, col, G, P,
+                                          D, lr, eps);
     }
   }
 }
@@ -126,12 +240,9 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
     const int32_t* __restrict__ order, const int32_t* __restrict__ list_begin,
     ACC* __restrict__ partials, int32_t T, int32_t B, int32_t D, int32_t C, int32_t G,
     int32_t log2G, int32_t P) {
-  using GRAW = typename raw_vec<float, V>::type;
-  constexpr int UNROLL = PMAX <= 2 ? 4 : 1;
   const int lane = lane_id();
   const int slot = lane >> log2G;
   const int col = lane & (G - 1);
-  const int NS = kWave >> log2G;
   const int x = blockIdx.x % kXcds;
   const int64_t first = list_begin[x];
   const int64_t n_items = list_begin[x + 1] - first;
@@ -144,53 +255,9 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
     const int32_t k0 = chunk_start[c];
     const int32_t kend = run_offsets[u + 1];
     const int32_t k1 = k0 + C < kend ? k0 + C : kend;
-    const int32_t t = sorted_bag[k0] / B;
-    const float* __restrict__ gt = grad + (int64_t)t * D;
     ACC acc[PMAX][V];
-    zero_acc<ACC, V, PMAX>(acc);
-    for (int32_t base = k0; base < k1; base += kWave) {
-      const int n = k1 - base < kWave ? k1 - base : kWave;
-      const int32_t my_bag = lane < n ? sorted_bag[base + lane] : 0;
-      float my_s = 0.f;
-      if constexpr (WEIGHTED) my_s = lane < n ? sorted_psw[base + lane] : 0.f;
-      for (int r0 = 0; r0 < n; r0 += NS * UNROLL) {
-        GRAW buf[UNROLL][PMAX];
-        float sc[UNROLL];
-#pragma unroll
-        for (int uu = 0; uu < UNROLL; ++uu) {
-          const int r = r0 + uu * NS + slot;
-          const bool ok = r < n;
-          const int32_t bag = __shfl(my_bag, r & (kWave - 1));
-          if constexpr (WEIGHTED) {
-            const float sv = __shfl(my_s, r & (kWave - 1));
-            sc[uu] = ok ? sv : 0.f;
-          } else {
-            sc[uu] = ok ? 1.f : 0.f;
-          }
-          const float* row = gt + (int64_t)(bag - t * B) * T * D;
-#pragma unroll
-          for (int p = 0; p < PMAX; ++p) {
-            const int e = (p * G + col) * V;
-            if (ok && p < P && e < D) buf[uu][p] = load_vec<float, V>(row + e);
-            else buf[uu][p] = GRAW{};
-          }
-        }
-#pragma unroll
-        for (int uu = 0; uu < UNROLL; ++uu) {
-          const ACC s = (ACC)sc[uu];
-#pragma unroll
-          for (int p = 0; p < PMAX; ++p) {
-            const float* x = reinterpret_cast<const float*>(&buf[uu][p]);
-#pragma unroll
-            for (int v = 0; v < V; ++v) acc[p][v] += s * (ACC)x[v];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < PMAX; ++p)
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[p][v] = across_slots_sum<ACC>(acc[p][v], G);
+    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, T, B, D, G,
+                                            log2G, P, acc);
     if (slot == 0) {
       ACC* out = partials + (int64_t)c * D;
 #pragma unroll

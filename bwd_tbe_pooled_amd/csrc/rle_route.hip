@@ -17,24 +17,49 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPer = kRleTile / kThreads;  // 16 consecutive elements per thread
 
-__device__ __forceinline__ bool is_head(const int32_t* __restrict__ keys, int64_t k) {
-  return k == 0 || keys[k] != keys[k - 1];
+// Run heads of the sorted keys. A wave walks 1024 consecutive slots in rounds
+// of 64 (coalesced); the previous key comes from the neighbouring lane, from
+// the last lane of the previous round, or (first round) from memory.
+struct HeadScan {
+  int32_t key[kPer];
+  uint64_t heads[kPer];
+};
+
+__device__ __forceinline__ void find_heads(const int32_t* __restrict__ keys, int64_t N,
+                                           int64_t wbase, HeadScan& h) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t k = wbase + r * kWave + lane;
+    h.key[r] = k < N ? keys[k] : 0;
+  }
+  int32_t carry = 0;
+  if (wbase > 0 && wbase < N) carry = keys[wbase - 1];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t k = wbase + r * kWave + lane;
+    int32_t prev = __shfl_up(h.key[r], 1);
+    if (lane == 0) prev = carry;
+    const bool head = k < N && (k == 0 || h.key[r] != prev);
+    h.heads[r] = __ballot(head);
+    carry = __shfl(h.key[r], kWave - 1);
+  }
 }
 
 // tile_heads[g] = number of run heads in sorted slots [g*TILE, (g+1)*TILE).
 __global__ __launch_bounds__(kThreads) void rle_count_kernel(const int32_t* __restrict__ keys,
                                                              int64_t N, int32_t* __restrict__ tile_heads) {
-  __shared__ int32_t scratch[4];
-  const int64_t base = (int64_t)blockIdx.x * kRleTile + (int64_t)threadIdx.x * kPer;
+  __shared__ int32_t wcount[4];
+  const int wave = threadIdx.x / kWave;
+  const int64_t wbase = (int64_t)blockIdx.x * kRleTile + (int64_t)wave * (kPer * kWave);
+  HeadScan h;
+  find_heads(keys, N, wbase, h);
   int32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t k = base + i;
-    if (k < N && is_head(keys, k)) ++c;
-  }
-  int32_t total;
-  block256_exclusive_scan(c, scratch, total);
-  if (threadIdx.x == 0) tile_heads[blockIdx.x] = total;
+  for (int r = 0; r < kPer; ++r) c += __popcll(h.heads[r]);
+  if (lane_id() == 0) wcount[wave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) tile_heads[blockIdx.x] = wcount[0] + wcount[1] + wcount[2] + wcount[3];
 }
 
 // Single workgroup: exclusive scan of `ncols` interleaved arrays vals[c*n + i]
@@ -82,28 +107,28 @@ __global__ __launch_bounds__(kThreads) void rle_write_kernel(const int32_t* __re
                                                              const int32_t* __restrict__ tile_base,
                                                              int32_t* __restrict__ run_keys,
                                                              int32_t* __restrict__ run_offsets) {
-  __shared__ int32_t scratch[4];
-  const int64_t base = (int64_t)blockIdx.x * kRleTile + (int64_t)threadIdx.x * kPer;
-  uint32_t flags = 0;
+  __shared__ int32_t wcount[4];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int64_t wbase = (int64_t)blockIdx.x * kRleTile + (int64_t)wave * (kPer * kWave);
+  HeadScan h;
+  find_heads(keys, N, wbase, h);
   int32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t k = base + i;
-    if (k < N && is_head(keys, k)) {
-      flags |= 1u << i;
-      ++c;
-    }
-  }
-  int32_t total;
-  int32_t u = tile_base[blockIdx.x] + block256_exclusive_scan(c, scratch, total);
+  for (int r = 0; r < kPer; ++r) c += __popcll(h.heads[r]);
+  if (lane == 0) wcount[wave] = c;
+  __syncthreads();
+  int32_t u = tile_base[blockIdx.x];
+  for (int w = 0; w < wave; ++w) u += wcount[w];
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (flags & (1u << i)) {
-      const int64_t k = base + i;
-      run_keys[u] = keys[k];
-      run_offsets[u] = (int32_t)k;
-      ++u;
+  for (int r = 0; r < kPer; ++r) {
+    if ((h.heads[r] >> lane) & 1ull) {
+      const int32_t uu = u + __popcll(h.heads[r] & lt);
+      run_keys[uu] = h.key[r];
+      run_offsets[uu] = (int32_t)(wbase + r * kWave + lane);
     }
+    u += __popcll(h.heads[r]);
   }
 }
 

@@ -30,13 +30,31 @@ constexpr int kThreads = 256;
 constexpr int kItems = kSortTile / kThreads;   // 16 per lane
 constexpr int kWaveSpan = kSortTile / 4;       // 1024 consecutive elements per wave
 
-// bag_of[j] = bag of lookup j: one thread per bag writes its positions.
+// bag_of[j] = bag of lookup j. A wave takes 64 consecutive bags, whose
+// lookups are contiguous; each lane finds the bag of a position by binary
+// search over the 65 staged offsets, so the writes are coalesced.
 __global__ __launch_bounds__(256) void linearize_kernel(const int32_t* __restrict__ offsets,
                                                         int64_t nbags, int32_t* __restrict__ bag_of) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nbags) return;
-  const int32_t a = offsets[i], e = offsets[i + 1];
-  for (int32_t j = a; j < e; ++j) bag_of[j] = (int32_t)i;
+  __shared__ int32_t s_off[4][kWave + 1];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * kWave;
+  if (b0 >= nbags) return;
+  const int nb = nbags - b0 < kWave ? (int)(nbags - b0) : kWave;
+  if (lane < nb) s_off[wave][lane] = offsets[b0 + lane];
+  if (lane == 0) s_off[wave][nb] = offsets[b0 + nb];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int32_t P0 = s_off[wave][0], P1 = s_off[wave][nb];
+  for (int32_t q = P0 + lane; q < P1; q += kWave) {
+    int lo = 0, hi = nb - 1;  // last bag i with s_off[i] <= q (empty bags share offsets)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[wave][mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    bag_of[q] = (int32_t)(b0 + lo);
+  }
 }
 
 // tile_base[t] = first tile of table t's segment; tile_base[T] = tile count.
@@ -84,22 +102,46 @@ __device__ __forceinline__ TileInfo tile_info(int64_t g, const int32_t* __restri
   return ti;
 }
 
+// Per-tile digit counts. Lanes with equal digits are found with one ballot per
+// key bit and counted by one leader lane into its wave's histogram, so skewed
+// keys (many equal digits) cause no LDS atomic contention.
 __global__ __launch_bounds__(kThreads) void sort_upsweep_kernel(
     const int32_t* __restrict__ keys, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_base, int32_t T, int32_t B, int shift, int bits,
     int64_t tiles_max, int32_t* __restrict__ digit_counts) {
-  __shared__ int32_t hist[256];
+  __shared__ int32_t hist[4][256];
   const int64_t g = blockIdx.x;
   const TileInfo ti = tile_info(g, tile_base, offsets, T, B);
   if (!ti.valid) return;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
   const int radix = 1 << bits;
   const uint32_t mask = (uint32_t)radix - 1;
-  for (int d = threadIdx.x; d < radix; d += kThreads) hist[d] = 0;
+  for (int d = threadIdx.x; d < 4 * 256; d += kThreads) (&hist[0][0])[d] = 0;
   __syncthreads();
-  for (int32_t j = ti.a + threadIdx.x; j < ti.e; j += kThreads)
-    atomicAdd(&hist[((uint32_t)keys[j] >> shift) & mask], 1);
+  const int32_t wbase = ti.a + wave * kWaveSpan;
+  int32_t key[kItems];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int32_t j = wbase + r * kWave + lane;
+    key[r] = j < ti.e ? keys[j] : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int32_t j = wbase + r * kWave + lane;
+    const bool ok = j < ti.e;
+    const uint32_t dig = ((uint32_t)key[r] >> shift) & mask;
+    uint64_t m = __ballot(ok);
+    for (int bi = 0; bi < bits; ++bi) {
+      const bool bit = (dig >> bi) & 1u;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    if (ok && lane == __ffsll((unsigned long long)m) - 1) hist[wave][dig] += __popcll(m);
+  }
   __syncthreads();
-  for (int d = threadIdx.x; d < radix; d += kThreads) digit_counts[(int64_t)d * tiles_max + g] = hist[d];
+  for (int d = threadIdx.x; d < radix; d += kThreads)
+    digit_counts[(int64_t)d * tiles_max + g] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
 }
 
 // One workgroup per (table, digit): exclusive scan of the digit's counts over
