@@ -125,6 +125,7 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
     }
     L.sorted_keys = take(n4);
     L.tile_base = take(sizeof(int32_t) * ((size_t)p.T + 1));
+    L.tile_desc = take(sizeof(int32_t) * 4 * (size_t)p.sort_tiles_max);
     const int64_t radix = int64_t(1) << p.sort_bits;
     L.digit_counts = take(sizeof(int32_t) * (size_t)(radix * p.sort_tiles_max));
     L.digit_tot = take(sizeof(int32_t) * (size_t)(radix * p.T));
@@ -265,6 +266,7 @@ tbe_status run_preprocess(const tbe_desc* d, const Problem& p, const int32_t* in
   }
   b.sorted_keys = at<int32_t>(ws, L.sorted_keys);
   b.tile_base = at<int32_t>(ws, L.tile_base);
+  b.tile_desc = at<int4>(ws, L.tile_desc);
   b.digit_counts = at<int32_t>(ws, L.digit_counts);
   b.digit_tot = at<int32_t>(ws, L.digit_tot);
   timer_begin(d->timer, TBE_STAGE_LINEARIZE, s);

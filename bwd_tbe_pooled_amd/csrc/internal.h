@@ -61,6 +61,7 @@ struct WsLayout {
   size_t sortB[4];
   size_t sorted_keys;  // int32[N]
   size_t tile_base;    // int32[T+1]
+  size_t tile_desc;    // int4[sort_tiles_max]
   size_t digit_counts; // int32[radix * sort_tiles_max]
   size_t digit_tot;    // int32[T * radix]
   size_t rle_tiles;    // int32[2 * n_rle_tiles]
@@ -98,6 +99,7 @@ struct SortBuffers {
   int32_t* B[4];
   int32_t* sorted_keys;
   int32_t* tile_base;
+  int4* tile_desc;
   int32_t* digit_counts;
   int32_t* digit_tot;
 };

@@ -83,22 +83,37 @@ struct TileInfo {
   bool valid;
 };
 
-__device__ __forceinline__ TileInfo tile_info(int64_t g, const int32_t* __restrict__ tile_base,
-                                              const int32_t* __restrict__ offsets, int32_t T,
-                                              int32_t B) {
-  TileInfo ti;
-  ti.valid = g < tile_base[T];
-  if (!ti.valid) return ti;
-  int32_t lo = 0, hi = T - 1;  // last t with tile_base[t] <= g (empty tables share a base)
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (tile_base[mid] <= g) lo = mid; else hi = mid - 1;
+// tile_desc[g] = (table, first element, end element, first element of the
+// table's segment) of tile g, or table = -1 past the last tile. Computed once
+// per sort so that each pass's workgroups read their tile with one load.
+__global__ __launch_bounds__(256) void sort_tiles_kernel(const int32_t* __restrict__ tile_base,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int32_t T, int32_t B, int64_t tiles_max,
+                                                         int4* __restrict__ tile_desc) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= tiles_max) return;
+  int4 d = make_int4(-1, 0, 0, 0);
+  if (g < tile_base[T]) {
+    int32_t lo = 0, hi = T - 1;  // last t with tile_base[t] <= g (empty tables share a base)
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (tile_base[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    const int32_t seg_a = offsets[(int64_t)lo * B];
+    const int32_t seg_e = offsets[(int64_t)(lo + 1) * B];
+    const int32_t a = seg_a + (int32_t)(g - tile_base[lo]) * kSortTile;
+    d = make_int4(lo, a, a + kSortTile < seg_e ? a + kSortTile : seg_e, seg_a);
   }
-  ti.t = lo;
-  const int32_t seg_a = offsets[(int64_t)lo * B];
-  const int32_t seg_e = offsets[(int64_t)(lo + 1) * B];
-  ti.a = seg_a + (int32_t)(g - tile_base[lo]) * kSortTile;
-  ti.e = ti.a + kSortTile < seg_e ? ti.a + kSortTile : seg_e;
+  tile_desc[g] = d;
+}
+
+__device__ __forceinline__ TileInfo tile_info(int64_t g, const int4* __restrict__ tile_desc) {
+  const int4 d = tile_desc[g];
+  TileInfo ti;
+  ti.valid = d.x >= 0;
+  ti.t = d.x;
+  ti.a = d.y;
+  ti.e = d.z;
   return ti;
 }
 
@@ -106,12 +121,11 @@ __device__ __forceinline__ TileInfo tile_info(int64_t g, const int32_t* __restri
 // key bit and counted by one leader lane into its wave's histogram, so skewed
 // keys (many equal digits) cause no LDS atomic contention.
 __global__ __launch_bounds__(kThreads) void sort_upsweep_kernel(
-    const int32_t* __restrict__ keys, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_base, int32_t T, int32_t B, int shift, int bits,
+    const int32_t* __restrict__ keys, const int4* __restrict__ tile_desc, int shift, int bits,
     int64_t tiles_max, int32_t* __restrict__ digit_counts) {
   __shared__ int32_t hist[4][256];
   const int64_t g = blockIdx.x;
-  const TileInfo ti = tile_info(g, tile_base, offsets, T, B);
+  const TileInfo ti = tile_info(g, tile_desc);
   if (!ti.valid) return;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -186,10 +200,9 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
     const int32_t* __restrict__ keys_in, const int32_t* __restrict__ pos_in,
     const int32_t* __restrict__ bag_in, const float* __restrict__ psw_in,
     int32_t* __restrict__ keys_out, int32_t* __restrict__ pos_out, int32_t* __restrict__ bag_out,
-    float* __restrict__ psw_out, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ toff, int32_t T, int32_t B,
-    int shift, int bits, int64_t tiles_max, const int32_t* __restrict__ digit_counts,
-    const int32_t* __restrict__ digit_tot) {
+    float* __restrict__ psw_out, const int4* __restrict__ tile_desc,
+    const int32_t* __restrict__ toff, int shift, int bits, int64_t tiles_max,
+    const int32_t* __restrict__ digit_counts, const int32_t* __restrict__ digit_tot) {
   __shared__ int32_t wave_hist[4][256];
   __shared__ int32_t digit_off[256];   // tile-local start of each digit
   __shared__ int32_t gdelta[256];      // global position minus tile-local position
@@ -197,7 +210,8 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
   __shared__ int32_t scratch[4];
 
   const int64_t g = blockIdx.x;
-  const TileInfo ti = tile_info(g, tile_base, offsets, T, B);
+  const int4 desc = tile_desc[g];
+  const TileInfo ti = tile_info(g, tile_desc);
   if (!ti.valid) return;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -269,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
   const int32_t tot_start = block256_exclusive_scan(d < radix ? tot : 0, scratch, total);
   if (d < radix) {
     digit_off[d] = local_start;
-    const int32_t seg_a = offsets[(int64_t)ti.t * B];
+    const int32_t seg_a = desc.w;
     gdelta[d] = seg_a + tot_start + digit_counts[(int64_t)d * tiles_max + g] - local_start;
   }
   __syncthreads();
@@ -338,18 +352,15 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
 template <bool FIRST, bool LAST>
 hipError_t launch_downsweep(bool weighted, dim3 grid, hipStream_t s, const int32_t* ki,
                             const int32_t* pi, const int32_t* bi, const float* wi, int32_t* ko,
-                            int32_t* po, int32_t* bo, float* wo, const int32_t* offsets,
-                            const int32_t* tile_base, const int32_t* toff, int32_t T, int32_t B,
-                            int shift, int bits, int64_t tiles_max, const int32_t* dc,
-                            const int32_t* dt) {
+                            int32_t* po, int32_t* bo, float* wo, const int4* tile_desc,
+                            const int32_t* toff, int shift, int bits, int64_t tiles_max,
+                            const int32_t* dc, const int32_t* dt) {
   if (weighted)
     hipLaunchKernelGGL((sort_downsweep_kernel<FIRST, LAST, true>), grid, dim3(kThreads), 0, s, ki,
-                       pi, bi, wi, ko, po, bo, wo, offsets, tile_base, toff, T, B, shift, bits,
-                       tiles_max, dc, dt);
+                       pi, bi, wi, ko, po, bo, wo, tile_desc, toff, shift, bits, tiles_max, dc, dt);
   else
     hipLaunchKernelGGL((sort_downsweep_kernel<FIRST, LAST, false>), grid, dim3(kThreads), 0, s, ki,
-                       pi, bi, wi, ko, po, bo, wo, offsets, tile_base, toff, T, B, shift, bits,
-                       tiles_max, dc, dt);
+                       pi, bi, wi, ko, po, bo, wo, tile_desc, toff, shift, bits, tiles_max, dc, dt);
   return hipGetLastError();
 }
 
@@ -372,6 +383,9 @@ hipError_t launch_sort(const Problem& p, const int32_t* indices, const int32_t* 
   hipLaunchKernelGGL(sort_setup_kernel, dim3(1), dim3(256), 0, s, offsets, p.T, p.B, b.tile_base);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (p.N == 0) return hipSuccess;
+  hipLaunchKernelGGL(sort_tiles_kernel, dim3((unsigned)((p.sort_tiles_max + 255) / 256)), dim3(256),
+                     0, s, b.tile_base, offsets, p.T, p.B, p.sort_tiles_max, b.tile_desc);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const dim3 tgrid((unsigned)p.sort_tiles_max);
   const int radix = 1 << p.sort_bits;
   const bool weighted = p.weighted;
@@ -392,29 +406,20 @@ hipError_t launch_sort(const Problem& p, const int32_t* indices, const int32_t* 
     int32_t* bo = last ? meta.sorted_bag : dst[2];
     float* wo = last ? meta.sorted_psw : (float*)dst[3];
 
-    hipLaunchKernelGGL(sort_upsweep_kernel, tgrid, dim3(kThreads), 0, s, ki, offsets, b.tile_base,
-                       p.T, p.B, shift, p.sort_bits, p.sort_tiles_max, b.digit_counts);
+    hipLaunchKernelGGL(sort_upsweep_kernel, tgrid, dim3(kThreads), 0, s, ki, b.tile_desc, shift,
+                       p.sort_bits, p.sort_tiles_max, b.digit_counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(sort_scan_kernel, dim3((unsigned)(p.T * radix)), dim3(kThreads), 0, s,
                        b.digit_counts, b.tile_base, radix, p.sort_tiles_max, b.digit_tot);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (first && last)
-      err = launch_downsweep<true, true>(weighted, tgrid, s, ki, pi, bi, wi, ko, po, bo, wo, offsets,
-                                         b.tile_base, toff, p.T, p.B, shift, p.sort_bits,
-                                         p.sort_tiles_max, b.digit_counts, b.digit_tot);
-    else if (first)
-      err = launch_downsweep<true, false>(weighted, tgrid, s, ki, pi, bi, wi, ko, po, bo, wo,
-                                          offsets, b.tile_base, toff, p.T, p.B, shift, p.sort_bits,
-                                          p.sort_tiles_max, b.digit_counts, b.digit_tot);
-    else if (last)
-      err = launch_downsweep<false, true>(weighted, tgrid, s, ki, pi, bi, wi, ko, po, bo, wo,
-                                          offsets, b.tile_base, toff, p.T, p.B, shift, p.sort_bits,
-                                          p.sort_tiles_max, b.digit_counts, b.digit_tot);
-    else
-      err = launch_downsweep<false, false>(weighted, tgrid, s, ki, pi, bi, wi, ko, po, bo, wo,
-                                           offsets, b.tile_base, toff, p.T, p.B, shift,
-                                           p.sort_bits, p.sort_tiles_max, b.digit_counts,
-                                           b.digit_tot);
+#define TBE_DOWNSWEEP(F, L)                                                                    \
+  launch_downsweep<F, L>(weighted, tgrid, s, ki, pi, bi, wi, ko, po, bo, wo, b.tile_desc, toff, \
+                         shift, p.sort_bits, p.sort_tiles_max, b.digit_counts, b.digit_tot)
+    if (first && last) err = TBE_DOWNSWEEP(true, true);
+    else if (first) err = TBE_DOWNSWEEP(true, false);
+    else if (last) err = TBE_DOWNSWEEP(false, true);
+    else err = TBE_DOWNSWEEP(false, false);
+#undef TBE_DOWNSWEEP
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
