@@ -142,7 +142,7 @@ def main():
     out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device=dev)
     timer = tbe.Timer(capacity=args.steps + 1)
     desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype)
-    meta = tbe.Meta(desc, N, True)
+    meta = tbe.Meta(desc, N, True, with_pos=False)   # the backward needs no positions
     ws_f = tbe.workspace(desc, N, True, tbe.TBE_OP_FORWARD_PREPROCESS)
     ws_b = tbe.workspace(desc, N, True, tbe.TBE_OP_BACKWARD)
     if args.profile_copy:

@@ -148,7 +148,9 @@ def tbe_workspace_bytes(desc: Desc, N: int, weighted: bool, op: int) -> int:
 class Meta:
     """Device buffers of a tbe_meta, allocated to the library's capacities."""
 
-    def __init__(self, desc: Desc, N: int, weighted: bool, device="cuda"):
+    def __init__(self, desc: Desc, N: int, weighted: bool, device="cuda", with_pos: bool = True):
+        """with_pos=False leaves sorted_pos NULL: the sort then does not carry
+        lookup positions (the backward never reads them)."""
         import torch
         caps = tbe_meta_capacity(desc, N, weighted)
         self.caps = dict(zip(META_FIELDS, caps))
@@ -157,6 +159,8 @@ class Meta:
             used = {"counts", "hist"}
         else:
             used = set(META_FIELDS) - {"hist"} - (set() if weighted else {"sorted_psw"})
+            if not with_pos:
+                used -= {"sorted_pos"}
         self.tensors = {}
         for name in META_FIELDS:
             if name not in used:

@@ -116,7 +116,6 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
   L.has_pre = pre && generic;
   if (L.has_pre) {
     const size_t n4 = sizeof(int32_t) * (size_t)p.N;
-    L.bag_of = take(n4);
     const int sets = p.sort_passes >= 3 ? 2 : (p.sort_passes == 2 ? 1 : 0);
     for (int k = 0; k < 4; ++k) {
       const bool need = k < 3 || p.weighted;
@@ -125,7 +124,7 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
     }
     L.sorted_keys = take(n4);
     L.tile_base = take(sizeof(int32_t) * ((size_t)p.T + 1));
-    L.tile_desc = take(sizeof(int32_t) * 4 * (size_t)p.sort_tiles_max);
+    L.tile_desc = take(sizeof(int32_t) * 8 * (size_t)p.sort_tiles_max);
     const int64_t radix = int64_t(1) << p.sort_bits;
     L.digit_counts = take(sizeof(int32_t) * (size_t)(radix * p.sort_tiles_max));
     L.digit_tot = take(sizeof(int32_t) * (size_t)(radix * p.T));
@@ -209,7 +208,7 @@ T* at(void* ws, size_t off) {
 }
 
 bool meta_ok_generic(const tbe_meta* m, bool weighted) {
-  return m && m->counts && m->run_keys && m->run_offsets && m->sorted_pos && m->sorted_bag &&
+  return m && m->counts && m->run_keys && m->run_offsets && m->sorted_bag &&
          (!weighted || m->sorted_psw) && m->short_runs && m->long_runs && m->long_chunk_begin &&
          m->chunk_run && m->chunk_start;
 }
@@ -259,7 +258,6 @@ tbe_status run_preprocess(const tbe_desc* d, const Problem& p, const int32_t* in
                           void* ws, const WsLayout& L, hipStream_t s) {
   const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
   SortBuffers b{};
-  b.bag_of = at<int32_t>(ws, L.bag_of);
   for (int k = 0; k < 4; ++k) {
     b.A[k] = L.sortA[k] ? at<int32_t>(ws, L.sortA[k]) : nullptr;
     b.B[k] = L.sortB[k] ? at<int32_t>(ws, L.sortB[k]) : nullptr;
@@ -270,10 +268,10 @@ tbe_status run_preprocess(const tbe_desc* d, const Problem& p, const int32_t* in
   b.digit_counts = at<int32_t>(ws, L.digit_counts);
   b.digit_tot = at<int32_t>(ws, L.digit_tot);
   timer_begin(d->timer, TBE_STAGE_LINEARIZE, s);
-  TBE_TRY_HIP(launch_linearize(p, offsets, b.bag_of, s));
+  TBE_TRY_HIP(launch_sort_setup(p, offsets, b, s));
   timer_end(d->timer, TBE_STAGE_LINEARIZE, s);
   timer_begin(d->timer, TBE_STAGE_SORT, s);
-  TBE_TRY_HIP(launch_sort(p, indices, offsets, psw, tinfo, b, meta, d->timer, s));
+  TBE_TRY_HIP(launch_sort(p, indices, offsets, psw, tinfo, b, meta, s));
   timer_end(d->timer, TBE_STAGE_SORT, s);
   timer_begin(d->timer, TBE_STAGE_RLE_ROUTE, s);
   TBE_TRY_HIP(launch_rle_route(p, b.sorted_keys, at<int32_t>(ws, L.rle_tiles),

@@ -56,12 +56,11 @@ struct WsLayout {
   size_t tinfo;        // int32 toff[T], int32 rows[T]
   size_t flags;        // int32[16]
   // generic preprocessing
-  size_t bag_of;       // int32[N]
   size_t sortA[4];     // key, pos, bag, psw  (int32/float [N] each)
   size_t sortB[4];
   size_t sorted_keys;  // int32[N]
   size_t tile_base;    // int32[T+1]
-  size_t tile_desc;    // int4[sort_tiles_max]
+  size_t tile_desc;    // int4[2 * sort_tiles_max]
   size_t digit_counts; // int32[radix * sort_tiles_max]
   size_t digit_tot;    // int32[T * radix]
   size_t rle_tiles;    // int32[2 * n_rle_tiles]
@@ -94,20 +93,19 @@ hipError_t launch_forward_pool(const Problem& p, const void* W, const int32_t* i
                                float* out, hipStream_t s);
 
 struct SortBuffers {
-  int32_t* bag_of;
-  int32_t* A[4];
-  int32_t* B[4];
+  int32_t* A[4];       // key, pos, bag, psw after even passes
+  int32_t* B[4];       // ... after odd passes
   int32_t* sorted_keys;
   int32_t* tile_base;
-  int4* tile_desc;
+  int4* tile_desc;     // two int4 per tile
   int32_t* digit_counts;
   int32_t* digit_tot;
 };
-hipError_t launch_linearize(const Problem& p, const int32_t* offsets, int32_t* bag_of,
-                            hipStream_t s);
+hipError_t launch_sort_setup(const Problem& p, const int32_t* offsets, const SortBuffers& b,
+                             hipStream_t s);
 hipError_t launch_sort(const Problem& p, const int32_t* indices, const int32_t* offsets,
                        const float* psw, const int32_t* tinfo, const SortBuffers& b,
-                       const tbe_meta& meta, tbe_timer* timer, hipStream_t s);
+                       const tbe_meta& meta, hipStream_t s);
 hipError_t launch_rle_route(const Problem& p, const int32_t* sorted_keys, int32_t* rle_tiles,
                             int32_t* route_tiles, const tbe_meta& meta, hipStream_t s);
 

@@ -16,8 +16,11 @@
 //             ballots: 64 lanes find equal digits with one ballot per key bit),
 //             reorder the tile in LDS, then write each digit bucket with
 //             consecutive lanes on consecutive addresses.
-// Pass 0 reads indices directly and takes position and bag id as payload; the
-// last pass writes the full key (toff[t] + row) and the metadata arrays.
+// Pass 0 reads the indices directly; the bag of each lookup comes from the
+// tile's bag offsets staged in LDS (no bag-id array is written or read). The
+// payload is (bag, per-sample weight), plus the original position only when
+// the caller asks for it (the backward does not need it). The last pass
+// writes the linearized key toff[t] + row and the metadata arrays.
 #include "block_scan.h"
 #include "device.h"
 #include "internal.h"
@@ -29,33 +32,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kItems = kSortTile / kThreads;   // 16 per lane
 constexpr int kWaveSpan = kSortTile / 4;       // 1024 consecutive elements per wave
-
-// bag_of[j] = bag of lookup j. A wave takes 64 consecutive bags, whose
-// lookups are contiguous; each lane finds the bag of a position by binary
-// search over the 65 staged offsets, so the writes are coalesced.
-__global__ __launch_bounds__(256) void linearize_kernel(const int32_t* __restrict__ offsets,
-                                                        int64_t nbags, int32_t* __restrict__ bag_of) {
-  __shared__ int32_t s_off[4][kWave + 1];
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const int64_t b0 = ((int64_t)blockIdx.x * 4 + wave) * kWave;
-  if (b0 >= nbags) return;
-  const int nb = nbags - b0 < kWave ? (int)(nbags - b0) : kWave;
-  if (lane < nb) s_off[wave][lane] = offsets[b0 + lane];
-  if (lane == 0) s_off[wave][nb] = offsets[b0 + nb];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int32_t P0 = s_off[wave][0], P1 = s_off[wave][nb];
-  for (int32_t q = P0 + lane; q < P1; q += kWave) {
-    int lo = 0, hi = nb - 1;  // last bag i with s_off[i] <= q (empty bags share offsets)
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_off[wave][mid] <= q) lo = mid; else hi = mid - 1;
-    }
-    bag_of[q] = (int32_t)(b0 + lo);
-  }
-}
 
 // tile_base[t] = first tile of table t's segment; tile_base[T] = tile count.
 __global__ __launch_bounds__(256) void sort_setup_kernel(const int32_t* __restrict__ offsets,
@@ -80,40 +56,61 @@ __global__ __launch_bounds__(256) void sort_setup_kernel(const int32_t* __restri
 
 struct TileInfo {
   int32_t t, a, e;  // table, element range [a, e)
+  int32_t seg_a;    // first element of the table's segment
+  int32_t bag0, bag1;  // bags containing elements a and e-1
   bool valid;
 };
 
-// tile_desc[g] = (table, first element, end element, first element of the
-// table's segment) of tile g, or table = -1 past the last tile. Computed once
-// per sort so that each pass's workgroups read their tile with one load.
+// Last bag i in [lo, hi] with offsets[i] <= x (empty bags share offsets, so
+// this is the bag that contains position x).
+__device__ __forceinline__ int32_t bag_of_position(const int32_t* __restrict__ offsets, int32_t lo,
+                                                   int32_t hi, int32_t x) {
+  while (lo < hi) {
+    const int32_t mid = lo + (hi - lo + 1) / 2;
+    if (offsets[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// tile_desc[g] = (table, first element, end element, segment start) and
+// (first bag, last bag) of tile g; table = -1 past the last tile. Computed
+// once per sort so that each pass's workgroups read their tile with two loads.
 __global__ __launch_bounds__(256) void sort_tiles_kernel(const int32_t* __restrict__ tile_base,
                                                          const int32_t* __restrict__ offsets,
                                                          int32_t T, int32_t B, int64_t tiles_max,
                                                          int4* __restrict__ tile_desc) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= tiles_max) return;
-  int4 d = make_int4(-1, 0, 0, 0);
+  int4 d0 = make_int4(-1, 0, 0, 0), d1 = make_int4(0, 0, 0, 0);
   if (g < tile_base[T]) {
     int32_t lo = 0, hi = T - 1;  // last t with tile_base[t] <= g (empty tables share a base)
     while (lo < hi) {
       const int32_t mid = (lo + hi + 1) >> 1;
       if (tile_base[mid] <= g) lo = mid; else hi = mid - 1;
     }
-    const int32_t seg_a = offsets[(int64_t)lo * B];
-    const int32_t seg_e = offsets[(int64_t)(lo + 1) * B];
+    const int32_t seg_a = offsets[lo * B];
+    const int32_t seg_e = offsets[(lo + 1) * B];
     const int32_t a = seg_a + (int32_t)(g - tile_base[lo]) * kSortTile;
-    d = make_int4(lo, a, a + kSortTile < seg_e ? a + kSortTile : seg_e, seg_a);
+    const int32_t e = a + kSortTile < seg_e ? a + kSortTile : seg_e;
+    d0 = make_int4(lo, a, e, seg_a);
+    d1 = make_int4(bag_of_position(offsets, lo * B, (lo + 1) * B - 1, a),
+                   bag_of_position(offsets, lo * B, (lo + 1) * B - 1, e - 1), 0, 0);
   }
-  tile_desc[g] = d;
+  tile_desc[2 * g] = d0;
+  tile_desc[2 * g + 1] = d1;
 }
 
 __device__ __forceinline__ TileInfo tile_info(int64_t g, const int4* __restrict__ tile_desc) {
-  const int4 d = tile_desc[g];
+  const int4 d0 = tile_desc[2 * g];
+  const int4 d1 = tile_desc[2 * g + 1];
   TileInfo ti;
-  ti.valid = d.x >= 0;
-  ti.t = d.x;
-  ti.a = d.y;
-  ti.e = d.z;
+  ti.valid = d0.x >= 0;
+  ti.t = d0.x;
+  ti.a = d0.y;
+  ti.e = d0.z;
+  ti.seg_a = d0.w;
+  ti.bag0 = d1.x;
+  ti.bag1 = d1.y;
   return ti;
 }
 
@@ -193,24 +190,25 @@ __global__ __launch_bounds__(kThreads) void sort_scan_kernel(int32_t* __restrict
   if (threadIdx.x == 0) digit_tot[(int64_t)t * radix + d] = carry;
 }
 
-// FIRST: keys_in = indices, positions are j, bags come from bag_of.
-// LAST:  keys_out receives toff[t] + row (the linearized key).
-template <bool FIRST, bool LAST, bool WEIGHTED>
+// FIRST: keys_in = indices, the position of an element is its index, and its
+// bag is found among the tile's bag offsets. LAST: keys_out receives
+// toff[t] + row. WITH_POS: the original position travels as payload.
+template <bool FIRST, bool LAST, bool WEIGHTED, bool WITH_POS>
 __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
     const int32_t* __restrict__ keys_in, const int32_t* __restrict__ pos_in,
     const int32_t* __restrict__ bag_in, const float* __restrict__ psw_in,
-    int32_t* __restrict__ keys_out, int32_t* __restrict__ pos_out, int32_t* __restrict__ bag_out,
-    float* __restrict__ psw_out, const int4* __restrict__ tile_desc,
-    const int32_t* __restrict__ toff, int shift, int bits, int64_t tiles_max,
-    const int32_t* __restrict__ digit_counts, const int32_t* __restrict__ digit_tot) {
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ keys_out,
+    int32_t* __restrict__ pos_out, int32_t* __restrict__ bag_out, float* __restrict__ psw_out,
+    const int4* __restrict__ tile_desc, const int32_t* __restrict__ toff, int shift, int bits,
+    int64_t tiles_max, const int32_t* __restrict__ digit_counts,
+    const int32_t* __restrict__ digit_tot) {
   __shared__ int32_t wave_hist[4][256];
   __shared__ int32_t digit_off[256];   // tile-local start of each digit
   __shared__ int32_t gdelta[256];      // global position minus tile-local position
-  __shared__ int32_t stage[kSortTile];
+  __shared__ int32_t stage[kSortTile + 1];
   __shared__ int32_t scratch[4];
 
   const int64_t g = blockIdx.x;
-  const int4 desc = tile_desc[g];
   const TileInfo ti = tile_info(g, tile_desc);
   if (!ti.valid) return;
   const int wave = threadIdx.x / kWave;
@@ -220,7 +218,6 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 
   for (int d = threadIdx.x; d < 4 * 256; d += kThreads) (&wave_hist[0][0])[d] = 0;
-  __syncthreads();
 
   int32_t key[kItems], pos[kItems], bag[kItems], rank[kItems];
   float w[kItems];
@@ -230,15 +227,37 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
     const int32_t j = wbase + r * kWave + lane;
     const bool ok = j < ti.e;
     key[r] = ok ? keys_in[j] : 0;
-    if constexpr (FIRST) {
-      pos[r] = j;
-      bag[r] = ok ? bag_in[j] : 0;
-    } else {
-      pos[r] = ok ? pos_in[j] : 0;
-      bag[r] = ok ? bag_in[j] : 0;
-    }
+    if constexpr (WITH_POS) pos[r] = FIRST ? j : (ok ? pos_in[j] : 0);
+    if constexpr (!FIRST) bag[r] = ok ? bag_in[j] : 0;
     if constexpr (WEIGHTED) w[r] = ok ? psw_in[j] : 0.f;
   }
+  if constexpr (FIRST) {
+    // Bags of the tile: offsets[bag0 .. bag1+1], staged when they fit.
+    const int32_t nwin = ti.bag1 - ti.bag0 + 2;
+    const bool staged = nwin <= kSortTile + 1;
+    if (staged)
+      for (int i = threadIdx.x; i < nwin; i += kThreads) stage[i] = offsets[ti.bag0 + i];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+      const int32_t j = wbase + r * kWave + lane;
+      int32_t b = 0;
+      if (j < ti.e) {
+        if (staged) {
+          int32_t lo = 0, hi = nwin - 2;
+          while (lo < hi) {
+            const int32_t mid = lo + (hi - lo + 1) / 2;
+            if (stage[mid] <= j) lo = mid; else hi = mid - 1;
+          }
+          b = ti.bag0 + lo;
+        } else {
+          b = bag_of_position(offsets, ti.bag0, ti.bag1, j);
+        }
+      }
+      bag[r] = b;
+    }
+  }
+  __syncthreads();
 
   // Stable ranking inside the wave, round by round in element order.
 #pragma unroll
@@ -283,8 +302,7 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
   const int32_t tot_start = block256_exclusive_scan(d < radix ? tot : 0, scratch, total);
   if (d < radix) {
     digit_off[d] = local_start;
-    const int32_t seg_a = desc.w;
-    gdelta[d] = seg_a + tot_start + digit_counts[(int64_t)d * tiles_max + g] - local_start;
+    gdelta[d] = ti.seg_a + tot_start + digit_counts[(int64_t)d * tiles_max + g] - local_start;
   }
   __syncthreads();
 
@@ -315,15 +333,17 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
     }
   }
   // payloads, one array at a time through the same LDS stage
-  __syncthreads();
+  if constexpr (WITH_POS) {
+    __syncthreads();
 #pragma unroll
-  for (int r = 0; r < kItems; ++r)
-    if (lp[r] >= 0) stage[lp[r]] = pos[r];
-  __syncthreads();
+    for (int r = 0; r < kItems; ++r)
+      if (lp[r] >= 0) stage[lp[r]] = pos[r];
+    __syncthreads();
 #pragma unroll
-  for (int q = 0; q < kItems; ++q) {
-    const int32_t i = q * kThreads + threadIdx.x;
-    if (i < nvalid) pos_out[dest[q]] = stage[i];
+    for (int q = 0; q < kItems; ++q) {
+      const int32_t i = q * kThreads + threadIdx.x;
+      if (i < nvalid) pos_out[dest[q]] = stage[i];
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -349,72 +369,79 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
   }
 }
 
+struct PassArgs {
+  const int32_t *ki, *pi, *bi;
+  const float* wi;
+  int32_t *ko, *po, *bo;
+  float* wo;
+};
+
 template <bool FIRST, bool LAST>
-hipError_t launch_downsweep(bool weighted, dim3 grid, hipStream_t s, const int32_t* ki,
-                            const int32_t* pi, const int32_t* bi, const float* wi, int32_t* ko,
-                            int32_t* po, int32_t* bo, float* wo, const int4* tile_desc,
+hipError_t launch_downsweep(bool weighted, bool with_pos, dim3 grid, hipStream_t s,
+                            const PassArgs& a, const int32_t* offsets, const int4* tile_desc,
                             const int32_t* toff, int shift, int bits, int64_t tiles_max,
                             const int32_t* dc, const int32_t* dt) {
-  if (weighted)
-    hipLaunchKernelGGL((sort_downsweep_kernel<FIRST, LAST, true>), grid, dim3(kThreads), 0, s, ki,
-                       pi, bi, wi, ko, po, bo, wo, tile_desc, toff, shift, bits, tiles_max, dc, dt);
-  else
-    hipLaunchKernelGGL((sort_downsweep_kernel<FIRST, LAST, false>), grid, dim3(kThreads), 0, s, ki,
-                       pi, bi, wi, ko, po, bo, wo, tile_desc, toff, shift, bits, tiles_max, dc, dt);
+#define TBE_DS(W, P)                                                                           \
+  hipLaunchKernelGGL((sort_downsweep_kernel<FIRST, LAST, W, P>), grid, dim3(kThreads), 0, s,   \
+                     a.ki, a.pi, a.bi, a.wi, offsets, a.ko, a.po, a.bo, a.wo, tile_desc, toff, \
+                     shift, bits, tiles_max, dc, dt)
+  if (weighted && with_pos) TBE_DS(true, true);
+  else if (weighted) TBE_DS(true, false);
+  else if (with_pos) TBE_DS(false, true);
+  else TBE_DS(false, false);
+#undef TBE_DS
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_linearize(const Problem& p, const int32_t* offsets, int32_t* bag_of,
-                            hipStream_t s) {
-  if (p.nbags == 0) return hipSuccess;
-  const int64_t blocks = (p.nbags + 255) / 256;
-  hipLaunchKernelGGL(linearize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, offsets, p.nbags,
-                     bag_of);
+hipError_t launch_sort_setup(const Problem& p, const int32_t* offsets, const SortBuffers& b,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(sort_setup_kernel, dim3(1), dim3(256), 0, s, offsets, p.T, p.B, b.tile_base);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.N == 0) return err;
+  hipLaunchKernelGGL(sort_tiles_kernel, dim3((unsigned)((p.sort_tiles_max + 255) / 256)), dim3(256),
+                     0, s, b.tile_base, offsets, p.T, p.B, p.sort_tiles_max, b.tile_desc);
   return hipGetLastError();
 }
 
 hipError_t launch_sort(const Problem& p, const int32_t* indices, const int32_t* offsets,
                        const float* psw, const int32_t* tinfo, const SortBuffers& b,
-                       const tbe_meta& meta, tbe_timer* timer, hipStream_t s) {
-  (void)timer;
+                       const tbe_meta& meta, hipStream_t s) {
   hipError_t err;
-  hipLaunchKernelGGL(sort_setup_kernel, dim3(1), dim3(256), 0, s, offsets, p.T, p.B, b.tile_base);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   if (p.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(sort_tiles_kernel, dim3((unsigned)((p.sort_tiles_max + 255) / 256)), dim3(256),
-                     0, s, b.tile_base, offsets, p.T, p.B, p.sort_tiles_max, b.tile_desc);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   const dim3 tgrid((unsigned)p.sort_tiles_max);
   const int radix = 1 << p.sort_bits;
   const bool weighted = p.weighted;
+  const bool with_pos = meta.sorted_pos != nullptr;
   const int32_t* toff = tinfo;
   for (int pass = 0; pass < p.sort_passes; ++pass) {
     const bool first = pass == 0;
     const bool last = pass == p.sort_passes - 1;
     const int shift = pass * p.sort_bits;
-    // source and destination buffers
-    int32_t* const* src = (pass % 2 == 1) ? b.A : b.B;  // pass 1 reads A, pass 2 reads B, ...
-    int32_t* const* dst = (pass % 2 == 0) ? b.A : b.B;  // pass 0 writes A, pass 1 writes B, ...
-    const int32_t* ki = first ? indices : src[0];
-    const int32_t* pi = first ? nullptr : src[1];
-    const int32_t* bi = first ? b.bag_of : src[2];
-    const float* wi = first ? psw : (const float*)src[3];
-    int32_t* ko = last ? b.sorted_keys : dst[0];
-    int32_t* po = last ? meta.sorted_pos : dst[1];
-    int32_t* bo = last ? meta.sorted_bag : dst[2];
-    float* wo = last ? meta.sorted_psw : (float*)dst[3];
+    // source and destination buffers: pass 0 writes A, pass 1 reads A and
+    // writes B, pass 2 reads B, ...; the last pass writes the outputs.
+    int32_t* const* src = (pass % 2 == 1) ? b.A : b.B;
+    int32_t* const* dst = (pass % 2 == 0) ? b.A : b.B;
+    PassArgs a;
+    a.ki = first ? indices : src[0];
+    a.pi = first ? nullptr : src[1];
+    a.bi = first ? nullptr : src[2];
+    a.wi = first ? psw : (const float*)src[3];
+    a.ko = last ? b.sorted_keys : dst[0];
+    a.po = last ? meta.sorted_pos : dst[1];
+    a.bo = last ? meta.sorted_bag : dst[2];
+    a.wo = last ? meta.sorted_psw : (float*)dst[3];
 
-    hipLaunchKernelGGL(sort_upsweep_kernel, tgrid, dim3(kThreads), 0, s, ki, b.tile_desc, shift,
+    hipLaunchKernelGGL(sort_upsweep_kernel, tgrid, dim3(kThreads), 0, s, a.ki, b.tile_desc, shift,
                        p.sort_bits, p.sort_tiles_max, b.digit_counts);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(sort_scan_kernel, dim3((unsigned)(p.T * radix)), dim3(kThreads), 0, s,
                        b.digit_counts, b.tile_base, radix, p.sort_tiles_max, b.digit_tot);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-#define TBE_DOWNSWEEP(F, L)                                                                    \
-  launch_downsweep<F, L>(weighted, tgrid, s, ki, pi, bi, wi, ko, po, bo, wo, b.tile_desc, toff, \
-                         shift, p.sort_bits, p.sort_tiles_max, b.digit_counts, b.digit_tot)
+#define TBE_DOWNSWEEP(F, L)                                                                     \
+  launch_downsweep<F, L>(weighted, with_pos, tgrid, s, a, offsets, b.tile_desc, toff, shift,    \
+                         p.sort_bits, p.sort_tiles_max, b.digit_counts, b.digit_tot)
     if (first && last) err = TBE_DOWNSWEEP(true, true);
     else if (first) err = TBE_DOWNSWEEP(true, false);
     else if (last) err = TBE_DOWNSWEEP(false, true);

@@ -83,7 +83,7 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
 /* Stages a timer can attribute device time to. */
 typedef enum {
     TBE_STAGE_FWD_POOL = 0,     /* generic forward gather-and-pool            */
-    TBE_STAGE_LINEARIZE = 1,    /* table offsets upload, bag ids per lookup   */
+    TBE_STAGE_LINEARIZE = 1,    /* sort setup: table segments and tiles       */
     TBE_STAGE_SORT = 2,         /* radix passes                               */
     TBE_STAGE_RLE_ROUTE = 3,    /* run-length encoding and routing            */
     TBE_STAGE_BWD_SHORT = 4,    /* short runs: accumulate + Adagrad + store   */
@@ -126,7 +126,9 @@ typedef struct {
  *   counts[4] = 1 if a small-table count exceeded 255 (else 0);
  *   run_keys[u]       linearized key of run u, strictly increasing;
  *   run_offsets[u]    first sorted slot of run u; run_offsets[U] = N;
- *   sorted_pos[k]     lookup position at sorted slot k (stable order);
+ *   sorted_pos[k]     lookup position at sorted slot k (stable order); optional:
+ *                     when NULL the sort does not carry positions (the
+ *                     backward does not need them) and writes none;
  *   sorted_bag[k]     bag id t*B+b of that lookup;
  *   sorted_psw[k]     its per-sample weight (only if weighted; may be NULL
  *                     for unweighted problems);

@@ -63,7 +63,7 @@ def make_desc(cfg, S=0, C=0, flags=0, timer=None):
 
 
 def run_library(cfg, batch, W, m, *, meta_in_forward: bool, backward_meta: bool = True,
-                S=0, C=0, flags=0, dev=None):
+                S=0, C=0, flags=0, dev=None, with_pos: bool = True):
     """Forward (+ preprocessing when meta_in_forward) and backward through the
     C ABI. W and m are updated in place. Returns out and the metadata."""
     tbe = lib()
@@ -72,7 +72,7 @@ def run_library(cfg, batch, W, m, *, meta_in_forward: bool, backward_meta: bool 
     N = batch.indices.size
     weighted = batch.psw is not None
     out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device="cuda")
-    meta = tbe.Meta(desc, N, weighted)
+    meta = tbe.Meta(desc, N, weighted, with_pos=with_pos)
     if meta_in_forward:
         ws = tbe.workspace(desc, N, weighted, tbe.TBE_OP_FORWARD_PREPROCESS)
         tbe.tbe_forward(desc, W, dev["indices"], dev["offsets"], dev["psw"], out, meta, ws)
@@ -99,7 +99,7 @@ def meta_host(meta, path):
     h["run_keys"] = meta["run_keys"][:U].cpu().numpy()
     h["run_offsets"] = meta["run_offsets"][:U + 1].cpu().numpy()
     N = int(h["run_offsets"][-1])
-    h["sorted_pos"] = meta["sorted_pos"][:N].cpu().numpy()
+    h["sorted_pos"] = meta["sorted_pos"][:N].cpu().numpy() if "sorted_pos" in meta.tensors else None
     h["sorted_bag"] = meta["sorted_bag"][:N].cpu().numpy()
     h["sorted_psw"] = meta["sorted_psw"][:N].cpu().numpy() if "sorted_psw" in meta.tensors else None
     h["short_runs"] = meta["short_runs"][:ns].cpu().numpy()
@@ -127,6 +127,8 @@ def assert_meta_equal(h, pre):
     assert int(h["counts"][2]) == pre["long_runs"].size
     assert int(h["counts"][3]) == pre["chunk_run"].size
     for name in META_INT:
+        if name == "sorted_pos" and h[name] is None:
+            continue
         np.testing.assert_array_equal(h[name], pre[name], err_msg=name)
     if pre["sorted_psw"] is not None:
         np.testing.assert_array_equal(h["sorted_psw"].view(np.uint32),

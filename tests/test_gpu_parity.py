@@ -24,7 +24,8 @@ def _need_gpu():
     import bwd_tbe_pooled_amd  # noqa: F401  (fails loudly if the library is missing)
 
 
-def _full_check(cfg, batch, *, meta_in_forward, backward_meta=True, S=0, C=0, m0="zeros"):
+def _full_check(cfg, batch, *, meta_in_forward, backward_meta=True, S=0, C=0, m0="zeros",
+                with_pos=True):
     print(f"\n[parity] {cfg.name} T={cfg.T} B={cfg.B} D={cfg.D} {cfg.dtype} N={batch.indices.size} "
           f"S={S or 256} C={C or 256} meta_fwd={meta_in_forward} meta_bwd={backward_meta}",
           flush=True)
@@ -34,7 +35,7 @@ def _full_check(cfg, batch, *, meta_in_forward, backward_meta=True, S=0, C=0, m0
     uk = np.unique(keys_all)
     Wrows, mrows = host_rows(W0, m0t, uk)
     r = run_library(cfg, batch, W, m, meta_in_forward=meta_in_forward,
-                    backward_meta=backward_meta, S=S, C=C)
+                    backward_meta=backward_meta, S=S, C=C, with_pos=with_pos)
     pre, out, bw = oracle_all(cfg, batch, Wrows, mrows, uk, S or 256, C or 256)
     err = rel_err(r["out"].cpu().numpy(), out)
     assert err <= TOL[cfg.dtype], f"forward rel err {err:.3g}"
@@ -61,6 +62,21 @@ def test_config4_reduced_batch_full_compare():
     cfg = CONFIGS[4]
     batch = make_batch(cfg, B=2048)
     _full_check(batch.cfg, batch, meta_in_forward=True, backward_meta=True)
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_metadata_without_positions(k):
+    """sorted_pos left NULL: the sort carries only bags and weights, which must
+    still match the oracle's stable order bit for bit."""
+    cfg = CONFIGS[k]
+    batch = make_batch(cfg, B=2048)
+    _full_check(batch.cfg, batch, meta_in_forward=True, with_pos=False)
+
+
+def test_config4_reduced_batch_without_positions():
+    cfg = CONFIGS[4]
+    batch = make_batch(cfg, B=1024)
+    _full_check(batch.cfg, batch, meta_in_forward=True, with_pos=False)
 
 
 def test_config2_fp64_partials_with_small_chunks():
