@@ -69,7 +69,7 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   p->path = small_eligible(d, N, weighted, mx) ? TBE_PATH_SMALL_TABLE : TBE_PATH_GENERIC;
   int nbits = 0;
   while ((int64_t(1) << nbits) < mx) ++nbits;
-  p->sort_passes = std::max(1, (nbits + 7) / 8);
+  p->sort_passes = std::max(1, (nbits + 6) / 7);  // digits of at most 7 bits
   p->sort_bits = std::max(1, (nbits + p->sort_passes - 1) / p->sort_passes);
   p->sort_tiles_max = (N + kSortTile - 1) / kSortTile + d->T;
   p->cap_runs = std::min<int64_t>(N, sum);

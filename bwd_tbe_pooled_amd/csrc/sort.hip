@@ -114,45 +114,58 @@ __device__ __forceinline__ TileInfo tile_info(int64_t g, const int4* __restrict_
   return ti;
 }
 
-// Per-tile digit counts. Lanes with equal digits are found with one ballot per
-// key bit and counted by one leader lane into its wave's histogram, so skewed
-// keys (many equal digits) cause no LDS atomic contention.
+// Per-tile digit counts (digits of at most 7 bits). Each thread counts its
+// elements into its own column of byte counters, cnt[d mod 32][thread] byte
+// (d / 32), so no two lanes ever update the same word; then eight threads per
+// row add the row's 256 columns with 16-bit lanes (sums fit: at most 4096 per
+// tile) and combine with shuffles. Rows are padded by one word and the
+// summing threads start at staggered columns, so LDS banks rarely collide.
 __global__ __launch_bounds__(kThreads) void sort_upsweep_kernel(
     const int32_t* __restrict__ keys, const int4* __restrict__ tile_desc, int shift, int bits,
     int64_t tiles_max, int32_t* __restrict__ digit_counts) {
-  __shared__ int32_t hist[4][256];
+  __shared__ uint32_t cnt[32][kThreads + 1];
   const int64_t g = blockIdx.x;
   const TileInfo ti = tile_info(g, tile_desc);
   if (!ti.valid) return;
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
+  const int tid = threadIdx.x;
   const int radix = 1 << bits;
   const uint32_t mask = (uint32_t)radix - 1;
-  for (int d = threadIdx.x; d < 4 * 256; d += kThreads) (&hist[0][0])[d] = 0;
-  __syncthreads();
-  const int32_t wbase = ti.a + wave * kWaveSpan;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) cnt[r][tid] = 0;
   int32_t key[kItems];
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
-    const int32_t j = wbase + r * kWave + lane;
-    key[r] = j < ti.e ? keys[j] : 0;
+  for (int q = 0; q < kItems; ++q) {
+    const int32_t j = ti.a + q * kThreads + tid;
+    key[q] = j < ti.e ? keys[j] : 0;
   }
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
-    const int32_t j = wbase + r * kWave + lane;
-    const bool ok = j < ti.e;
-    const uint32_t dig = ((uint32_t)key[r] >> shift) & mask;
-    uint64_t m = __ballot(ok);
-    for (int bi = 0; bi < bits; ++bi) {
-      const bool bit = (dig >> bi) & 1u;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
+  for (int q = 0; q < kItems; ++q) {
+    if (ti.a + q * kThreads + tid < ti.e) {
+      const uint32_t d = ((uint32_t)key[q] >> shift) & mask;
+      cnt[d & 31][tid] += 1u << (8 * (d >> 5));
     }
-    if (ok && lane == __ffsll((unsigned long long)m) - 1) hist[wave][dig] += __popcll(m);
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < radix; d += kThreads)
-    digit_counts[(int64_t)d * tiles_max + g] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+  const int row = tid >> 3, part = tid & 7;
+  uint32_t lo = 0, hi = 0;  // 16-bit lanes: digits row, row+64 | row+32, row+96
+#pragma unroll 8
+  for (int c = 0; c < 32; ++c) {
+    const uint32_t w = cnt[row][part * 32 + ((c + part * 4) & 31)];
+    lo += w & 0x00FF00FFu;
+    hi += (w >> 8) & 0x00FF00FFu;
+  }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    lo += __shfl_xor(lo, m);
+    hi += __shfl_xor(hi, m);
+  }
+  if (part == 0) {
+    const int32_t c0 = lo & 0xFFFF, c64 = lo >> 16, c32 = hi & 0xFFFF, c96 = hi >> 16;
+    if (row < radix) digit_counts[(int64_t)row * tiles_max + g] = c0;
+    if (row + 32 < radix) digit_counts[(int64_t)(row + 32) * tiles_max + g] = c32;
+    if (row + 64 < radix) digit_counts[(int64_t)(row + 64) * tiles_max + g] = c64;
+    if (row + 96 < radix) digit_counts[(int64_t)(row + 96) * tiles_max + g] = c96;
+  }
 }
 
 // One workgroup per (table, digit): exclusive scan of the digit's counts over
@@ -232,29 +245,18 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
     if constexpr (WEIGHTED) w[r] = ok ? psw_in[j] : 0.f;
   }
   if constexpr (FIRST) {
-    // Bags of the tile: offsets[bag0 .. bag1+1], staged when they fit.
-    const int32_t nwin = ti.bag1 - ti.bag0 + 2;
-    const bool staged = nwin <= kSortTile + 1;
-    if (staged)
-      for (int i = threadIdx.x; i < nwin; i += kThreads) stage[i] = offsets[ti.bag0 + i];
+    // Bag of every element of the tile: each thread takes bags of the tile and
+    // writes the bag id into the LDS slots of its lookups.
+    for (int32_t bg = ti.bag0 + threadIdx.x; bg <= ti.bag1; bg += kThreads) {
+      const int32_t lo = offsets[bg] > ti.a ? offsets[bg] : ti.a;
+      const int32_t hi = offsets[bg + 1] < ti.e ? offsets[bg + 1] : ti.e;
+      for (int32_t j = lo; j < hi; ++j) stage[j - ti.a] = bg;
+    }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kItems; ++r) {
       const int32_t j = wbase + r * kWave + lane;
-      int32_t b = 0;
-      if (j < ti.e) {
-        if (staged) {
-          int32_t lo = 0, hi = nwin - 2;
-          while (lo < hi) {
-            const int32_t mid = lo + (hi - lo + 1) / 2;
-            if (stage[mid] <= j) lo = mid; else hi = mid - 1;
-          }
-          b = ti.bag0 + lo;
-        } else {
-          b = bag_of_position(offsets, ti.bag0, ti.bag1, j);
-        }
-      }
-      bag[r] = b;
+      bag[r] = j < ti.e ? stage[j - ti.a] : 0;
     }
   }
   __syncthreads();
