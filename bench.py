@@ -49,6 +49,19 @@ def algorithmic_bytes(cfg, N, U, n_chunks, long_lookups, weighted):
     return dict(fwd=fwd, bwd=bwd, bwd_long=long_kernel)
 
 
+def small_table_bytes(cfg, N):
+    """Algorithmic bytes and MFMA flops of the small-table path (counts kept
+    as uint8, 64 per bag): forward reads indices, offsets and the tables and
+    writes the pooled rows and counts; backward reads counts and gradients,
+    applies Adagrad to the 64 rows of every table."""
+    T, B, D, E = cfg.T, cfg.B, cfg.D, 64
+    fwd = 4 * N + 4 * (T * B + 1) + 4 * T * B * D + T * B * E + 2 * T * E * D
+    bwd = T * B * E + 4 * T * B * D + T * E * (2 * 2 * D + 8)
+    fwd_flop = 2 * T * B * E * D
+    bwd_flop = 2 * 2 * T * B * E * D          # hi and lo products
+    return dict(fwd=fwd, bwd=bwd, fwd_flop=fwd_flop, bwd_flop=bwd_flop)
+
+
 def cpu_baseline(cfg, batch, W0, B_sample):
     """The oracle (single thread, fp64) on the first B_sample bags of every
     table; its time is scaled by lookups to the whole batch."""
@@ -56,6 +69,7 @@ def cpu_baseline(cfg, batch, W0, B_sample):
     import oracle
     T, B = cfg.T, cfg.B
     offs = batch.offsets
+    w16 = W0.dtype != torch.float32
     parts_idx, parts_psw, lengths = [], [], []
     for t in range(T):
         a, e = int(offs[t * B]), int(offs[t * B + B_sample])
@@ -69,7 +83,8 @@ def cpu_baseline(cfg, batch, W0, B_sample):
     keys, bags = oracle.linearize(T, B_sample, cfg.rows, idx, off)
     uk = np.unique(keys)
     kt = torch.from_numpy(uk.astype(np.int64)).to(W0.device)
-    Wrows = W0.index_select(0, kt).cpu().view(torch.int16).numpy().view(np.uint16)
+    Wrows = W0.index_select(0, kt).cpu()
+    Wrows = Wrows.view(torch.int16).numpy().view(np.uint16) if w16 else Wrows.numpy()
     m = np.zeros(uk.size, dtype=np.float32)
     t0 = time.perf_counter()
     keys, bags = oracle.linearize(T, B_sample, cfg.rows, idx, off)
@@ -111,6 +126,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-bags", type=int, default=32768)
+    ap.add_argument("--workload", choices=["large", "small"], default="large",
+                    help="large: T=32 E=2M D=128 bf16 B=131072 (the headline); "
+                         "small: the small-table histogram path, T=64 E=64 D=128 f16 B=32768 L=64")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -127,6 +145,8 @@ def main():
     import bwd_tbe_pooled_amd as tbe
     from workloads import CONFIGS, init_state, init_weights, make_batch
 
+    if args.workload == "small":
+        return main_small(args, torch, tbe)
     cfg = CONFIGS[WORKLOAD]
     log("generating the batch")
     batch = make_batch(cfg)
@@ -234,6 +254,81 @@ def main():
         "cpu_baseline": cpu,
         "context": "B200 figures on the pages (not this workload's hardware): combined "
                    "79.537 ms -> 66.183 ms with forward-side preprocessing",
+    }
+    print(json.dumps(result), flush=True)
+
+
+def main_small(args, torch, tbe):
+    from workloads import CONFIGS, init_state, init_weights, make_batch
+    cfg = CONFIGS[5]
+    log("generating the small-table batch")
+    batch = make_batch(cfg)
+    N = batch.indices.size
+    dev = torch.device("cuda")
+    idx = torch.from_numpy(batch.indices).to(dev)
+    off = torch.from_numpy(batch.offsets).to(dev)
+    grad = torch.from_numpy(batch.grad).to(dev)
+    W = init_weights(cfg, dev)
+    W0 = W.clone() if not args.no_cpu_baseline else None
+    m = init_state(cfg, dev)
+    out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device=dev)
+    timer = tbe.Timer(capacity=args.steps + 1)
+    desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype)
+    assert tbe.tbe_select_path(desc, N, False) == tbe.TBE_PATH_SMALL_TABLE
+    meta = tbe.Meta(desc, N, False)
+    ws_f = tbe.workspace(desc, N, False, tbe.TBE_OP_FORWARD_PREPROCESS)
+    ws_b = tbe.workspace(desc, N, False, tbe.TBE_OP_BACKWARD)
+    torch.cuda.synchronize()
+
+    def step():
+        tbe.tbe_forward(desc, W, idx, off, None, out, meta, ws_f)
+        tbe.tbe_backward_adagrad(desc, W, m, grad, idx, off, None, meta, cfg.lr, cfg.eps, ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    desc.set_timer(timer)
+    timer.reset()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    desc.set_timer(None)
+    st = timer.read()
+    avg = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in st.items()}
+    by = small_table_bytes(cfg, N)
+    fwd_ms, bwd_ms = avg["small_fwd"], avg["small_bwd"] + avg["small_apply"]
+    cand = {"small_fwd": (avg["small_fwd"], by["fwd"]), "small_bwd": (avg["small_bwd"], by["bwd"])}
+    dom = max(cand, key=lambda k: cand[k][0])
+    achieved = cand[dom][1] / (cand[dom][0] * 1e6)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(cfg, batch, W0, min(args.cpu_sample_bags // 4, cfg.B))
+    result = {
+        "metric": "TBE small-table path fwd+bwd(Adagrad) ms and achieved HBM GB/s % peak, "
+                  "T=64 E=64 B=32K D=128",
+        "value": round(wall_ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "T=64 E=64 D=128 f16 B=32768 L=64 uniform rows, small-table "
+                               "histogram path", "T": cfg.T, "E": 64, "D": cfg.D, "B": cfg.B, "N": N,
+                   "parallelism": "single GPU"},
+        "stages_ms": {k: round(v, 4) for k, v in avg.items() if st[k][1]},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "combined_ms": round(fwd_ms + bwd_ms, 4),
+        "fwd": {"bytes": by["fwd"], "GBps": round(by["fwd"] / (fwd_ms * 1e6), 1),
+                "frac_peak": round(by["fwd"] / (fwd_ms * 1e6) / PEAK_HBM_GBPS, 4),
+                "mfma_TFLOPs": round(by["fwd_flop"] / (fwd_ms * 1e9), 2)},
+        "bwd": {"bytes": by["bwd"], "GBps": round(by["bwd"] / (bwd_ms * 1e6), 1),
+                "frac_peak": round(by["bwd"] / (bwd_ms * 1e6) / PEAK_HBM_GBPS, 4),
+                "mfma_TFLOPs": round(by["bwd_flop"] / (avg["small_bwd"] * 1e9), 2)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": cand[dom][1],
+                     "avg_launch_ms": round(cand[dom][0], 4)},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
 

@@ -32,6 +32,7 @@ static bool small_eligible(const tbe_desc* d, int64_t N, int weighted, int64_t m
   if (d->flags & TBE_FLAG_FORCE_GENERIC) return false;
   if (weighted || d->wdtype != TBE_F16) return false;
   if (max_rows > kSmallE || d->D < 64 || d->D > 128) return false;
+  if ((int64_t)d->T * d->D >= (int64_t(1) << 27)) return false;  // gradient offsets stay int32
   const int64_t nbags = (int64_t)d->T * d->B;
   if (nbags == 0) return false;
   return N >= 64 * nbags;  // average bag length N / (T*B) >= 64
@@ -133,6 +134,7 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
     const int64_t rt = (p.cap_runs + kRleTile - 1) / kRleTile;
     L.route_tiles = take(sizeof(int32_t) * (size_t)(3 * rt + 4));
   }
+  if (!generic && op == TBE_OP_FORWARD) L.hist = take((size_t)p.nbags * kSmallE);
   L.has_meta = op == TBE_OP_BACKWARD_SELF;
   if (L.has_meta) {
     int64_t caps[TBE_META_NUM_ARRAYS];
@@ -213,7 +215,9 @@ bool meta_ok_generic(const tbe_meta* m, bool weighted) {
          m->chunk_run && m->chunk_start;
 }
 
-bool meta_ok_small(const tbe_meta* m) { return m && m->counts && m->hist; }
+bool meta_ok_small(const tbe_meta* m) {
+  return m && m->counts && m->hist && ((uintptr_t)m->hist & 15) == 0;  // 16-byte count loads
+}
 
 tbe_meta carve_meta(void* ws, const WsLayout& L) {
   tbe_meta m{};
@@ -344,8 +348,8 @@ tbe_status tbe_forward(const tbe_desc* desc, const void* W, const int32_t* indic
   if (p.path == TBE_PATH_SMALL_TABLE) {
     int32_t* counts = meta ? meta->counts : at<int32_t>(ws, L.flags) + 8;
     timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
-    TBE_TRY_HIP(launch_small_forward(p, W, indices, offsets, tinfo, out, meta ? meta->hist : nullptr,
-                                     counts, s));
+    uint8_t* hist = meta ? meta->hist : at<uint8_t>(ws, L.hist);
+    TBE_TRY_HIP(launch_small_forward(p, W, indices, offsets, tinfo, out, hist, counts, s));
     timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
     return TBE_OK;
   }

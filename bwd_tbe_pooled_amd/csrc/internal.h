@@ -70,6 +70,7 @@ struct WsLayout {
   // backward
   size_t partials;     // long-run chunk partials / small-table partials
   size_t part_counts;  // small-table per-split row counts
+  size_t hist;         // small-table counts of a forward given no metadata
   size_t sched;        // long-chunk schedule (order, buckets, list bounds)
   bool has_pre, has_meta, has_partials;
 };

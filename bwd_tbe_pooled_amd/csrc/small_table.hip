@@ -29,7 +29,15 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int kBagTile = 64;            // bags per forward workgroup / backward stage
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBagTile = 64;            // bags per count tile
+constexpr int kHStride = kSmallE + 4;   // LDS count row, padded: 16-byte aligned, banks rotate
+constexpr int kFwdTiles = 4;            // bag tiles per recounting forward workgroup
+constexpr int kPoolTiles = 8;           // bag tiles per pooling workgroup
+constexpr int kMaxD = 128;              // widest row on this path
+constexpr int kWStride = kMaxD + 8;     // staged W_t row (f16), same bytes as a count row
+constexpr int kTStride = kBagTile + 8;  // transposed f16 count row (16-byte aligned)
+static_assert(kSmallE * kWStride * 2 == kBagTile * kHStride * 4, "W_t stage aliases H");
 constexpr uint32_t kExactCount = 2048;  // counts exact in f16 up to here
 
 __device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
@@ -40,230 +48,467 @@ __device__ __forceinline__ _Float16 w_half(const f16_t* W, int64_t idx) {
   return __builtin_bit_cast(_Float16, W[idx].bits);
 }
 
-// Build the counts of bags [b0, b0+nb) of table t in LDS (uint32 [64][64]).
-__device__ void count_bags(uint32_t (*H)[kSmallE], const int32_t* __restrict__ indices,
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_xor((int)x, m);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
+// Count the lookups of bags [bag0, bag0 + nb) of one table into H. The bags'
+// lookups form one contiguous range of the index array, read with coalesced
+// loads, U per thread in flight; each lookup finds its bag by a binary
+// search over the bags' offsets staged in LDS (the largest bag whose first
+// lookup is at or before it, so empty bags are skipped).
+template <int U = 8>
+__device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
+                           const int32_t* __restrict__ indices,
                            const int32_t* __restrict__ offsets, int64_t bag0, int nb) {
-  for (int i = threadIdx.x; i < kBagTile * kSmallE; i += kThreads) (&H[0][0])[i] = 0;
+  __syncthreads();  // earlier readers of H and s_off are done
+  uint4* h4 = reinterpret_cast<uint4*>(&H[0][0]);
+  for (int q = threadIdx.x; q < kBagTile * kHStride / 4; q += kThreads) h4[q] = uint4{0, 0, 0, 0};
+  // Entries past the last bag read as "after every lookup", so the search
+  // below needs no bounds test.
+  if (threadIdx.x <= kBagTile)
+    s_off[threadIdx.x] = (int)threadIdx.x <= nb ? offsets[bag0 + threadIdx.x] : INT32_MAX;
   __syncthreads();
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  for (int bl = wave; bl < nb; bl += kThreads / kWave) {
-    const int32_t a = offsets[bag0 + bl], e = offsets[bag0 + bl + 1];
-    for (int32_t j = a + lane; j < e; j += kWave)
-      atomicAdd(&H[bl][indices[j] & (kSmallE - 1)], 1u);
+  const int32_t J0 = s_off[0], J1 = s_off[nb];
+  for (int32_t w0 = J0; w0 < J1; w0 += kThreads * U) {
+    int32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t j = w0 + u * kThreads + (int32_t)threadIdx.x;
+      v[u] = j < J1 ? indices[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t j = w0 + u * kThreads + (int32_t)threadIdx.x;
+      if (j < J1) {
+        int k = 0;
+#pragma unroll
+        for (int st = kBagTile / 2; st > 0; st >>= 1) k += s_off[k + st] <= j ? st : 0;
+        atomicAdd(&H[k][v[u] & (kSmallE - 1)], 1u);
+      }
+    }
   }
   __syncthreads();
 }
 
-template <bool WITH_OUT, bool WITH_HIST>
-__global__ __launch_bounds__(kThreads) void small_forward_kernel(
-    const f16_t* __restrict__ W, const int32_t* __restrict__ indices,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ toff,
-    const int32_t* __restrict__ trows, float* __restrict__ out, uint8_t* __restrict__ hist,
-    int32_t* __restrict__ counts, int32_t T, int32_t B, int32_t D) {
-  __shared__ uint32_t H[kBagTile][kSmallE];
-  __shared__ uint32_t s_max;
+// Saturating uint8 counts of the workgroup's 64 bags, written to hist, and
+// the flags: counts[4] when a count exceeds 255, counts[5] when one exceeds
+// 2048. Grid (ceil(B / 64), T); one tile per workgroup keeps many in flight.
+__global__ __launch_bounds__(kThreads) void small_count_kernel(
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
+    uint8_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t B) {
+  __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
+  __shared__ int32_t s_off[kBagTile + 1];
+  __shared__ uint32_t s_wmax[kWaves];
   const int32_t t = blockIdx.y;
-  const int32_t b0 = blockIdx.x * kBagTile;
+  const int32_t b0 = (int32_t)blockIdx.x * kBagTile;
   const int nb = B - b0 < kBagTile ? B - b0 : kBagTile;
   const int64_t bag0 = (int64_t)t * B + b0;
-  if (threadIdx.x == 0) s_max = 0;
-  count_bags(H, indices, offsets, bag0, nb);
-
-  // Save the counts (uint8, saturating) and find the tile's largest count.
-  uint32_t local_max = 0;
+  count_tile<16>(H, s_off, indices, offsets, bag0, nb);
+  uint32_t mx = 0;
   for (int q = threadIdx.x; q < nb * (kSmallE / 4); q += kThreads) {
-    const int bl = q / (kSmallE / 4), e4 = (q % (kSmallE / 4)) * 4;
-    uint32_t packed = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t c = H[bl][e4 + k];
-      local_max = c > local_max ? c : local_max;
-      packed |= (c > 255u ? 255u : c) << (8 * k);
-    }
-    if constexpr (WITH_HIST)
-      *reinterpret_cast<uint32_t*>(hist + (bag0 + bl) * kSmallE + e4) = packed;
+    const int bl = q >> 4, e4 = (q & 15) * 4;
+    const uint4 c = *reinterpret_cast<const uint4*>(&H[bl][e4]);
+    const uint32_t a = c.x > c.y ? c.x : c.y, b = c.z > c.w ? c.z : c.w;
+    mx = mx > (a > b ? a : b) ? mx : (a > b ? a : b);
+    const uint32_t packed = (c.x > 255u ? 255u : c.x) | (c.y > 255u ? 255u : c.y) << 8 |
+                            (c.z > 255u ? 255u : c.z) << 16 | (c.w > 255u ? 255u : c.w) << 24;
+    *reinterpret_cast<uint32_t*>(hist + (bag0 + bl) * kSmallE + e4) = packed;
   }
-  if (local_max > 0) atomicMax(&s_max, local_max);
+  mx = wave_max_u32(mx);
+  if (lane_id() == 0) s_wmax[threadIdx.x / kWave] = mx;
   __syncthreads();
-  if (WITH_HIST && threadIdx.x == 0 && s_max > 255u) atomicOr(&counts[4], 1);
-  if constexpr (!WITH_OUT) return;
+  if (threadIdx.x == 0) {
+    uint32_t tmax = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tmax = s_wmax[w] > tmax ? s_wmax[w] : tmax;
+    if (tmax > 255u) atomicOr(&counts[4], 1);
+    if (tmax > kExactCount) atomicOr(&counts[5], 1);
+  }
+}
 
+// Stage W_t (zero-padded to 64 x 128) in LDS with coalesced loads and pick a
+// wave's B operands out of it: rows e(ks, kb, j) of the two 32-column tiles
+// (w >> 1) and (w >> 1) + 2, for the k order the caller's A operands use.
+template <typename EOF_>
+__device__ void load_w_operands(const f16_t* __restrict__ Wt, int32_t Et, int32_t D,
+                                _Float16 (*Ws)[kWStride], half8 (&bw)[kSmallE / 16][2],
+                                EOF_ e_of) {
+  for (int q = threadIdx.x; q < kSmallE * kMaxD; q += kThreads) {
+    const int e = q / kMaxD, d = q % kMaxD;
+    Ws[e][d] = (e < Et && d < D) ? w_half(Wt, (int64_t)e * D + d) : (_Float16)0.f;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int i = lane & 31, kb = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < kSmallE / 16; ++ks)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int d = ((wave >> 1) + 2 * q) * 32 + i;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bw[ks][q][j] = Ws[e_of(ks, kb, j)][d];
+    }
+}
+
+// Store a wave's two 32 x 32 output blocks (bag rows mt*32.., column tiles
+// (w >> 1) and (w >> 1) + 2) of the tile at bag b0.
+__device__ __forceinline__ void store_out_blocks(float* __restrict__ ot, int64_t ostride,
+                                                 const float16v (&acc)[2], int32_t b0, int nb,
+                                                 int32_t D) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int i = lane & 31, kb = lane >> 5;
+  const int mt = wave & 1;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int d = ((wave >> 1) + 2 * q) * 32 + i;
+    if (d >= D) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int bl = mt * 32 + 8 * (r / 4) + 4 * kb + (r % 4);
+      if (bl < nb) ot[(int64_t)(b0 + bl) * ostride + d] = acc[q][r];
+    }
+  }
+}
+
+// Forward contraction out[b, t-block] = H_t[b, :] . W_t from the saved uint8
+// counts (all at most 255, so counts[4] is clear; else this grid exits and the
+// recounting kernel below runs). A wave's A operand rows are its lanes' bags,
+// read straight from hist: the contraction order over e is free as long as
+// both operands use it, so lane (i, kb) takes e = kb*32 + ks*8 + j, i.e. 32
+// consecutive count bytes, two 16-byte loads per tile. No LDS or barriers in
+// the tile loop; the next tile's counts are loaded before this tile's MFMAs.
+// Grid (ceil(B / (kPoolTiles * 64)), T).
+__global__ __launch_bounds__(kThreads) void small_pool_kernel(
+    const f16_t* __restrict__ W, const uint8_t* __restrict__ hist,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ toff,
+    const int32_t* __restrict__ trows, float* __restrict__ out, int32_t T, int32_t B,
+    int32_t D) {
+  __shared__ __align__(16) _Float16 Ws[kSmallE][kWStride];
+  if (counts[4] != 0) return;
+  const int32_t t = blockIdx.y;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int i = lane & 31, kb = lane >> 5;
+  const int mt = wave & 1;
+  half8 bw[kSmallE / 16][2];
+  load_w_operands(W + (int64_t)toff[t] * D, trows[t], D, Ws, bw,
+                  [](int ks, int kb_, int j) { return kb_ * 32 + ks * 8 + j; });
+  float* ot = out + (int64_t)t * D;
+  const int64_t ostride = (int64_t)T * D;
+  const int32_t tb0 = (int32_t)blockIdx.x * kPoolTiles * kBagTile;
+  auto load_counts = [&](int32_t b0, uint4& h0, uint4& h1) {
+    const int32_t b = b0 + mt * 32 + i;
+    h0 = h1 = uint4{0, 0, 0, 0};
+    if (b < B) {
+      const uint4* p = reinterpret_cast<const uint4*>(hist + ((int64_t)t * B + b) * kSmallE + kb * 32);
+      h0 = p[0];
+      h1 = p[1];
+    }
+  };
+  uint4 n0, n1;
+  load_counts(tb0, n0, n1);
+  for (int k = 0; k < kPoolTiles; ++k) {
+    const int32_t b0 = tb0 + k * kBagTile;
+    if (b0 >= B) break;
+    const int nb = B - b0 < kBagTile ? B - b0 : kBagTile;
+    const uint32_t w8[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+    if (k + 1 < kPoolTiles && b0 + kBagTile < B) load_counts(b0 + kBagTile, n0, n1);
+    float16v acc[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kSmallE / 16; ++ks) {
+      half8 a;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        a[j] = (_Float16)(float)((w8[2 * ks + j / 4] >> (8 * (j % 4))) & 0xffu);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[q] = mfma32(a, bw[ks][q], acc[q]);
+    }
+    store_out_blocks(ot, ostride, acc, b0, nb, D);
+  }
+}
+
+// Forward when some saved count saturated (counts[4] set; else this grid
+// exits): recount each 64-bag tile exactly in LDS, then contract on the
+// matrix cores, or in plain f32 for a tile with a count above 2048.
+// Grid (ceil(B / (kFwdTiles * 64)), T).
+__global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
+    const f16_t* __restrict__ W, const int32_t* __restrict__ indices,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ toff, const int32_t* __restrict__ trows, float* __restrict__ out,
+    int32_t T, int32_t B, int32_t D) {
+  __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
+  __shared__ int32_t s_off[kBagTile + 1];
+  __shared__ uint32_t s_wmax[kWaves];
+  if (counts[4] == 0) return;
+  const int32_t t = blockIdx.y;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int i = lane & 31, kb = lane >> 5;
+  const int mt = wave & 1;
   const int32_t Et = trows[t];
   const f16_t* Wt = W + (int64_t)toff[t] * D;
   float* ot = out + (int64_t)t * D;
   const int64_t ostride = (int64_t)T * D;
+  half8 bw[kSmallE / 16][2];
+  load_w_operands(Wt, Et, D, reinterpret_cast<_Float16(*)[kWStride]>(&H[0][0]), bw,
+                  [](int ks, int kb_, int j) { return ks * 16 + kb_ * 8 + j; });
 
-  if (s_max > kExactCount) {
-    // Counts beyond f16's exact range: plain f32 dot products over the rows.
-    for (int q = threadIdx.x; q < nb * D; q += kThreads) {
-      const int bl = q / D, d = q % D;
-      float acc = 0.f;
-      for (int e = 0; e < Et && e < kSmallE; ++e)
-        acc += (float)H[bl][e] * (float)w_half(Wt, (int64_t)e * D + d);
-      ot[(int64_t)(b0 + bl) * ostride + d] = acc;
+  for (int k = 0; k < kFwdTiles; ++k) {
+    const int32_t b0 = ((int32_t)blockIdx.x * kFwdTiles + k) * kBagTile;
+    if (b0 >= B) break;
+    const int nb = B - b0 < kBagTile ? B - b0 : kBagTile;
+    count_tile(H, s_off, indices, offsets, (int64_t)t * B + b0, nb);
+    uint32_t mx = 0;
+    for (int q = threadIdx.x; q < nb * (kSmallE / 4); q += kThreads) {
+      const uint4 c = *reinterpret_cast<const uint4*>(&H[q >> 4][(q & 15) * 4]);
+      const uint32_t a = c.x > c.y ? c.x : c.y, b = c.z > c.w ? c.z : c.w;
+      mx = mx > (a > b ? a : b) ? mx : (a > b ? a : b);
     }
-    return;
-  }
+    mx = wave_max_u32(mx);
+    if (lane == 0) s_wmax[wave] = mx;
+    __syncthreads();
+    uint32_t tmax = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) tmax = s_wmax[w] > tmax ? s_wmax[w] : tmax;
 
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const int i = lane & 31, kb = lane >> 5;
-  const int mt = wave & 1;             // bag rows mt*32 .. +32
-  const int NT = (D + 31) / 32;        // 32-column tiles
-  float16v acc[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < kSmallE / 16; ++ks) {
-    half8 a;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = (_Float16)(float)H[mt * 32 + i][ks * 16 + kb * 8 + j];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nt = (wave >> 1) + 2 * q;
-      if (nt < NT) {
-        const int d = nt * 32 + i;
-        half8 bv;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int e = ks * 16 + kb * 8 + j;
-          bv[j] = (e < Et && d < D) ? w_half(Wt, (int64_t)e * D + d) : (_Float16)0.f;
-        }
-        acc[q] = mfma32(a, bv, acc[q]);
+    if (tmax > kExactCount) {
+      // Counts beyond f16's exact range: plain f32 dot products over the rows.
+      for (int q = threadIdx.x; q < nb * D; q += kThreads) {
+        const int bl = q / D, d = q % D;
+        float acc = 0.f;
+        for (int e = 0; e < Et && e < kSmallE; ++e)
+          acc += (float)H[bl][e] * (float)w_half(Wt, (int64_t)e * D + d);
+        ot[(int64_t)(b0 + bl) * ostride + d] = acc;
       }
+      continue;
     }
-  }
+    float16v acc[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int nt = (wave >> 1) + 2 * q;
-    if (nt >= NT) continue;
-    const int d = nt * 32 + i;
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r / 4) + 4 * kb + (r % 4);
-      const int bl = mt * 32 + row;
-      if (bl < nb && d < D) ot[(int64_t)(b0 + bl) * ostride + d] = acc[q][r];
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kSmallE / 16; ++ks) {
+      const uint4* hp = reinterpret_cast<const uint4*>(&H[mt * 32 + i][ks * 16 + kb * 8]);
+      const uint4 c0 = hp[0], c1 = hp[1];
+      half8 a;
+      a[0] = (_Float16)(float)c0.x; a[1] = (_Float16)(float)c0.y;
+      a[2] = (_Float16)(float)c0.z; a[3] = (_Float16)(float)c0.w;
+      a[4] = (_Float16)(float)c1.x; a[5] = (_Float16)(float)c1.y;
+      a[6] = (_Float16)(float)c1.z; a[7] = (_Float16)(float)c1.w;
+      // (operands of columns past D are zero: no test, so acc stays in AGPRs)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[q] = mfma32(a, bw[ks][q], acc[q]);
     }
+    store_out_blocks(ot, ostride, acc, b0, nb, D);
   }
 }
 
 // One workgroup per (table, split of the batch): partial G = H^T . grad over
 // the split's bags, written to partials[(t*splits + s)][64][D], and the
-// split's per-row counts to part_counts[(t*splits + s)][64].
+// split's per-row counts to part_counts[(t*splits + s)][64]. Wave w owns the
+// 32 columns w*32.. and both 32-row halves of G; each lane keeps the next
+// tile's gradient values in registers while the current tile is contracted.
+// Runs only when every count is exact in f16 (counts[5] clear).
 __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     const float* __restrict__ grad, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, float* __restrict__ partials,
     int32_t* __restrict__ part_counts, int32_t T, int32_t B, int32_t D, int32_t splits,
     int32_t bags_per_split) {
-  __shared__ uint32_t H[kBagTile][kSmallE];
-  __shared__ uint32_t s_max;
-  __shared__ float s_part[kSmallE][129];  // fallback accumulators (D <= 128)
+  __shared__ __align__(16) uint32_t H[kBagTile][kHStride];     // recounted counts
+  __shared__ __align__(16) _Float16 HT[kSmallE][kTStride];     // counts, row-major by table row
+  __shared__ int32_t s_off[kBagTile + 1];
+  if (counts[5] != 0) return;
   const int32_t t = blockIdx.y;
   const int32_t s = blockIdx.x;
-  const int32_t sb0 = s * bags_per_split;
+  const int32_t sb0 = s * bags_per_split < B ? s * bags_per_split : B;
   const int32_t sb1 = sb0 + bags_per_split < B ? sb0 + bags_per_split : B;
   const bool recount = counts[4] != 0;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int i = lane & 31, kb = lane >> 5;
-  const int nt = wave;                 // this wave's 32 columns
+  const int nt = wave;
   const int NT = (D + 31) / 32;
   const int d = nt * 32 + i;
+  const bool has_col = nt < NT && d < D;
   const float* gt = grad + (int64_t)t * D;
   const int64_t gstride = (int64_t)T * D;
+  // offset of (bag kb*8, column d) from a 16-bag group's first row; columns
+  // past D read column D-1 and are zeroed after the load
+  const int32_t lane_off = kb * 8 * (int32_t)gstride + (d < D ? d : D - 1);
 
   float16v acc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
-  for (int q = threadIdx.x; q < kSmallE * 129; q += kThreads) (&s_part[0][0])[q] = 0.f;
-  uint32_t row_count = 0;  // thread e < 64 accumulates the count of row e
+  uint32_t cnt[2] = {0u, 0u};  // count of row q*32 + i over this lane's half of the bags
+
+  // gradient of bag b0 + ks*16 + kb*8 + j at column d, in gn[ks*8 + j]
+  float gn[kBagTile / 2];
+  auto load_grad = [&](int32_t b0) {
+    const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
+    if (nb == kBagTile) {
+#pragma unroll
+      for (int ks = 0; ks < kBagTile / 16; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float* row = gt + (int64_t)(b0 + ks * 16 + j) * gstride;  // uniform
+          const float g = row[lane_off];
+          gn[ks * 8 + j] = has_col ? g : 0.f;
+        }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kBagTile / 16; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float* row = gt + (int64_t)(b0 + ks * 16 + j) * gstride;
+          const int bl = ks * 16 + kb * 8 + j;
+          gn[ks * 8 + j] = (has_col && bl < nb) ? row[lane_off] : 0.f;
+        }
+    }
+  };
+  if (sb0 < sb1) load_grad(sb0);
+
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const half2v ones = {(_Float16)1.f, (_Float16)1.f};
 
   for (int32_t b0 = sb0; b0 < sb1; b0 += kBagTile) {
     const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
     const int64_t bag0 = (int64_t)t * B + b0;
-    __syncthreads();
-    if (threadIdx.x == 0) s_max = 0;
-    if (recount) {
-      count_bags(H, indices, offsets, bag0, nb);
-    } else {
-      for (int q = threadIdx.x; q < kBagTile * (kSmallE / 4); q += kThreads) {
-        const int bl = q / (kSmallE / 4), e4 = (q % (kSmallE / 4)) * 4;
-        const uint32_t packed =
-            bl < nb ? *reinterpret_cast<const uint32_t*>(hist + (bag0 + bl) * kSmallE + e4) : 0u;
+    // B operands: this tile's gradients split into hi = f16(g) and
+    // lo = f16((g - hi) * 2^11); then the next tile's loads go out.
+    half8 hi[kBagTile / 16], lo[kBagTile / 16];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) H[bl][e4 + k] = (packed >> (8 * k)) & 0xffu;
-      }
-      __syncthreads();
-    }
-    uint32_t local_max = 0;
-    for (int q = threadIdx.x; q < nb * kSmallE; q += kThreads) {
-      const uint32_t c = (&H[0][0])[q];
-      local_max = c > local_max ? c : local_max;
-    }
-    if (local_max > kExactCount) atomicMax(&s_max, local_max);
-    if (threadIdx.x < kSmallE)
-      for (int bl = 0; bl < nb; ++bl) row_count += H[bl][threadIdx.x];
-    __syncthreads();
-
-    if (s_max > kExactCount) {
-      // f32 fallback for counts beyond f16's exact range.
-      for (int q = threadIdx.x; q < kSmallE * D; q += kThreads) {
-        const int e = q / D, dd = q % D;
-        float a = 0.f;
-        for (int bl = 0; bl < nb; ++bl)
-          a += (float)H[bl][e] * gt[(int64_t)(b0 + bl) * gstride + dd];
-        s_part[e][dd] += a;
-      }
-      continue;
-    }
-    if (nt >= NT) continue;
-#pragma unroll
-    for (int ks = 0; ks < kBagTile / 16; ++ks) {
-      // B operand: the gradient of 8 bags at column d, split into hi/lo halves.
-      half8 hi, lo;
+    for (int ks = 0; ks < kBagTile / 16; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int bl = ks * 16 + kb * 8 + j;
-        const float g = (bl < nb && d < D) ? gt[(int64_t)(b0 + bl) * gstride + d] : 0.f;
+        const float g = gn[ks * 8 + j];
         const _Float16 h = (_Float16)g;
-        hi[j] = h;
-        lo[j] = (_Float16)((g - (float)h) * 2048.f);
+        hi[ks][j] = h;
+        lo[ks][j] = (_Float16)((g - (float)h) * 2048.f);
+      }
+    if (b0 + kBagTile < sb1) load_grad(b0 + kBagTile);
+
+    if (recount) count_tile(H, s_off, indices, offsets, bag0, nb);
+    else __syncthreads();  // earlier readers of HT are done
+    {
+      // Counts of bag bl, rows e16..e16+15, into HT[e][bl] as f16 (exact).
+      const int bl = threadIdx.x >> 2, e16 = (threadIdx.x & 3) * 16;
+      uint32_t c[16];
+      if (recount) {
+        const uint4* hp = reinterpret_cast<const uint4*>(&H[bl][e16]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = hp[q];
+          c[4 * q] = v.x; c[4 * q + 1] = v.y; c[4 * q + 2] = v.z; c[4 * q + 3] = v.w;
+        }
+      } else {
+        uint4 v = uint4{0, 0, 0, 0};
+        if (bl < nb) v = *reinterpret_cast<const uint4*>(hist + (bag0 + bl) * kSmallE + e16);
+        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 16; ++q) c[q] = (wds[q >> 2] >> (8 * (q & 3))) & 0xffu;
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        half8 a_hi, a_lo;
+      for (int q = 0; q < 16; ++q) HT[e16 + q][bl] = (_Float16)(float)c[q];
+    }
+    __syncthreads();
+
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float c = (float)H[ks * 16 + kb * 8 + j][mt * 32 + i];
-          a_hi[j] = (_Float16)c;
-          a_lo[j] = (_Float16)(c * (1.f / 2048.f));
+    for (int ks = 0; ks < kBagTile / 16; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const half8 a_hi = *reinterpret_cast<const half8*>(&HT[mt * 32 + i][ks * 16 + kb * 8]);
+        const half8 a_lo = a_hi * (_Float16)(1.f / 2048.f);  // exact: counts <= 2048
+        float tc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const half2v pr = {a_hi[j], a_hi[j + 1]};
+          tc = __builtin_amdgcn_fdot2(pr, ones, tc, false);
         }
-        acc[mt] = mfma32(a_hi, hi, acc[mt]);
-        acc[mt] = mfma32(a_lo, lo, acc[mt]);
+        cnt[mt] += (uint32_t)tc;
+        acc[mt] = mfma32(a_hi, hi[ks], acc[mt]);  // zero gradients past D
+        acc[mt] = mfma32(a_lo, lo[ks], acc[mt]);
       }
     }
   }
-  __syncthreads();
+
   float* pt = partials + ((int64_t)t * splits + s) * kSmallE * D;
-  if (nt < NT) {
+  if (has_col) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int e = mt * 32 + 8 * (r / 4) + 4 * kb + (r % 4);
-        if (d < D) s_part[e][d] += acc[mt][r];
+        pt[(int64_t)e * D + d] = acc[mt][r];
       }
   }
-  __syncthreads();
-  for (int q = threadIdx.x; q < kSmallE * D; q += kThreads) pt[q] = s_part[q / D][q % D];
+  if (wave == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint32_t c = cnt[mt] + (uint32_t)__shfl_xor((int)cnt[mt], 32);
+      if (kb == 0) part_counts[((int64_t)t * splits + s) * kSmallE + mt * 32 + i] = (int32_t)c;
+    }
+  }
+}
+
+// The same partial sums in plain f32 arithmetic, for problems where some
+// count exceeds 2048 (counts[5] set): counts are recounted from the indices
+// and each thread accumulates 32 (row, column) elements of G over the bags.
+__global__ __launch_bounds__(kThreads) void small_backward_wide_kernel(
+    const float* __restrict__ grad, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
+    float* __restrict__ partials, int32_t* __restrict__ part_counts, int32_t T, int32_t B,
+    int32_t D, int32_t splits, int32_t bags_per_split) {
+  __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
+  __shared__ int32_t s_off[kBagTile + 1];
+  if (counts[5] == 0) return;
+  const int32_t t = blockIdx.y;
+  const int32_t s = blockIdx.x;
+  const int32_t sb0 = s * bags_per_split < B ? s * bags_per_split : B;
+  const int32_t sb1 = sb0 + bags_per_split < B ? sb0 + bags_per_split : B;
+  const int d = threadIdx.x % kMaxD;
+  const int e0 = (threadIdx.x / kMaxD) * (kSmallE / 2);  // rows e0 .. e0+31
+  const float* gt = grad + (int64_t)t * D;
+  const int64_t gstride = (int64_t)T * D;
+  float acc[kSmallE / 2];
+#pragma unroll
+  for (int r = 0; r < kSmallE / 2; ++r) acc[r] = 0.f;
+  uint32_t cnt = 0;  // thread e < 64: count of row e
+  for (int32_t b0 = sb0; b0 < sb1; b0 += kBagTile) {
+    const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
+    count_tile(H, s_off, indices, offsets, (int64_t)t * B + b0, nb);
+    if (threadIdx.x < kSmallE)
+      for (int bl = 0; bl < nb; ++bl) cnt += H[bl][threadIdx.x];
+    if (d < D) {
+      for (int bl = 0; bl < nb; ++bl) {
+        const float g = gt[(int64_t)(b0 + bl) * gstride + d];
+#pragma unroll
+        for (int r = 0; r < kSmallE / 2; ++r) acc[r] += (float)H[bl][e0 + r] * g;
+      }
+    }
+  }
+  float* pt = partials + ((int64_t)t * splits + s) * kSmallE * D;
+  if (d < D) {
+#pragma unroll
+    for (int r = 0; r < kSmallE / 2; ++r) pt[(int64_t)(e0 + r) * D + d] = acc[r];
+  }
   if (threadIdx.x < kSmallE)
-    part_counts[((int64_t)t * splits + s) * kSmallE + threadIdx.x] = (int32_t)row_count;
+    part_counts[((int64_t)t * splits + s) * kSmallE + threadIdx.x] = (int32_t)cnt;
 }
 
 // Reduce the splits of each (table, row) in ascending split order and apply
@@ -325,23 +570,21 @@ hipError_t launch_small_forward(const Problem& p, const void* W, const int32_t* 
                                 uint8_t* hist, int32_t* counts, hipStream_t s) {
   hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, s, counts);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (p.B == 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.B + kBagTile - 1) / kBagTile), (unsigned)p.T);
+  if (err != hipSuccess || p.B == 0) return err;
   const int32_t* toff = tinfo;
   const int32_t* trows = tinfo + p.T;
-  if (out && hist)
-    hipLaunchKernelGGL((small_forward_kernel<true, true>), grid, dim3(kThreads), 0, s,
-                       (const f16_t*)W, indices, offsets, toff, trows, out, hist, counts, p.T,
-                       p.B, p.D);
-  else if (out)
-    hipLaunchKernelGGL((small_forward_kernel<true, false>), grid, dim3(kThreads), 0, s,
-                       (const f16_t*)W, indices, offsets, toff, trows, out, hist, counts, p.T,
-                       p.B, p.D);
-  else
-    hipLaunchKernelGGL((small_forward_kernel<false, true>), grid, dim3(kThreads), 0, s,
-                       (const f16_t*)W, indices, offsets, toff, trows, out, hist, counts, p.T,
-                       p.B, p.D);
+  hipLaunchKernelGGL(small_count_kernel, dim3((unsigned)((p.B + kBagTile - 1) / kBagTile), (unsigned)p.T),
+                     dim3(kThreads), 0, s, indices, offsets, hist, counts, p.B);
+  if ((err = hipGetLastError()) != hipSuccess || !out) return err;
+  // Exactly one of the two computes the output, chosen on the device by counts[4].
+  const int64_t pool_bags = (int64_t)kBagTile * kPoolTiles;
+  hipLaunchKernelGGL(small_pool_kernel, dim3((unsigned)((p.B + pool_bags - 1) / pool_bags), (unsigned)p.T),
+                     dim3(kThreads), 0, s, (const f16_t*)W, hist, counts, toff, trows, out, p.T,
+                     p.B, p.D);
+  const int64_t re_bags = (int64_t)kBagTile * kFwdTiles;
+  hipLaunchKernelGGL(small_recount_forward_kernel,
+                     dim3((unsigned)((p.B + re_bags - 1) / re_bags), (unsigned)p.T), dim3(kThreads), 0,
+                     s, (const f16_t*)W, indices, offsets, counts, toff, trows, out, p.T, p.B, p.D);
   return hipGetLastError();
 }
 
@@ -352,7 +595,10 @@ hipError_t launch_small_backward(const Problem& p, const float* grad, const uint
   const int splits = p.small_splits;
   int32_t per = (p.B + splits - 1) / splits;
   const dim3 grid((unsigned)splits, (unsigned)p.T);
+  // Exactly one of the two does the work, chosen on the device by counts[5].
   hipLaunchKernelGGL(small_backward_kernel, grid, dim3(kThreads), 0, s, grad, hist, counts, indices,
+                     offsets, partials, part_counts, p.T, p.B, p.D, splits, per);
+  hipLaunchKernelGGL(small_backward_wide_kernel, grid, dim3(kThreads), 0, s, grad, counts, indices,
                      offsets, partials, part_counts, p.T, p.B, p.D, splits, per);
   return hipGetLastError();
 }

@@ -123,7 +123,8 @@ typedef struct {
  *
  * Generic path, with U runs (unique keys) over N lookups:
  *   counts[0] = U, counts[1] = n_short, counts[2] = n_long, counts[3] = n_chunks,
- *   counts[4] = 1 if a small-table count exceeded 255 (else 0);
+ *   counts[4] = 1 if a small-table count exceeded 255 (else 0),
+ *   counts[5] = 1 if a small-table count exceeded 2048 (else 0);
  *   run_keys[u]       linearized key of run u, strictly increasing;
  *   run_offsets[u]    first sorted slot of run u; run_offsets[U] = N;
  *   sorted_pos[k]     lookup position at sorted slot k (stable order); optional:
@@ -138,8 +139,11 @@ typedef struct {
  *   chunk_run[c], chunk_start[c]: chunk c covers sorted slots
  *                     chunk_start[c] .. min(chunk_start[c]+C, end of its run)-1.
  * Small-table path:
- *   hist[(t*B + b)*64 + e] = min(255, count of row e in bag (t,b)), uint8;
- *   counts[4] flags saturation (the backward then recounts from indices).
+ *   hist[(t*B + b)*64 + e] = min(255, count of row e in bag (t,b)), uint8,
+ *                     16-byte aligned (else TBE_ERR_ARG);
+ *   counts[4] flags saturation (the backward then recounts from indices);
+ *   counts[5] flags counts beyond f16's exact integers (the backward then
+ *   contracts in f32 arithmetic instead of on the matrix cores).
  * Pointers the chosen path does not use may be NULL.
  */
 typedef struct {

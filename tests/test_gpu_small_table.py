@@ -20,7 +20,8 @@ def _need_gpu():
     import bwd_tbe_pooled_amd  # noqa: F401
 
 
-def _check(cfg, batch, meta_in_forward=True, backward_meta=True, expect_saturated=False):
+def _check(cfg, batch, meta_in_forward=True, backward_meta=True, expect_saturated=False,
+           expect_wide=False):
     print(f"\n[small-table] T={cfg.T} B={cfg.B} D={cfg.D} E={max(cfg.rows)} N={batch.indices.size} "
           f"meta_fwd={meta_in_forward} meta_bwd={backward_meta}", flush=True)
     W, m = fresh_params(cfg)
@@ -37,6 +38,7 @@ def _check(cfg, batch, meta_in_forward=True, backward_meta=True, expect_saturate
     hist = r["meta"]["hist"].cpu().numpy().reshape(cfg.T, cfg.B, 64)
     np.testing.assert_array_equal(hist, np.minimum(H, 255))
     assert int(r["meta"]["counts"][4]) == int(expect_saturated)
+    assert int(r["meta"]["counts"][5]) == int(expect_wide)
     assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], "small-table")
     assert_untouched_unchanged(W0, W, m0, m, uk)
     return r
@@ -54,6 +56,14 @@ def test_config5_reduced_batch():
     _check(batch.cfg, batch)
 
 
+def test_forward_without_metadata_then_preprocess():
+    """Forward given no metadata keeps its counts in the workspace; the
+    metadata then comes from tbe_preprocess."""
+    cfg = CONFIGS[5]
+    batch = make_batch(cfg, B=700)
+    _check(batch.cfg, batch, meta_in_forward=False)
+
+
 def test_backward_without_saved_counts():
     cfg = CONFIGS[5]
     batch = make_batch(cfg, B=300)
@@ -67,19 +77,33 @@ def test_shapes(D, E):
     _check(cfg, batch)
 
 
-def test_saturated_counts_are_recounted():
-    """Bags with more than 255 lookups of one row: the saved uint8 counts
-    saturate, the flag is raised, and the backward recounts from indices."""
+def _saturated_batch(long_len):
     rng = np.random.default_rng(7)
     T, B, D, E = 2, 96, 128, 64
     lengths = np.full(T * B, 80)
     lengths[5] = 300
-    lengths[B + 7] = 2500                      # > 2048: beyond f16-exact counts
+    lengths[B + 7] = long_len
     offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     idx = rng.integers(0, E, size=offsets[-1]).astype(np.int32)
     idx[offsets[5]:offsets[6]] = 3
     idx[offsets[B + 7]:offsets[B + 8]] = 9
     cfg = _cfg(T, B, D, E, 80, seed=11)
     grad = rng.standard_normal((B, T * D)).astype(np.float32)
-    batch = Batch(cfg=cfg, indices=idx, offsets=offsets, psw=None, grad=grad)
-    _check(cfg, batch, expect_saturated=True)
+    return cfg, Batch(cfg=cfg, indices=idx, offsets=offsets, psw=None, grad=grad)
+
+
+@pytest.mark.parametrize("meta_in_forward", [True, False])
+def test_saturated_counts_are_recounted(meta_in_forward):
+    """Bags with more than 255 lookups of one row (but at most 2048): the saved
+    uint8 counts saturate, the flag is raised, and both directions recount
+    from indices and still contract on the matrix cores."""
+    cfg, batch = _saturated_batch(2048)
+    _check(cfg, batch, meta_in_forward=meta_in_forward, expect_saturated=True)
+
+
+@pytest.mark.parametrize("meta_in_forward", [True, False])
+def test_counts_beyond_f16_exact_integers(meta_in_forward):
+    """A bag with 2500 lookups of one row: counts above 2048 are not exact in
+    f16, so both directions fall back to f32 arithmetic."""
+    cfg, batch = _saturated_batch(2500)
+    _check(cfg, batch, meta_in_forward=meta_in_forward, expect_saturated=True, expect_wide=True)
