@@ -20,6 +20,11 @@ LIB_PATH = os.environ.get("TBE_LIBRARY") or os.path.join(_HERE, "libtbe.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bwd_tbe_pooled_amd.build`")
 
+# torch first: the library then binds to the HIP runtime torch has loaded,
+# so tensors, streams and kernels share one runtime in the process (loading
+# the library first would bring in a second HIP runtime beside torch's).
+import torch  # noqa: E402
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # --- C types ----------------------------------------------------------------
@@ -80,10 +85,17 @@ _lib.tbe_timer_destroy.restype = None
 _lib.tbe_timer_destroy.argtypes = [_P]
 
 
+_lib.tbe_last_error.restype = ctypes.c_char_p
+_lib.tbe_last_error.argtypes = []
+
+
 class TbeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {tbe_status_str(status)} (status {status})")
+        msg = f"{where}: {tbe_status_str(status)} (status {status})"
+        if status == TBE_ERR_HIP:
+            msg += ": " + _lib.tbe_last_error().decode()
+        super().__init__(msg)
 
 
 def tbe_status_str(status: int) -> str:
@@ -122,7 +134,6 @@ def _ptr(t):
 
 
 def _stream(stream):
-    import torch
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
@@ -151,7 +162,6 @@ class Meta:
     def __init__(self, desc: Desc, N: int, weighted: bool, device="cuda", with_pos: bool = True):
         """with_pos=False leaves sorted_pos NULL: the sort then does not carry
         lookup positions (the backward never reads them)."""
-        import torch
         caps = tbe_meta_capacity(desc, N, weighted)
         self.caps = dict(zip(META_FIELDS, caps))
         self.path = tbe_select_path(desc, N, weighted)
@@ -180,7 +190,6 @@ class Meta:
 
 
 def workspace(desc: Desc, N: int, weighted: bool, op: int, device="cuda"):
-    import torch
     nbytes = tbe_workspace_bytes(desc, N, weighted, op)
     if nbytes == 0:
         raise TbeError(TBE_ERR_ARG, "tbe_workspace_bytes")
@@ -237,6 +246,6 @@ class Timer:
 
 def exported_symbols() -> list:
     """Names the library exports from include/tbe.h (used by host tests)."""
-    return ["tbe_status_str", "tbe_select_path", "tbe_meta_capacity", "tbe_workspace_bytes",
+    return ["tbe_status_str", "tbe_last_error", "tbe_select_path", "tbe_meta_capacity", "tbe_workspace_bytes",
             "tbe_forward", "tbe_preprocess", "tbe_backward_adagrad", "tbe_timer_create",
             "tbe_timer_reset", "tbe_timer_read", "tbe_timer_destroy"]

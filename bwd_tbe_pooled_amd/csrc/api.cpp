@@ -1,6 +1,8 @@
 // C ABI of the TBE library: argument validation (host, before any launch),
 // path selection, workspace carving and the launch sequence of each call on
-// the caller's stream. No allocation of device memory, no global state.
+// the caller's stream. No allocation of device memory; the only global state
+// is the per-thread text of the last HIP failure.
+#include <cstdio>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -199,9 +201,18 @@ using namespace tbe;
 
 namespace {
 
+thread_local char g_last_error[256] = "";
+
+tbe_status hip_failure(hipError_t e, const char* what) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s (%s) in %s", hipGetErrorName(e),
+                hipGetErrorString(e), what);
+  return TBE_ERR_HIP;
+}
+
 #define TBE_TRY_HIP(expr)                                  \
   do {                                                     \
-    if ((expr) != hipSuccess) return TBE_ERR_HIP;          \
+    const hipError_t tbe_e_ = (expr);                      \
+    if (tbe_e_ != hipSuccess) return hip_failure(tbe_e_, #expr); \
   } while (0)
 
 template <typename T>
@@ -242,6 +253,10 @@ tbe_meta carve_meta(void* ws, const WsLayout& L) {
 // Common prologue: table info upload and optional validation.
 tbe_status prologue(const tbe_desc* d, const Problem& p, const int32_t* indices,
                     const int32_t* offsets, void* ws, const WsLayout& L, hipStream_t s) {
+  // The launchers report hipGetLastError(); clear what an earlier runtime
+  // call of the caller's may have left there, so that only this call's own
+  // launch errors are reported.
+  (void)hipGetLastError();
   int32_t* tinfo = at<int32_t>(ws, L.tinfo);
   TBE_TRY_HIP(launch_fill_tinfo(p, d->rows, tinfo, s));
   if (d->flags & TBE_FLAG_VALIDATE) {
@@ -294,6 +309,8 @@ tbe_status check_ws(const Problem& p, tbe_op op, void* ws, size_t ws_bytes, WsLa
 }  // namespace
 
 extern "C" {
+
+const char* tbe_last_error(void) { return g_last_error; }
 
 const char* tbe_status_str(tbe_status s) {
   switch (s) {

@@ -34,6 +34,7 @@ constexpr int kBagTile = 64;            // bags per count tile
 constexpr int kHStride = kSmallE + 4;   // LDS count row, padded: 16-byte aligned, banks rotate
 constexpr int kFwdTiles = 4;            // bag tiles per recounting forward workgroup
 constexpr int kPoolTiles = 8;           // bag tiles per pooling workgroup
+constexpr int kCountTiles = 4;          // bag tiles per counting workgroup
 constexpr int kMaxD = 128;              // widest row on this path
 constexpr int kWStride = kMaxD + 8;     // staged W_t row (f16), same bytes as a count row
 constexpr int kTStride = kBagTile + 8;  // transposed f16 count row (16-byte aligned)
@@ -57,71 +58,149 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return x;
 }
 
-// Count the lookups of bags [bag0, bag0 + nb) of one table into H. The bags'
-// lookups form one contiguous range of the index array, read with coalesced
-// loads, U per thread in flight; each lookup finds its bag by a binary
-// search over the bags' offsets staged in LDS (the largest bag whose first
-// lookup is at or before it, so empty bags are skipped).
-template <int U = 8>
+// Count the lookups of bags [bag0, bag0 + nb) of one table into H. Wave w
+// owns bags 16w .. 16w+15; a bag's lookups are contiguous, so its lanes read
+// 64 of them with one coalesced load and add them to the bag's row with one
+// LDS atomic, the bag known without any search. The first 64 lookups of
+// INFLIGHT bags are loaded before any of them is counted; lookups past the
+// 64th follow bag by bag, eight loads in flight.
+template <int INFLIGHT = 4>
 __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
                            const int32_t* __restrict__ indices,
                            const int32_t* __restrict__ offsets, int64_t bag0, int nb) {
+  constexpr int NBW = kBagTile / kWaves;
   __syncthreads();  // earlier readers of H and s_off are done
   uint4* h4 = reinterpret_cast<uint4*>(&H[0][0]);
   for (int q = threadIdx.x; q < kBagTile * kHStride / 4; q += kThreads) h4[q] = uint4{0, 0, 0, 0};
-  // Entries past the last bag read as "after every lookup", so the search
-  // below needs no bounds test.
-  if (threadIdx.x <= kBagTile)
-    s_off[threadIdx.x] = (int)threadIdx.x <= nb ? offsets[bag0 + threadIdx.x] : INT32_MAX;
+  if ((int)threadIdx.x <= nb) s_off[threadIdx.x] = offsets[bag0 + threadIdx.x];
   __syncthreads();
-  const int32_t J0 = s_off[0], J1 = s_off[nb];
-  for (int32_t w0 = J0; w0 < J1; w0 += kThreads * U) {
-    int32_t v[U];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int bw0 = wave * NBW;
+  for (int u0 = 0; u0 < NBW; u0 += INFLIGHT) {
+    int32_t v[INFLIGHT];
+    bool ok[INFLIGHT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t j = w0 + u * kThreads + (int32_t)threadIdx.x;
-      v[u] = j < J1 ? indices[j] : 0;
+    for (int u = 0; u < INFLIGHT; ++u) {
+      const int bl = bw0 + u0 + u;
+      const int32_t a = bl < nb ? s_off[bl] : 0;
+      const int32_t len = bl < nb ? s_off[bl + 1] - a : 0;
+      ok[u] = lane < len;
+      v[u] = ok[u] ? indices[a + lane] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t j = w0 + u * kThreads + (int32_t)threadIdx.x;
-      if (j < J1) {
-        int k = 0;
+    for (int u = 0; u < INFLIGHT; ++u)
+      if (ok[u]) atomicAdd(&H[bw0 + u0 + u][v[u] & (kSmallE - 1)], 1u);
+  }
+  for (int u = 0; u < NBW; ++u) {
+    const int bl = bw0 + u;
+    if (bl >= nb) break;
+    const int32_t a = s_off[bl];
+    const int64_t len = (int64_t)s_off[bl + 1] - a;
+    for (int64_t c = kWave; c < len; c += 8 * kWave) {
+      int32_t x[8];
 #pragma unroll
-        for (int st = kBagTile / 2; st > 0; st >>= 1) k += s_off[k + st] <= j ? st : 0;
-        atomicAdd(&H[k][v[u] & (kSmallE - 1)], 1u);
+      for (int q = 0; q < 8; ++q) {
+        const int64_t r = c + q * kWave + lane;
+        x[q] = r < len ? indices[a + r] : 0;
       }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (c + q * kWave + lane < len) atomicAdd(&H[bl][x[q] & (kSmallE - 1)], 1u);
     }
   }
   __syncthreads();
 }
 
-// Saturating uint8 counts of the workgroup's 64 bags, written to hist, and
-// the flags: counts[4] when a count exceeds 255, counts[5] when one exceeds
-// 2048. Grid (ceil(B / 64), T); one tile per workgroup keeps many in flight.
+// Saturating uint8 counts of kCountTiles consecutive 64-bag tiles of one
+// table, written to hist, and the flags: counts[4] when a count exceeds 255,
+// counts[5] when one exceeds 2048. Grid (ceil(B / (64 * kCountTiles)), T).
+// The tiles are pipelined: wave w owns bags 16w .. 16w+15 of each tile, and
+// the first 64 lookups of its bags in tile k+1 are loaded (one coalesced
+// load per bag) before it counts tile k with LDS atomics; the thread that
+// packs a count row into hist also clears it for the next tile.
 __global__ __launch_bounds__(kThreads) void small_count_kernel(
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
     uint8_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t B) {
+  constexpr int NBW = kBagTile / kWaves;
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
-  __shared__ int32_t s_off[kBagTile + 1];
+  __shared__ int32_t s_off[kBagTile * kCountTiles + 1];
   __shared__ uint32_t s_wmax[kWaves];
   const int32_t t = blockIdx.y;
-  const int32_t b0 = (int32_t)blockIdx.x * kBagTile;
-  const int nb = B - b0 < kBagTile ? B - b0 : kBagTile;
-  const int64_t bag0 = (int64_t)t * B + b0;
-  count_tile<16>(H, s_off, indices, offsets, bag0, nb);
+  const int32_t wb0 = (int32_t)blockIdx.x * kBagTile * kCountTiles;
+  const int32_t wnb = B - wb0 < kBagTile * kCountTiles ? B - wb0 : kBagTile * kCountTiles;
+  const int64_t wbag0 = (int64_t)t * B + wb0;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  uint4* h4 = reinterpret_cast<uint4*>(&H[0][0]);
+  for (int q = threadIdx.x; q < kBagTile * kHStride / 4; q += kThreads) h4[q] = uint4{0, 0, 0, 0};
+  for (int q = threadIdx.x; q <= wnb; q += kThreads) s_off[q] = offsets[wbag0 + q];
+  __syncthreads();
+
+  int32_t v[NBW];
+  bool ok[NBW];
+  auto load_first = [&](int k) {  // first 64 lookups of this wave's bags in tile k
+#pragma unroll
+    for (int u = 0; u < NBW; ++u) {
+      const int bl = k * kBagTile + wave * NBW + u;
+      const int32_t a = bl < wnb ? s_off[bl] : 0;
+      const int32_t len = bl < wnb ? s_off[bl + 1] - a : 0;
+      ok[u] = lane < len;
+      v[u] = ok[u] ? indices[a + lane] : 0;
+    }
+  };
+  load_first(0);
   uint32_t mx = 0;
-  for (int q = threadIdx.x; q < nb * (kSmallE / 4); q += kThreads) {
-    const int bl = q >> 4, e4 = (q & 15) * 4;
-    const uint4 c = *reinterpret_cast<const uint4*>(&H[bl][e4]);
-    const uint32_t a = c.x > c.y ? c.x : c.y, b = c.z > c.w ? c.z : c.w;
-    mx = mx > (a > b ? a : b) ? mx : (a > b ? a : b);
-    const uint32_t packed = (c.x > 255u ? 255u : c.x) | (c.y > 255u ? 255u : c.y) << 8 |
-                            (c.z > 255u ? 255u : c.z) << 16 | (c.w > 255u ? 255u : c.w) << 24;
-    *reinterpret_cast<uint32_t*>(hist + (bag0 + bl) * kSmallE + e4) = packed;
+  for (int k = 0; k < kCountTiles; ++k) {
+    const int tb0 = k * kBagTile;  // first bag of the tile, within the workgroup's range
+    if (tb0 >= wnb) break;
+    const int nb = wnb - tb0 < kBagTile ? wnb - tb0 : kBagTile;
+    int32_t cv[NBW];
+    bool cok[NBW];
+#pragma unroll
+    for (int u = 0; u < NBW; ++u) {
+      cv[u] = v[u];
+      cok[u] = ok[u];
+    }
+    if (k + 1 < kCountTiles) load_first(k + 1);
+#pragma unroll
+    for (int u = 0; u < NBW; ++u)
+      if (cok[u]) atomicAdd(&H[wave * NBW + u][cv[u] & (kSmallE - 1)], 1u);
+    // lookups past the 64th of each bag, eight loads in flight
+    for (int u = 0; u < NBW; ++u) {
+      const int bl = wave * NBW + u;
+      if (bl >= nb) break;
+      const int32_t a = s_off[tb0 + bl];
+      const int64_t len = (int64_t)s_off[tb0 + bl + 1] - a;
+      for (int64_t c = kWave; c < len; c += 8 * kWave) {
+        int32_t x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int64_t r = c + q * kWave + lane;
+          x[q] = r < len ? indices[a + r] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (c + q * kWave + lane < len) atomicAdd(&H[bl][x[q] & (kSmallE - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    const int64_t bag0 = wbag0 + tb0;
+    for (int q = threadIdx.x; q < nb * (kSmallE / 4); q += kThreads) {
+      const int bl = q >> 4, e4 = (q & 15) * 4;
+      uint4* hp = reinterpret_cast<uint4*>(&H[bl][e4]);
+      const uint4 c = *hp;
+      *hp = uint4{0, 0, 0, 0};
+      const uint32_t a = c.x > c.y ? c.x : c.y, b = c.z > c.w ? c.z : c.w;
+      mx = mx > (a > b ? a : b) ? mx : (a > b ? a : b);
+      const uint32_t packed = (c.x > 255u ? 255u : c.x) | (c.y > 255u ? 255u : c.y) << 8 |
+                              (c.z > 255u ? 255u : c.z) << 16 | (c.w > 255u ? 255u : c.w) << 24;
+      *reinterpret_cast<uint32_t*>(hist + (bag0 + bl) * kSmallE + e4) = packed;
+    }
+    __syncthreads();
   }
   mx = wave_max_u32(mx);
-  if (lane_id() == 0) s_wmax[threadIdx.x / kWave] = mx;
+  if (lane == 0) s_wmax[wave] = mx;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t tmax = 0;
@@ -185,7 +264,7 @@ __device__ __forceinline__ void store_out_blocks(float* __restrict__ ot, int64_t
 // both operands use it, so lane (i, kb) takes e = kb*32 + ks*8 + j, i.e. 32
 // consecutive count bytes, two 16-byte loads per tile. No LDS or barriers in
 // the tile loop; the next tile's counts are loaded before this tile's MFMAs.
-// Grid (ceil(B / (kPoolTiles * 64)), T).
+// Grid ceil(B / (kPoolTiles * 64)) * T, table = block % T.
 __global__ __launch_bounds__(kThreads) void small_pool_kernel(
     const f16_t* __restrict__ W, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ toff,
@@ -193,7 +272,8 @@ __global__ __launch_bounds__(kThreads) void small_pool_kernel(
     int32_t D) {
   __shared__ __align__(16) _Float16 Ws[kSmallE][kWStride];
   if (counts[4] != 0) return;
-  const int32_t t = blockIdx.y;
+  const int32_t t = blockIdx.x % T;   // tables vary fastest: the resident
+  const int32_t bx = blockIdx.x / T;  // workgroups write whole output rows
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int i = lane & 31, kb = lane >> 5;
@@ -203,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void small_pool_kernel(
                   [](int ks, int kb_, int j) { return kb_ * 32 + ks * 8 + j; });
   float* ot = out + (int64_t)t * D;
   const int64_t ostride = (int64_t)T * D;
-  const int32_t tb0 = (int32_t)blockIdx.x * kPoolTiles * kBagTile;
+  const int32_t tb0 = bx * kPoolTiles * kBagTile;
   auto load_counts = [&](int32_t b0, uint4& h0, uint4& h1) {
     const int32_t b = b0 + mt * 32 + i;
     h0 = h1 = uint4{0, 0, 0, 0};
@@ -319,9 +399,8 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
 // One workgroup per (table, split of the batch): partial G = H^T . grad over
 // the split's bags, written to partials[(t*splits + s)][64][D], and the
 // split's per-row counts to part_counts[(t*splits + s)][64]. Wave w owns the
-// 32 columns w*32.. and both 32-row halves of G; each lane keeps the next
-// tile's gradient values in registers while the current tile is contracted.
-// Runs only when every count is exact in f16 (counts[5] clear).
+// 32 columns w*32.. and both 32-row halves of G. Runs only when every count
+// is exact in f16 (counts[5] clear).
 __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     const float* __restrict__ grad, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
@@ -381,7 +460,6 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
         }
     }
   };
-  if (sb0 < sb1) load_grad(sb0);
 
   typedef _Float16 half2v __attribute__((ext_vector_type(2)));
   const half2v ones = {(_Float16)1.f, (_Float16)1.f};
@@ -390,7 +468,8 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
     const int64_t bag0 = (int64_t)t * B + b0;
     // B operands: this tile's gradients split into hi = f16(g) and
-    // lo = f16((g - hi) * 2^11); then the next tile's loads go out.
+    // lo = f16((g - hi) * 2^11).
+    load_grad(b0);
     half8 hi[kBagTile / 16], lo[kBagTile / 16];
 #pragma unroll
     for (int ks = 0; ks < kBagTile / 16; ++ks)
@@ -401,7 +480,6 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
         hi[ks][j] = h;
         lo[ks][j] = (_Float16)((g - (float)h) * 2048.f);
       }
-    if (b0 + kBagTile < sb1) load_grad(b0 + kBagTile);
 
     if (recount) count_tile(H, s_off, indices, offsets, bag0, nb);
     else __syncthreads();  // earlier readers of HT are done
@@ -573,12 +651,13 @@ hipError_t launch_small_forward(const Problem& p, const void* W, const int32_t* 
   if (err != hipSuccess || p.B == 0) return err;
   const int32_t* toff = tinfo;
   const int32_t* trows = tinfo + p.T;
-  hipLaunchKernelGGL(small_count_kernel, dim3((unsigned)((p.B + kBagTile - 1) / kBagTile), (unsigned)p.T),
+  const int64_t count_bags = (int64_t)kBagTile * kCountTiles;
+  hipLaunchKernelGGL(small_count_kernel, dim3((unsigned)((p.B + count_bags - 1) / count_bags), (unsigned)p.T),
                      dim3(kThreads), 0, s, indices, offsets, hist, counts, p.B);
   if ((err = hipGetLastError()) != hipSuccess || !out) return err;
   // Exactly one of the two computes the output, chosen on the device by counts[4].
   const int64_t pool_bags = (int64_t)kBagTile * kPoolTiles;
-  hipLaunchKernelGGL(small_pool_kernel, dim3((unsigned)((p.B + pool_bags - 1) / pool_bags), (unsigned)p.T),
+  hipLaunchKernelGGL(small_pool_kernel, dim3((unsigned)((p.B + pool_bags - 1) / pool_bags * p.T)),
                      dim3(kThreads), 0, s, (const f16_t*)W, hist, counts, toff, trows, out, p.T,
                      p.B, p.D);
   const int64_t re_bags = (int64_t)kBagTile * kFwdTiles;

@@ -182,6 +182,13 @@ typedef enum {
 const char* tbe_status_str(tbe_status s);
 
 /*
+ * After a call returned TBE_ERR_HIP: the HIP error and the step that failed,
+ * as text owned by the library (per calling thread, valid until that
+ * thread's next failing call; empty before any).
+ */
+const char* tbe_last_error(void);
+
+/*
  * Which path a call with this description, lookup count and weighting takes:
  * TBE_PATH_SMALL_TABLE when every table has E_t <= 64, 64 <= D <= 128, the
  * average bag length N/(T*B) >= 64, wdtype is f16, the problem is unweighted
