@@ -35,7 +35,7 @@ TBE_PATH_GENERIC, TBE_PATH_SMALL_TABLE = 0, 1
 (TBE_OP_FORWARD, TBE_OP_FORWARD_PREPROCESS, TBE_OP_PREPROCESS, TBE_OP_BACKWARD,
  TBE_OP_BACKWARD_SELF) = range(5)
 STAGES = ["fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "bwd_long", "bwd_apply",
-          "small_fwd", "small_bwd", "small_apply", "validate"]
+          "small_fwd", "small_bwd", "small_apply", "validate", "long_schedule", "small_count"]
 TBE_NUM_STAGES = len(STAGES)
 META_FIELDS = ["counts", "run_keys", "run_offsets", "sorted_pos", "sorted_bag", "sorted_psw",
                "short_runs", "long_runs", "long_chunk_begin", "chunk_run", "chunk_start", "hist"]

@@ -364,9 +364,12 @@ tbe_status tbe_forward(const tbe_desc* desc, const void* W, const int32_t* indic
   const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
   if (p.path == TBE_PATH_SMALL_TABLE) {
     int32_t* counts = meta ? meta->counts : at<int32_t>(ws, L.flags) + 8;
-    timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
     uint8_t* hist = meta ? meta->hist : at<uint8_t>(ws, L.hist);
-    TBE_TRY_HIP(launch_small_forward(p, W, indices, offsets, tinfo, out, hist, counts, s));
+    timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+    TBE_TRY_HIP(launch_small_count(p, indices, offsets, hist, counts, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    TBE_TRY_HIP(launch_small_pool(p, W, indices, offsets, tinfo, out, hist, counts, s));
     timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
     return TBE_OK;
   }
@@ -391,10 +394,9 @@ tbe_status tbe_preprocess(const tbe_desc* desc, const int32_t* indices, const in
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
   if (p.path == TBE_PATH_SMALL_TABLE) {
-    timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
-    TBE_TRY_HIP(launch_small_forward(p, nullptr, indices, offsets, at<int32_t>(ws, L.tinfo), nullptr,
-                                     meta->hist, meta->counts, s));
-    timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+    TBE_TRY_HIP(launch_small_count(p, indices, offsets, meta->hist, meta->counts, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
     return TBE_OK;
   }
   return run_preprocess(desc, p, indices, offsets, psw, *meta, ws, L, s);
@@ -423,10 +425,9 @@ tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
 
   if (p.path == TBE_PATH_SMALL_TABLE) {
     if (!meta) {
-      timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
-      TBE_TRY_HIP(launch_small_forward(p, nullptr, indices, offsets, tinfo, nullptr, m.hist,
-                                       m.counts, s));
-      timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
+      timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+      TBE_TRY_HIP(launch_small_count(p, indices, offsets, m.hist, m.counts, s));
+      timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
     }
     float* parts = at<float>(ws, L.partials);
     int32_t* pcounts = at<int32_t>(ws, L.part_counts);
@@ -447,6 +448,9 @@ tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
   timer_begin(desc->timer, TBE_STAGE_BWD_SHORT, s);
   TBE_TRY_HIP(launch_bwd_short(p, W, momentum, grad_out, m, tinfo, lr, eps, s));
   timer_end(desc->timer, TBE_STAGE_BWD_SHORT, s);
+  timer_begin(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
+  TBE_TRY_HIP(launch_long_schedule(p, m, at<int32_t>(ws, L.sched), s));
+  timer_end(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
   timer_begin(desc->timer, TBE_STAGE_BWD_LONG, s);
   TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, at<int32_t>(ws, L.sched), s));
   timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);

@@ -413,21 +413,9 @@ hipError_t short_typed(const Problem& p, const RowShape& rs, void* W, float* m, 
 
 template <typename ACC, int V, int PMAX>
 hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, const tbe_meta& meta,
-                      void* partials, int32_t* sched, hipStream_t s) {
-  int shift = 0;
-  while (((int64_t)(p.B - 1) >> shift) >= kSchedBuckets) ++shift;
-  int32_t* order = sched;
-  int32_t* bucket_of = order + p.cap_chunks;
-  int32_t* hist = bucket_of + p.cap_chunks;
-  int32_t* list_begin = hist + kXcds * kSchedBuckets;
-  hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, hist, kXcds * kSchedBuckets);
-  hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
-                     meta.sorted_bag, p.B, p.T, shift, hist, bucket_of);
-  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, hist, list_begin);
-  hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, bucket_of,
-                     hist, order);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+                      void* partials, const int32_t* sched, hipStream_t s) {
+  const int32_t* order = sched;
+  const int32_t* list_begin = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets;
   const int64_t blocks = (persistent_blocks(p.cap_chunks) + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)blocks);
   if (p.weighted)
@@ -500,7 +488,7 @@ hipError_t short_for(const Problem& p, void* W, float* m, const float* grad, con
 
 template <typename ACC>
 hipError_t long_for(const Problem& p, const float* grad, const tbe_meta& meta, void* partials,
-                    int32_t* sched, hipStream_t s) {
+                    const int32_t* sched, hipStream_t s) {
   const RowShape rs = grad_row_shape(p.D);
 #define CALL(VV, PP) long_typed<ACC, VV, PP>(p, rs, grad, meta, partials, sched, s)
   TBE_DISPATCH_V(rs, CALL);
@@ -531,8 +519,26 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t* sched,
+                                hipStream_t s) {
+  if (p.cap_chunks == 0) return hipSuccess;
+  int shift = 0;
+  while (((int64_t)(p.B - 1) >> shift) >= kSchedBuckets) ++shift;
+  int32_t* order = sched;
+  int32_t* bucket_of = order + p.cap_chunks;
+  int32_t* hist = bucket_of + p.cap_chunks;
+  int32_t* list_begin = hist + kXcds * kSchedBuckets;
+  hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, hist, kXcds * kSchedBuckets);
+  hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
+                     meta.sorted_bag, p.B, p.T, shift, hist, bucket_of);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, hist, list_begin);
+  hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, bucket_of,
+                     hist, order);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
-                           void* partials, int32_t* sched, hipStream_t s) {
+                           void* partials, const int32_t* sched, hipStream_t s) {
   if (p.cap_chunks == 0) return hipSuccess;
   if (p.wdtype == TBE_F32) return long_for<double>(p, grad, meta, partials, sched, s);
   return long_for<float>(p, grad, meta, partials, sched, s);

@@ -113,15 +113,19 @@ hipError_t launch_rle_route(const Problem& p, const int32_t* sorted_keys, int32_
 hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* grad,
                             const tbe_meta& meta, const int32_t* tinfo, double lr, double eps,
                             hipStream_t s);
+hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t* sched,
+                                hipStream_t s);
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
-                           void* partials, int32_t* sched, hipStream_t s);
+                           void* partials, const int32_t* sched, hipStream_t s);
 size_t long_schedule_ints(const Problem& p);  // workspace ints of the chunk schedule
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
                             const void* partials, double lr, double eps, hipStream_t s);
 
-hipError_t launch_small_forward(const Problem& p, const void* W, const int32_t* indices,
-                                const int32_t* offsets, const int32_t* tinfo, float* out,
-                                uint8_t* hist, int32_t* counts, hipStream_t s);
+hipError_t launch_small_count(const Problem& p, const int32_t* indices, const int32_t* offsets,
+                              uint8_t* hist, int32_t* counts, hipStream_t s);
+hipError_t launch_small_pool(const Problem& p, const void* W, const int32_t* indices,
+                             const int32_t* offsets, const int32_t* tinfo, float* out,
+                             const uint8_t* hist, const int32_t* counts, hipStream_t s);
 hipError_t launch_small_backward(const Problem& p, const float* grad, const uint8_t* hist,
                                  const int32_t* counts, const int32_t* indices,
                                  const int32_t* offsets, float* partials, int32_t* part_counts,

@@ -643,18 +643,24 @@ int small_splits_for(int32_t T, int32_t B) {
   return (int)(per_table < max_splits ? per_table : max_splits);
 }
 
-hipError_t launch_small_forward(const Problem& p, const void* W, const int32_t* indices,
-                                const int32_t* offsets, const int32_t* tinfo, float* out,
-                                uint8_t* hist, int32_t* counts, hipStream_t s) {
+hipError_t launch_small_count(const Problem& p, const int32_t* indices, const int32_t* offsets,
+                              uint8_t* hist, int32_t* counts, hipStream_t s) {
   hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, s, counts);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.B == 0) return err;
+  if (p.B > 0) {
+    const int64_t count_bags = (int64_t)kBagTile * kCountTiles;
+    hipLaunchKernelGGL(small_count_kernel,
+                       dim3((unsigned)((p.B + count_bags - 1) / count_bags), (unsigned)p.T),
+                       dim3(kThreads), 0, s, indices, offsets, hist, counts, p.B);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_small_pool(const Problem& p, const void* W, const int32_t* indices,
+                             const int32_t* offsets, const int32_t* tinfo, float* out,
+                             const uint8_t* hist, const int32_t* counts, hipStream_t s) {
+  if (p.B == 0) return hipSuccess;
   const int32_t* toff = tinfo;
   const int32_t* trows = tinfo + p.T;
-  const int64_t count_bags = (int64_t)kBagTile * kCountTiles;
-  hipLaunchKernelGGL(small_count_kernel, dim3((unsigned)((p.B + count_bags - 1) / count_bags), (unsigned)p.T),
-                     dim3(kThreads), 0, s, indices, offsets, hist, counts, p.B);
-  if ((err = hipGetLastError()) != hipSuccess || !out) return err;
   // Exactly one of the two computes the output, chosen on the device by counts[4].
   const int64_t pool_bags = (int64_t)kBagTile * kPoolTiles;
   hipLaunchKernelGGL(small_pool_kernel, dim3((unsigned)((p.B + pool_bags - 1) / pool_bags * p.T)),

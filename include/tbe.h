@@ -89,11 +89,13 @@ typedef enum {
     TBE_STAGE_BWD_SHORT = 4,    /* short runs: accumulate + Adagrad + store   */
     TBE_STAGE_BWD_LONG = 5,     /* long-run chunks: partial sums to workspace */
     TBE_STAGE_BWD_APPLY = 6,    /* long runs: reduce partials + Adagrad       */
-    TBE_STAGE_SMALL_FWD = 7,    /* small-table histogram + contraction        */
+    TBE_STAGE_SMALL_FWD = 7,    /* small-table contraction (forward output)   */
     TBE_STAGE_SMALL_BWD = 8,    /* small-table transposed contraction         */
     TBE_STAGE_SMALL_APPLY = 9,  /* small-table reduce + Adagrad               */
     TBE_STAGE_VALIDATE = 10,    /* TBE_FLAG_VALIDATE check                    */
-    TBE_NUM_STAGES = 11
+    TBE_STAGE_LONG_SCHEDULE = 11, /* per-XCD order of the long-run chunks     */
+    TBE_STAGE_SMALL_COUNT = 12, /* small-table per-bag row counts             */
+    TBE_NUM_STAGES = 13
 } tbe_stage;
 
 typedef struct tbe_timer tbe_timer;   /* opaque; see tbe_timer_create */

@@ -233,6 +233,8 @@ def test_stage_timer_counts_each_stage():
     tbe.tbe_backward_adagrad(desc, W, m, dev["grad"], dev["indices"], dev["offsets"], None, meta,
                              0.01, 1e-8, wsb)
     t = timer.read()
-    for st in ("fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "bwd_long", "bwd_apply"):
+    for st in ("fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "long_schedule",
+               "bwd_long", "bwd_apply"):
         assert t[st][1] == 1 and t[st][0] > 0, st
-    assert t["small_fwd"][1] == 0
+    for st in ("small_count", "small_fwd", "small_bwd", "small_apply", "validate"):
+        assert t[st][1] == 0, st
