@@ -32,6 +32,7 @@
 //   so concurrent chunks on one XCD read gradient rows of nearby bags, which
 //   its L2 keeps. Each chunk still writes its own partial, so the result does
 //   not depend on the schedule.
+#include <algorithm>
 #include "adagrad.h"
 #include "device.h"
 #include "internal.h"
@@ -416,7 +417,14 @@ hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, c
                       void* partials, const int32_t* sched, hipStream_t s) {
   const int32_t* order = sched;
   const int32_t* list_begin = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets;
-  const int64_t blocks = (persistent_blocks(p.cap_chunks) + kXcds - 1) / kXcds * kXcds;
+  // Two workgroups (eight waves) per CU. More chunks in flight widen the
+  // window of bags whose gradient rows the XCD's L2 must hold at once: with
+  // T=32, E=2M, D=128, B=131072 and Zipf-Mandelbrot rows (287,766 chunks),
+  // 1, 2, 3, 4 and 8 workgroups per CU took 4.87, 3.21, 3.43, 3.80 and
+  // 4.01 ms on one MI355X.
+  const int64_t per_xcd = 2 * std::max(1, device_cu_count() / kXcds);
+  int64_t blocks = (persistent_blocks(p.cap_chunks) + kXcds - 1) / kXcds * kXcds;
+  if (blocks > per_xcd * kXcds) blocks = per_xcd * kXcds;
   const dim3 grid((unsigned)blocks);
   if (p.weighted)
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, true>), grid, dim3(kThreads), 0, s, grad,

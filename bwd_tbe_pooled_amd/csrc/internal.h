@@ -84,6 +84,9 @@ void timer_begin(tbe_timer* t, int stage, hipStream_t s);
 void timer_end(tbe_timer* t, int stage, hipStream_t s);
 
 // --- launchers (return hipSuccess or the first launch error) ----------------
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 hipError_t launch_fill_tinfo(const Problem& p, const int64_t* rows_host, int32_t* tinfo,
                              hipStream_t s);
 hipError_t launch_validate(const Problem& p, const int32_t* indices, const int32_t* offsets,

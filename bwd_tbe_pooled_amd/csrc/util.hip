@@ -2,6 +2,7 @@
 // memory copy, so callers may free their host array right after the call),
 // and the opt-in validation of offsets and index ranges (page 1, checklist
 // item 5 makes the bounds check optional and off by default).
+#include <atomic>
 #include <algorithm>
 
 #include "device.h"
@@ -20,6 +21,19 @@ __global__ void fill_tinfo_kernel2(int32_t* tinfo, int32_t T, int32_t t0, int32_
     tinfo[t0 + i] = c.toff[i];
     tinfo[T + t0 + i] = c.rows[i];
   }
+}
+
+int device_cu_count() {
+  // Cached per device: the attribute query is a host call, made once.
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 hipError_t launch_fill_tinfo(const Problem& p, const int64_t* rows_host, int32_t* tinfo,
