@@ -34,6 +34,7 @@
 //   not depend on the schedule.
 #include <algorithm>
 #include "adagrad.h"
+#include "block_scan.h"
 #include "device.h"
 #include "internal.h"
 
@@ -346,31 +347,11 @@ __global__ __launch_bounds__(256) void sched_count_kernel(
 __global__ __launch_bounds__(1024) void sched_scan_kernel(int32_t* __restrict__ hist,
                                                           int32_t* __restrict__ list_begin) {
   __shared__ int32_t wsum[16];
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  constexpr int n = kXcds * kSchedBuckets;
-  int32_t carry = 0;
-  for (int base = 0; base < n; base += 1024) {
-    const int i = base + threadIdx.x;
-    const int32_t v = hist[i];
-    int32_t inc = v;
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int32_t y = __shfl_up(inc, d);
-      if (lane >= d) inc += y;
-    }
-    if (lane == kWave - 1) wsum[wave] = inc;
-    __syncthreads();
-    int32_t pre = 0, tot = 0;
-    for (int w = 0; w < 16; ++w) {
-      if (w < wave) pre += wsum[w];
-      tot += wsum[w];
-    }
-    const int32_t ex = carry + pre + inc - v;
-    hist[i] = ex;
-    if (i % kSchedBuckets == 0) list_begin[i / kSchedBuckets] = ex;
-    carry += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) list_begin[kXcds] = carry;
+  const int32_t tot = block1024_scan_inplace(
+      hist, (int64_t)kXcds * kSchedBuckets, wsum, [&](int64_t i, int32_t prefix) {
+        if (i % kSchedBuckets == 0) list_begin[i / kSchedBuckets] = prefix;
+      });
+  if (threadIdx.x == 0) list_begin[kXcds] = tot;
 }
 
 __global__ __launch_bounds__(256) void sched_scatter_kernel(const int32_t* __restrict__ counts,

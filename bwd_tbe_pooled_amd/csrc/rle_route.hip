@@ -67,28 +67,10 @@ __global__ __launch_bounds__(kThreads) void rle_count_kernel(const int32_t* __re
 __global__ __launch_bounds__(1024) void scan_tiles_kernel(int32_t* __restrict__ vals, int64_t n,
                                                           int ncols, int32_t* __restrict__ totals) {
   __shared__ int32_t wsum[16];
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
   for (int c = 0; c < ncols; ++c) {
-    int32_t* v = vals + (int64_t)c * n;
-    int32_t carry = 0;
-    for (int64_t base = 0; base < n; base += 1024) {
-      const int64_t i = base + threadIdx.x;
-      const int32_t x = i < n ? v[i] : 0;
-      const int32_t inc = wave_inclusive_scan(x);
-      if (lane == kWave - 1) wsum[wave] = inc;
-      __syncthreads();
-      int32_t pre = 0, tot = 0;
-      for (int w = 0; w < 16; ++w) {
-        const int32_t s = wsum[w];
-        if (w < wave) pre += s;
-        tot += s;
-      }
-      if (i < n) v[i] = carry + pre + inc - x;
-      carry += tot;
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) totals[c] = carry;
+    const int32_t tot =
+        block1024_scan_inplace(vals + (int64_t)c * n, n, wsum, [](int64_t, int32_t) {});
+    if (threadIdx.x == 0) totals[c] = tot;
   }
 }
 
