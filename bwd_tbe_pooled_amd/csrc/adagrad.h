@@ -9,7 +9,8 @@
 namespace tbe {
 
 // One row held by the G lanes of a slot (every lane of
-// the slot holds its V*PMAX elements of g). Plain stores.
+// the slot holds its V*PMAX elements of g). The updated row and state are
+// written once per step, so they are streamed past L2.
 template <typename WT, typename ACC, int V, int PMAX>
 __device__ __forceinline__ void adagrad_row(WT* __restrict__ wrow, float* __restrict__ mrow,
                                             ACC (&g)[PMAX][V], int col, int G, int P, int D,
@@ -34,10 +35,10 @@ __device__ __forceinline__ void adagrad_row(WT* __restrict__ wrow, float* __rest
       WT* o = reinterpret_cast<WT*>(&outv);
 #pragma unroll
       for (int v = 0; v < V; ++v) store_w(&o[v], w[v] - g[p][v] * scale);
-      *reinterpret_cast<RAW*>(wrow + e) = outv;
+      store_stream(reinterpret_cast<RAW*>(wrow + e), outv);
     }
   }
-  if (col == 0) *mrow = (float)m1;
+  if (col == 0) store_stream(mrow, (float)m1);
 }
 
 // The same step split in two, so that the row's weights and state can be
@@ -85,10 +86,10 @@ __device__ __forceinline__ void apply_row_state(WT* __restrict__ wrow, float* __
       WT* o = reinterpret_cast<WT*>(&outv);
 #pragma unroll
       for (int v = 0; v < V; ++v) store_w(&o[v], w[v] - g[p][v] * scale);
-      *reinterpret_cast<RAW*>(wrow + e) = outv;
+      store_stream(reinterpret_cast<RAW*>(wrow + e), outv);
     }
   }
-  if (col == 0) *mrow = (float)m1;
+  if (col == 0) store_stream(mrow, (float)m1);
 }
 
 }  // namespace tbe

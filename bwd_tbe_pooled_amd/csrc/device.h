@@ -68,6 +68,29 @@ struct raw_vec {
   using type = typename vec_bytes<V * (int)sizeof(T)>::type;
 };
 
+// Nontemporal store for data written once and not read again by the same
+// kernel (pooled outputs, updated rows): it leaves the L2 to the rows that
+// are re-read.
+template <typename R>
+__device__ __forceinline__ void store_stream(R* p, const R& v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (sizeof(R) == 32) {
+    const u32x4* s = reinterpret_cast<const u32x4*>(&v);
+    __builtin_nontemporal_store(s[0], reinterpret_cast<u32x4*>(p));
+    __builtin_nontemporal_store(s[1], reinterpret_cast<u32x4*>(p) + 1);
+  } else if constexpr (sizeof(R) == 16) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+  } else if constexpr (sizeof(R) == 8) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2*>(p));
+  } else if constexpr (sizeof(R) == 4) {
+    __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, v), reinterpret_cast<uint32_t*>(p));
+  } else {
+    static_assert(sizeof(R) == 2, "store_stream: 2, 4, 8, 16 or 32 bytes");
+    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, v), reinterpret_cast<uint16_t*>(p));
+  }
+}
+
 // Plain (cached) load: weight rows and gradient rows are both re-read many
 // times per batch (hot rows, and every lookup of a bag), so they go through L2.
 template <typename T, int V>

@@ -118,8 +118,12 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
   for (int p = 0; p < PMAX; ++p) {
     const int e = (p * G + col) * V;
     if (p < P && e < D) {
+      // written once: streamed past L2, which keeps the hot rows instead
+      typename vec_bytes<V * 4>::type ov;
+      float* of = reinterpret_cast<float*>(&ov);
 #pragma unroll
-      for (int v = 0; v < V; ++v) o[e + v] = (float)acc[p][v];
+      for (int v = 0; v < V; ++v) of[v] = (float)acc[p][v];
+      store_stream(reinterpret_cast<decltype(ov)*>(o + e), ov);
     }
   }
 }

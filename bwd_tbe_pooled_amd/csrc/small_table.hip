@@ -252,7 +252,7 @@ __device__ __forceinline__ void store_out_blocks(float* __restrict__ ot, int64_t
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int bl = mt * 32 + 8 * (r / 4) + 4 * kb + (r % 4);
-      if (bl < nb) ot[(int64_t)(b0 + bl) * ostride + d] = acc[q][r];
+      if (bl < nb) store_stream(&ot[(int64_t)(b0 + bl) * ostride + d], acc[q][r]);
     }
   }
 }
