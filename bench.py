@@ -329,7 +329,7 @@ def main_small(args, torch, tbe):
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        cpu = cpu_baseline(cfg, batch, W0, min(args.cpu_sample_bags // 4, cfg.B))
+        cpu = cpu_baseline(cfg, batch, W0, min(args.cpu_sample_bags // 8, cfg.B))
     result = {
         "metric": "TBE small-table path fwd+bwd(Adagrad) ms and achieved HBM GB/s % peak, "
                   "T=64 E=64 B=32K D=128",
