@@ -152,6 +152,9 @@ def main():
     ap.add_argument("--workload", choices=["large", "small"], default="large",
                     help="large: T=32 E=2M D=128 bf16 B=131072 (the headline); "
                          "small: the small-table histogram path, T=64 E=64 D=128 f16 B=32768 L=64")
+    ap.add_argument("--check", choices=["none", "fused", "validate"], default="none",
+                    help="index checking: none (default), fused into the kernels "
+                         "(TBE_FLAG_CHECK), or the separate synchronous pass (TBE_FLAG_VALIDATE)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -184,7 +187,9 @@ def main():
     m = init_state(cfg, dev)
     out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device=dev)
     timer = tbe.Timer(capacity=args.steps + 1)
-    desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    flags = {"none": 0, "fused": tbe.TBE_FLAG_CHECK, "validate": tbe.TBE_FLAG_VALIDATE}[args.check]
+    desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, flags=flags, error_flags=err)
     meta = tbe.Meta(desc, N, True, with_pos=False)   # the backward needs no positions
     ws_f = tbe.workspace(desc, N, True, tbe.TBE_OP_FORWARD_PREPROCESS)
     ws_b = tbe.workspace(desc, N, True, tbe.TBE_OP_BACKWARD)
@@ -251,7 +256,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "T=32 E=2M D=128 bf16 B=131072 Poisson(20) Zipf-Mandelbrot weighted, "
-                               "preprocessing in forward",
+                               "preprocessing in forward"
+                               + ("" if args.check == "none" else f", index check: {args.check}"),
                    "T": cfg.T, "E": cfg.rows[0], "D": cfg.D, "B": cfg.B, "N": N, "U": U,
                    "long_runs": n_long, "chunks": n_chunks, "long_lookups": long_lookups,
                    "parallelism": "single GPU"},

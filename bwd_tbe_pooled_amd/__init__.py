@@ -30,7 +30,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 # --- C types ----------------------------------------------------------------
 TBE_OK, TBE_ERR_ARG, TBE_ERR_UNSUPPORTED, TBE_ERR_WORKSPACE, TBE_ERR_INDEX_RANGE, TBE_ERR_HIP = range(6)
 TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
-TBE_FLAG_VALIDATE, TBE_FLAG_FORCE_GENERIC = 0x1, 0x2
+TBE_FLAG_VALIDATE, TBE_FLAG_FORCE_GENERIC, TBE_FLAG_CHECK = 0x1, 0x2, 0x4
+TBE_ERROR_INDEX = 0x1
 TBE_PATH_GENERIC, TBE_PATH_SMALL_TABLE = 0, 1
 (TBE_OP_FORWARD, TBE_OP_FORWARD_PREPROCESS, TBE_OP_PREPROCESS, TBE_OP_BACKWARD,
  TBE_OP_BACKWARD_SELF) = range(5)
@@ -47,7 +48,8 @@ class tbe_desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("D", ctypes.c_int32), ("B", ctypes.c_int32),
                 ("rows", ctypes.POINTER(ctypes.c_int64)), ("wdtype", ctypes.c_int),
                 ("short_max", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("timer", ctypes.c_void_p)]
+                ("flags", ctypes.c_uint32), ("timer", ctypes.c_void_p),
+                ("error_flags", ctypes.c_void_p)]
 
 
 class tbe_meta(ctypes.Structure):
@@ -112,12 +114,15 @@ class Desc:
     """Owns a tbe_desc and the host rows array it points to."""
 
     def __init__(self, T: int, D: int, B: int, rows: Sequence[int], dtype: str,
-                 short_max: int = 0, chunk: int = 0, flags: int = 0, timer: "Timer" = None):
+                 short_max: int = 0, chunk: int = 0, flags: int = 0, timer: "Timer" = None,
+                 error_flags=None):
         self._rows = (ctypes.c_int64 * len(rows))(*[int(r) for r in rows])
         self.c = tbe_desc(T=int(T), D=int(D), B=int(B),
                           rows=ctypes.cast(self._rows, ctypes.POINTER(ctypes.c_int64)),
                           wdtype=DTYPE_CODES[dtype], short_max=int(short_max), chunk=int(chunk),
-                          flags=int(flags), timer=timer.handle if timer else None)
+                          flags=int(flags), timer=timer.handle if timer else None,
+                          error_flags=_ptr(error_flags))
+        self._error_flags = error_flags  # keeps the device word alive
         self.T, self.D, self.B, self.dtype = int(T), int(D), int(B), dtype
         self.rows = [int(r) for r in rows]
 

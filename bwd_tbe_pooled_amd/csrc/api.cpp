@@ -44,7 +44,8 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   if (!d || !p || !d->rows) return TBE_ERR_ARG;
   if (d->T < 1 || d->D < 1 || d->B < 0 || N < 0) return TBE_ERR_ARG;
   if (d->wdtype != TBE_F32 && d->wdtype != TBE_F16 && d->wdtype != TBE_BF16) return TBE_ERR_UNSUPPORTED;
-  if (d->flags & ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC)) return TBE_ERR_ARG;
+  if (d->flags & ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC | TBE_FLAG_CHECK)) return TBE_ERR_ARG;
+  if ((d->flags & TBE_FLAG_CHECK) && !d->error_flags) return TBE_ERR_ARG;
   if (d->short_max < 0 || d->chunk < 0) return TBE_ERR_ARG;
   int64_t sum = 0, mx = 0;
   for (int32_t t = 0; t < d->T; ++t) {
@@ -79,6 +80,7 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   p->cap_long = N / p->S;
   p->cap_chunks = p->cap_long ? N / p->C + p->cap_long : 0;
   p->small_splits = small_splits_for(d->T, d->B);
+  p->err = (d->flags & TBE_FLAG_CHECK) ? d->error_flags : nullptr;
   return TBE_OK;
 }
 
@@ -366,7 +368,7 @@ tbe_status tbe_forward(const tbe_desc* desc, const void* W, const int32_t* indic
     int32_t* counts = meta ? meta->counts : at<int32_t>(ws, L.flags) + 8;
     uint8_t* hist = meta ? meta->hist : at<uint8_t>(ws, L.hist);
     timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
-    TBE_TRY_HIP(launch_small_count(p, indices, offsets, hist, counts, s));
+    TBE_TRY_HIP(launch_small_count(p, indices, offsets, tinfo, hist, counts, s));
     timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
     timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
     TBE_TRY_HIP(launch_small_pool(p, W, indices, offsets, tinfo, out, hist, counts, s));
@@ -395,7 +397,8 @@ tbe_status tbe_preprocess(const tbe_desc* desc, const int32_t* indices, const in
   if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
   if (p.path == TBE_PATH_SMALL_TABLE) {
     timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
-    TBE_TRY_HIP(launch_small_count(p, indices, offsets, meta->hist, meta->counts, s));
+    TBE_TRY_HIP(launch_small_count(p, indices, offsets, at<int32_t>(ws, L.tinfo), meta->hist,
+                                   meta->counts, s));
     timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
     return TBE_OK;
   }
@@ -426,14 +429,14 @@ tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
   if (p.path == TBE_PATH_SMALL_TABLE) {
     if (!meta) {
       timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
-      TBE_TRY_HIP(launch_small_count(p, indices, offsets, m.hist, m.counts, s));
+      TBE_TRY_HIP(launch_small_count(p, indices, offsets, tinfo, m.hist, m.counts, s));
       timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
     }
     float* parts = at<float>(ws, L.partials);
     int32_t* pcounts = at<int32_t>(ws, L.part_counts);
     timer_begin(desc->timer, TBE_STAGE_SMALL_BWD, s);
     TBE_TRY_HIP(launch_small_backward(p, grad_out, m.hist, m.counts, indices, offsets, parts,
-                                      pcounts, s));
+                                      pcounts, tinfo, s));
     timer_end(desc->timer, TBE_STAGE_SMALL_BWD, s);
     timer_begin(desc->timer, TBE_STAGE_SMALL_APPLY, s);
     TBE_TRY_HIP(launch_small_apply(p, W, momentum, tinfo, parts, pcounts, lr, eps, s));

@@ -30,12 +30,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename WT, int V, int PMAX, bool WEIGHTED>
+// CHECK: the bounds check fused into the gather (an index outside its table
+// is read as row 0 and sets TBE_ERROR_INDEX in *err).
+template <typename WT, int V, int PMAX, bool WEIGHTED, bool CHECK>
 __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
     const WT* __restrict__ W, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, const float* __restrict__ psw,
     const int32_t* __restrict__ toff, float* __restrict__ out, int32_t T, int32_t B, int32_t D,
-    int32_t G, int32_t log2G, int32_t P, int64_t nbags, int64_t nblocks) {
+    int32_t G, int32_t log2G, int32_t P, int64_t nbags, int64_t nblocks, int32_t* __restrict__ err) {
   using ACC = typename acc_of<WT>::type;
   using RAW = typename raw_vec<WT, V>::type;
   constexpr int UNROLL = PMAX == 1 ? 4 : 1;
@@ -62,6 +64,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
   const int32_t t = has_bag ? (int32_t)(my_bag / B) : 0;
   const int32_t b = has_bag ? (int32_t)(my_bag - (int64_t)t * B) : 0;
   const WT* __restrict__ Wt = W + (int64_t)(has_bag ? toff[t] : 0) * D;
+  const uint32_t Et = CHECK ? (uint32_t)(has_bag ? toff[T + t] : 1) : 0u;  // tinfo rows follow
+  bool bad = false;
 
   ACC acc[PMAX][V];
 #pragma unroll
@@ -87,7 +91,12 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
         const int32_t jj = j + u;
         const bool ok = jj < hi;
         const int32_t li = ok ? jj - w0 : 0;
-        const int32_t idx = s_idx[wave][li];
+        int32_t idx = s_idx[wave][li];
+        if constexpr (CHECK) {
+          const bool out = ok && (uint32_t)idx >= Et;
+          bad |= out;
+          idx = out ? 0 : idx;
+        }
         if constexpr (WEIGHTED) sc[u] = ok ? s_w[wave][li] : 0.f;
         else sc[u] = ok ? 1.f : 0.f;
         const WT* row = Wt + (int64_t)idx * D;
@@ -112,6 +121,9 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
     }
   }
 
+  if constexpr (CHECK) {
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
+  }
   if (!has_bag) return;
   float* o = out + (int64_t)b * T * D + (int64_t)t * D;
 #pragma unroll
@@ -137,14 +149,18 @@ hipError_t launch_typed(const Problem& p, const RowShape& rs, const void* W, con
   const int64_t nblocks = (p.nbags + bags_per_block - 1) / bags_per_block;
   if (nblocks == 0) return hipSuccess;
   const dim3 grid((unsigned)xcd_grid(nblocks));
-  if (psw)
-    hipLaunchKernelGGL((fwd_pool_kernel<WT, V, PMAX, true>), grid, dim3(kFwdThreads), 0, s,
-                       (const WT*)W, indices, offsets, psw, toff, out, p.T, p.B, p.D, rs.G,
-                       rs.log2G, rs.P, p.nbags, nblocks);
-  else
-    hipLaunchKernelGGL((fwd_pool_kernel<WT, V, PMAX, false>), grid, dim3(kFwdThreads), 0, s,
-                       (const WT*)W, indices, offsets, psw, toff, out, p.T, p.B, p.D, rs.G,
-                       rs.log2G, rs.P, p.nbags, nblocks);
+#define TBE_FWD(WGT, CHK)                                                                      \
+  hipLaunchKernelGGL((fwd_pool_kernel<WT, V, PMAX, WGT, CHK>), grid, dim3(kFwdThreads), 0, s,  \
+                     (const WT*)W, indices, offsets, psw, toff, out, p.T, p.B, p.D, rs.G,      \
+                     rs.log2G, rs.P, p.nbags, nblocks, p.err)
+  if (psw) {
+    if (p.err) TBE_FWD(true, true);
+    else TBE_FWD(true, false);
+  } else {
+    if (p.err) TBE_FWD(false, true);
+    else TBE_FWD(false, false);
+  }
+#undef TBE_FWD
   return hipGetLastError();
 }
 

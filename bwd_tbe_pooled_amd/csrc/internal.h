@@ -45,6 +45,8 @@ struct Problem {
   int64_t cap_runs, cap_long, cap_chunks;
   // small-table backward split
   int small_splits;
+  // TBE_FLAG_CHECK: where kernels that read indices report a bad one (else null)
+  int32_t* err;
 };
 
 tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p);
@@ -125,14 +127,15 @@ hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta&
                             const void* partials, double lr, double eps, hipStream_t s);
 
 hipError_t launch_small_count(const Problem& p, const int32_t* indices, const int32_t* offsets,
-                              uint8_t* hist, int32_t* counts, hipStream_t s);
+                              const int32_t* tinfo, uint8_t* hist, int32_t* counts,
+                              hipStream_t s);
 hipError_t launch_small_pool(const Problem& p, const void* W, const int32_t* indices,
                              const int32_t* offsets, const int32_t* tinfo, float* out,
                              const uint8_t* hist, const int32_t* counts, hipStream_t s);
 hipError_t launch_small_backward(const Problem& p, const float* grad, const uint8_t* hist,
                                  const int32_t* counts, const int32_t* indices,
                                  const int32_t* offsets, float* partials, int32_t* part_counts,
-                                 hipStream_t s);
+                                 const int32_t* tinfo, hipStream_t s);
 hipError_t launch_small_apply(const Problem& p, void* W, float* m, const int32_t* tinfo,
                               const float* partials, const int32_t* part_counts, double lr,
                               double eps, hipStream_t s);

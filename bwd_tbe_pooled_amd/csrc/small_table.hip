@@ -64,10 +64,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // LDS atomic, the bag known without any search. The first 64 lookups of
 // INFLIGHT bags are loaded before any of them is counted; lookups past the
 // 64th follow bag by bag, eight loads in flight.
+// A lookup's row: without a bounds check (err null) the index is masked to
+// the 64 rows the buffers hold; with one (TBE_FLAG_CHECK) an index outside
+// the table's Et rows counts as row 0 and is reported.
+__device__ __forceinline__ uint32_t count_row(int32_t v, uint32_t Et, const int32_t* err,
+                                              bool& bad) {
+  if (!err) return (uint32_t)v & (kSmallE - 1);
+  const bool out = (uint32_t)v >= Et;
+  bad |= out;
+  return out ? 0u : (uint32_t)v;
+}
+
 template <int INFLIGHT = 4>
 __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
                            const int32_t* __restrict__ indices,
-                           const int32_t* __restrict__ offsets, int64_t bag0, int nb) {
+                           const int32_t* __restrict__ offsets, int64_t bag0, int nb,
+                           uint32_t Et, int32_t* __restrict__ err) {
   constexpr int NBW = kBagTile / kWaves;
   __syncthreads();  // earlier readers of H and s_off are done
   uint4* h4 = reinterpret_cast<uint4*>(&H[0][0]);
@@ -77,6 +89,7 @@ __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int bw0 = wave * NBW;
+  bool bad = false;
   for (int u0 = 0; u0 < NBW; u0 += INFLIGHT) {
     int32_t v[INFLIGHT];
     bool ok[INFLIGHT];
@@ -90,7 +103,7 @@ __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
     }
 #pragma unroll
     for (int u = 0; u < INFLIGHT; ++u)
-      if (ok[u]) atomicAdd(&H[bw0 + u0 + u][v[u] & (kSmallE - 1)], 1u);
+      if (ok[u]) atomicAdd(&H[bw0 + u0 + u][count_row(v[u], Et, err, bad)], 1u);
   }
   for (int u = 0; u < NBW; ++u) {
     const int bl = bw0 + u;
@@ -106,9 +119,10 @@ __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (c + q * kWave + lane < len) atomicAdd(&H[bl][x[q] & (kSmallE - 1)], 1u);
+        if (c + q * kWave + lane < len) atomicAdd(&H[bl][count_row(x[q], Et, err, bad)], 1u);
     }
   }
+  if (err && __ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
   __syncthreads();
 }
 
@@ -121,7 +135,8 @@ __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
 // packs a count row into hist also clears it for the next tile.
 __global__ __launch_bounds__(kThreads) void small_count_kernel(
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
-    uint8_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t B) {
+    uint8_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t B,
+    const int32_t* __restrict__ trows, int32_t* __restrict__ err) {
   constexpr int NBW = kBagTile / kWaves;
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
   __shared__ int32_t s_off[kBagTile * kCountTiles + 1];
@@ -132,6 +147,8 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
   const int64_t wbag0 = (int64_t)t * B + wb0;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
+  const uint32_t Et = (uint32_t)trows[t];
+  bool bad = false;
   uint4* h4 = reinterpret_cast<uint4*>(&H[0][0]);
   for (int q = threadIdx.x; q < kBagTile * kHStride / 4; q += kThreads) h4[q] = uint4{0, 0, 0, 0};
   for (int q = threadIdx.x; q <= wnb; q += kThreads) s_off[q] = offsets[wbag0 + q];
@@ -165,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
     if (k + 1 < kCountTiles) load_first(k + 1);
 #pragma unroll
     for (int u = 0; u < NBW; ++u)
-      if (cok[u]) atomicAdd(&H[wave * NBW + u][cv[u] & (kSmallE - 1)], 1u);
+      if (cok[u]) atomicAdd(&H[wave * NBW + u][count_row(cv[u], Et, err, bad)], 1u);
     // lookups past the 64th of each bag, eight loads in flight
     for (int u = 0; u < NBW; ++u) {
       const int bl = wave * NBW + u;
@@ -181,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (c + q * kWave + lane < len) atomicAdd(&H[bl][x[q] & (kSmallE - 1)], 1u);
+          if (c + q * kWave + lane < len) atomicAdd(&H[bl][count_row(x[q], Et, err, bad)], 1u);
       }
     }
     __syncthreads();
@@ -199,6 +216,7 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
     }
     __syncthreads();
   }
+  if (err && __ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
   mx = wave_max_u32(mx);
   if (lane == 0) s_wmax[wave] = mx;
   __syncthreads();
@@ -327,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
     const f16_t* __restrict__ W, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ toff, const int32_t* __restrict__ trows, float* __restrict__ out,
-    int32_t T, int32_t B, int32_t D) {
+    int32_t T, int32_t B, int32_t D, int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
   __shared__ int32_t s_off[kBagTile + 1];
   __shared__ uint32_t s_wmax[kWaves];
@@ -349,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
     const int32_t b0 = ((int32_t)blockIdx.x * kFwdTiles + k) * kBagTile;
     if (b0 >= B) break;
     const int nb = B - b0 < kBagTile ? B - b0 : kBagTile;
-    count_tile(H, s_off, indices, offsets, (int64_t)t * B + b0, nb);
+    count_tile(H, s_off, indices, offsets, (int64_t)t * B + b0, nb, (uint32_t)Et, err);
     uint32_t mx = 0;
     for (int q = threadIdx.x; q < nb * (kSmallE / 4); q += kThreads) {
       const uint4 c = *reinterpret_cast<const uint4*>(&H[q >> 4][(q & 15) * 4]);
@@ -406,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, float* __restrict__ partials,
     int32_t* __restrict__ part_counts, int32_t T, int32_t B, int32_t D, int32_t splits,
-    int32_t bags_per_split) {
+    int32_t bags_per_split, const int32_t* __restrict__ trows, int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];     // recounted counts
   __shared__ __align__(16) _Float16 HT[kSmallE][kTStride];     // counts, row-major by table row
   __shared__ int32_t s_off[kBagTile + 1];
@@ -481,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
         lo[ks][j] = (_Float16)((g - (float)h) * 2048.f);
       }
 
-    if (recount) count_tile(H, s_off, indices, offsets, bag0, nb);
+    if (recount) count_tile(H, s_off, indices, offsets, bag0, nb, (uint32_t)trows[t], err);
     else __syncthreads();  // earlier readers of HT are done
     {
       // Counts of bag bl, rows e16..e16+15, into HT[e][bl] as f16 (exact).
@@ -551,7 +569,8 @@ __global__ __launch_bounds__(kThreads) void small_backward_wide_kernel(
     const float* __restrict__ grad, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
     float* __restrict__ partials, int32_t* __restrict__ part_counts, int32_t T, int32_t B,
-    int32_t D, int32_t splits, int32_t bags_per_split) {
+    int32_t D, int32_t splits, int32_t bags_per_split, const int32_t* __restrict__ trows,
+    int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
   __shared__ int32_t s_off[kBagTile + 1];
   if (counts[5] == 0) return;
@@ -569,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_wide_kernel(
   uint32_t cnt = 0;  // thread e < 64: count of row e
   for (int32_t b0 = sb0; b0 < sb1; b0 += kBagTile) {
     const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
-    count_tile(H, s_off, indices, offsets, (int64_t)t * B + b0, nb);
+    count_tile(H, s_off, indices, offsets, (int64_t)t * B + b0, nb, (uint32_t)trows[t], err);
     if (threadIdx.x < kSmallE)
       for (int bl = 0; bl < nb; ++bl) cnt += H[bl][threadIdx.x];
     if (d < D) {
@@ -644,13 +663,15 @@ int small_splits_for(int32_t T, int32_t B) {
 }
 
 hipError_t launch_small_count(const Problem& p, const int32_t* indices, const int32_t* offsets,
-                              uint8_t* hist, int32_t* counts, hipStream_t s) {
+                              const int32_t* tinfo, uint8_t* hist, int32_t* counts,
+                              hipStream_t s) {
   hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, s, counts);
   if (p.B > 0) {
     const int64_t count_bags = (int64_t)kBagTile * kCountTiles;
     hipLaunchKernelGGL(small_count_kernel,
                        dim3((unsigned)((p.B + count_bags - 1) / count_bags), (unsigned)p.T),
-                       dim3(kThreads), 0, s, indices, offsets, hist, counts, p.B);
+                       dim3(kThreads), 0, s, indices, offsets, hist, counts, p.B, tinfo + p.T,
+                       p.err);
   }
   return hipGetLastError();
 }
@@ -669,22 +690,25 @@ hipError_t launch_small_pool(const Problem& p, const void* W, const int32_t* ind
   const int64_t re_bags = (int64_t)kBagTile * kFwdTiles;
   hipLaunchKernelGGL(small_recount_forward_kernel,
                      dim3((unsigned)((p.B + re_bags - 1) / re_bags), (unsigned)p.T), dim3(kThreads), 0,
-                     s, (const f16_t*)W, indices, offsets, counts, toff, trows, out, p.T, p.B, p.D);
+                     s, (const f16_t*)W, indices, offsets, counts, toff, trows, out, p.T, p.B, p.D,
+                     p.err);
   return hipGetLastError();
 }
 
 hipError_t launch_small_backward(const Problem& p, const float* grad, const uint8_t* hist,
                                  const int32_t* counts, const int32_t* indices,
                                  const int32_t* offsets, float* partials, int32_t* part_counts,
-                                 hipStream_t s) {
+                                 const int32_t* tinfo, hipStream_t s) {
   const int splits = p.small_splits;
   int32_t per = (p.B + splits - 1) / splits;
   const dim3 grid((unsigned)splits, (unsigned)p.T);
   // Exactly one of the two does the work, chosen on the device by counts[5].
   hipLaunchKernelGGL(small_backward_kernel, grid, dim3(kThreads), 0, s, grad, hist, counts, indices,
-                     offsets, partials, part_counts, p.T, p.B, p.D, splits, per);
+                     offsets, partials, part_counts, p.T, p.B, p.D, splits, per, tinfo + p.T,
+                     p.err);
   hipLaunchKernelGGL(small_backward_wide_kernel, grid, dim3(kThreads), 0, s, grad, counts, indices,
-                     offsets, partials, part_counts, p.T, p.B, p.D, splits, per);
+                     offsets, partials, part_counts, p.T, p.B, p.D, splits, per, tinfo + p.T,
+                     p.err);
   return hipGetLastError();
 }
 

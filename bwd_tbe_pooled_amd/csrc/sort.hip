@@ -122,7 +122,7 @@ __device__ __forceinline__ TileInfo tile_info(int64_t g, const int4* __restrict_
 // summing threads start at staggered columns, so LDS banks rarely collide.
 __global__ __launch_bounds__(kThreads) void sort_upsweep_kernel(
     const int32_t* __restrict__ keys, const int4* __restrict__ tile_desc, int shift, int bits,
-    int64_t tiles_max, int32_t* __restrict__ digit_counts) {
+    int64_t tiles_max, int32_t* __restrict__ digit_counts, const int32_t* __restrict__ clamp_rows) {
   __shared__ uint32_t cnt[32][kThreads + 1];
   const int64_t g = blockIdx.x;
   const TileInfo ti = tile_info(g, tile_desc);
@@ -137,6 +137,11 @@ __global__ __launch_bounds__(kThreads) void sort_upsweep_kernel(
   for (int q = 0; q < kItems; ++q) {
     const int32_t j = ti.a + q * kThreads + tid;
     key[q] = j < ti.e ? keys[j] : 0;
+  }
+  if (clamp_rows) {  // bounds check of the first pass: a bad row sorts as row 0
+    const uint32_t Et = (uint32_t)clamp_rows[ti.t];
+#pragma unroll
+    for (int q = 0; q < kItems; ++q) key[q] = (uint32_t)key[q] < Et ? key[q] : 0;
   }
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
@@ -214,7 +219,8 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
     int32_t* __restrict__ pos_out, int32_t* __restrict__ bag_out, float* __restrict__ psw_out,
     const int4* __restrict__ tile_desc, const int32_t* __restrict__ toff, int shift, int bits,
     int64_t tiles_max, const int32_t* __restrict__ digit_counts,
-    const int32_t* __restrict__ digit_tot) {
+    const int32_t* __restrict__ digit_tot, const int32_t* __restrict__ clamp_rows,
+    int32_t* __restrict__ err) {
   __shared__ int32_t wave_hist[4][256];
   __shared__ int32_t digit_off[256];   // tile-local start of each digit
   __shared__ int32_t gdelta[256];      // global position minus tile-local position
@@ -243,6 +249,19 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
     if constexpr (WITH_POS) pos[r] = FIRST ? j : (ok ? pos_in[j] : 0);
     if constexpr (!FIRST) bag[r] = ok ? bag_in[j] : 0;
     if constexpr (WEIGHTED) w[r] = ok ? psw_in[j] : 0.f;
+  }
+  if (clamp_rows) {
+    // Bounds check fused into the first pass: a row outside its table sorts
+    // (and is later read and updated) as row 0, and the call reports it.
+    const uint32_t Et = (uint32_t)clamp_rows[ti.t];
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < kItems; ++r) {
+      const bool out = wbase + r * kWave + lane < ti.e && (uint32_t)key[r] >= Et;
+      bad |= out;
+      key[r] = out ? 0 : key[r];
+    }
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
   }
   if constexpr (FIRST) {
     // Bag of every element of the tile: each thread takes bags of the tile and
@@ -382,11 +401,12 @@ template <bool FIRST, bool LAST>
 hipError_t launch_downsweep(bool weighted, bool with_pos, dim3 grid, hipStream_t s,
                             const PassArgs& a, const int32_t* offsets, const int4* tile_desc,
                             const int32_t* toff, int shift, int bits, int64_t tiles_max,
-                            const int32_t* dc, const int32_t* dt) {
+                            const int32_t* dc, const int32_t* dt, const int32_t* clamp_rows,
+                            int32_t* err) {
 #define TBE_DS(W, P)                                                                           \
   hipLaunchKernelGGL((sort_downsweep_kernel<FIRST, LAST, W, P>), grid, dim3(kThreads), 0, s,   \
                      a.ki, a.pi, a.bi, a.wi, offsets, a.ko, a.po, a.bo, a.wo, tile_desc, toff, \
-                     shift, bits, tiles_max, dc, dt)
+                     shift, bits, tiles_max, dc, dt, clamp_rows, err)
   if (weighted && with_pos) TBE_DS(true, true);
   else if (weighted) TBE_DS(true, false);
   else if (with_pos) TBE_DS(false, true);
@@ -435,15 +455,18 @@ hipError_t launch_sort(const Problem& p, const int32_t* indices, const int32_t* 
     a.bo = last ? meta.sorted_bag : dst[2];
     a.wo = last ? meta.sorted_psw : (float*)dst[3];
 
+    // TBE_FLAG_CHECK: the first pass reads the indices, so it clamps them
+    const int32_t* clamp_rows = (first && p.err) ? tinfo + p.T : nullptr;
     hipLaunchKernelGGL(sort_upsweep_kernel, tgrid, dim3(kThreads), 0, s, a.ki, b.tile_desc, shift,
-                       p.sort_bits, p.sort_tiles_max, b.digit_counts);
+                       p.sort_bits, p.sort_tiles_max, b.digit_counts, clamp_rows);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipLaunchKernelGGL(sort_scan_kernel, dim3((unsigned)(p.T * radix)), dim3(kThreads), 0, s,
                        b.digit_counts, b.tile_base, radix, p.sort_tiles_max, b.digit_tot);
     if ((err = hipGetLastError()) != hipSuccess) return err;
 #define TBE_DOWNSWEEP(F, L)                                                                     \
   launch_downsweep<F, L>(weighted, with_pos, tgrid, s, a, offsets, b.tile_desc, toff, shift,    \
-                         p.sort_bits, p.sort_tiles_max, b.digit_counts, b.digit_tot)
+                         p.sort_bits, p.sort_tiles_max, b.digit_counts, b.digit_tot, clamp_rows,  \
+                         p.err)
     if (first && last) err = TBE_DOWNSWEEP(true, true);
     else if (first) err = TBE_DOWNSWEEP(true, false);
     else if (last) err = TBE_DOWNSWEEP(false, true);

@@ -75,6 +75,15 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
                                         device before any other work; waits
                                         for the check (host synchronisation) */
 #define TBE_FLAG_FORCE_GENERIC 0x2u  /* never take the small-table path */
+#define TBE_FLAG_CHECK         0x4u  /* bounds check fused into the kernels
+                                        that read indices (page 1, checklist
+                                        item 5): an index outside [0, E_t)
+                                        is read as row 0 and sets
+                                        TBE_ERROR_INDEX in *desc->error_flags;
+                                        no extra pass, no host synchronisation */
+
+/* Bits OR-ed into *tbe_desc.error_flags under TBE_FLAG_CHECK. */
+#define TBE_ERROR_INDEX 0x1u   /* some index was outside its table */
 
 /* Execution paths chosen on the host (tbe_select_path). */
 #define TBE_PATH_GENERIC     0
@@ -114,6 +123,11 @@ typedef struct {
     int32_t chunk;          /* C: lookups per long-run chunk; 0 means 256 */
     uint32_t flags;         /* TBE_FLAG_* */
     tbe_timer* timer;       /* optional stage timer, NULL for none */
+    int32_t* error_flags;   /* device int32, required with TBE_FLAG_CHECK
+                               (else ignored): TBE_ERROR_* bits are OR-ed in
+                               by the kernels; the library never clears it.
+                               Offsets must still be valid: only
+                               TBE_FLAG_VALIDATE checks them. */
 } tbe_desc;
 
 /*

@@ -57,17 +57,18 @@ def device_batch(batch, device="cuda"):
     return d
 
 
-def make_desc(cfg, S=0, C=0, flags=0, timer=None):
+def make_desc(cfg, S=0, C=0, flags=0, timer=None, error_flags=None):
     tbe = lib()
-    return tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, S, C, flags, timer)
+    return tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, S, C, flags, timer,
+                    error_flags=error_flags)
 
 
 def run_library(cfg, batch, W, m, *, meta_in_forward: bool, backward_meta: bool = True,
-                S=0, C=0, flags=0, dev=None, with_pos: bool = True):
+                S=0, C=0, flags=0, dev=None, with_pos: bool = True, error_flags=None):
     """Forward (+ preprocessing when meta_in_forward) and backward through the
     C ABI. W and m are updated in place. Returns out and the metadata."""
     tbe = lib()
-    desc = make_desc(cfg, S, C, flags)
+    desc = make_desc(cfg, S, C, flags, error_flags=error_flags)
     dev = dev or device_batch(batch)
     N = batch.indices.size
     weighted = batch.psw is not None

@@ -238,3 +238,58 @@ def test_stage_timer_counts_each_stage():
         assert t[st][1] == 1 and t[st][0] > 0, st
     for st in ("small_count", "small_fwd", "small_bwd", "small_apply", "validate"):
         assert t[st][1] == 0, st
+
+
+# --- bounds check fused into the kernels (TBE_FLAG_CHECK) -------------------
+
+def _plant_bad_indices(batch, seed, count=24):
+    """Copy of the batch with `count` indices moved outside their tables, and
+    the batch the oracle should see: those lookups read as row 0."""
+    from dataclasses import replace
+    rng = np.random.default_rng(seed)
+    N = batch.indices.size
+    pos = rng.choice(N, size=min(count, N), replace=False)
+    bad = batch.indices.copy()
+    big = np.array([10 ** 9, 2 ** 31 - 1, -1, -7], dtype=np.int64)
+    bad[pos] = np.where(rng.random(pos.size) < 0.5,
+                        max(batch.cfg.rows) + rng.integers(0, 5, pos.size), big[pos % 4])
+    fixed = batch.indices.copy()
+    fixed[pos] = 0
+    return replace(batch, indices=bad), replace(batch, indices=fixed)
+
+
+@pytest.mark.parametrize("k,B,meta_fwd", [(3, 512, True), (4, 1024, True), (4, 1024, False)])
+def test_fused_check_reads_bad_indices_as_row_zero(k, B, meta_fwd):
+    import bwd_tbe_pooled_amd as tbe
+    batch = make_batch(CONFIGS[k], B=B)
+    cfg = batch.cfg
+    bad, fixed = _plant_bad_indices(batch, seed=k + B)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    W, m = fresh_params(cfg)
+    W0, m0 = W.clone(), m.clone()
+    keys, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, fixed.indices, fixed.offsets)
+    uk = np.unique(keys)
+    Wrows, mrows = host_rows(W0, m0, uk)
+    r = run_library(cfg, bad, W, m, meta_in_forward=meta_fwd, flags=tbe.TBE_FLAG_CHECK,
+                    error_flags=err)
+    assert int(err.item()) == tbe.TBE_ERROR_INDEX
+    pre, out, bw = oracle_all(cfg, fixed, Wrows, mrows, uk, 256, 256)
+    assert rel_err(r["out"].cpu().numpy(), out) <= TOL[cfg.dtype]
+    assert_meta_equal(meta_host(r["meta"], 0), pre)
+    assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], "checked")
+    assert_untouched_unchanged(W0, W, m0, m, uk)
+
+
+def test_fused_check_is_silent_and_bitwise_neutral_on_valid_input():
+    import bwd_tbe_pooled_amd as tbe
+    batch = make_batch(CONFIGS[4], B=1024)
+    cfg = batch.cfg
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = []
+    for flags in (0, tbe.TBE_FLAG_CHECK):
+        W, m = fresh_params(cfg)
+        r = run_library(cfg, batch, W, m, meta_in_forward=True, flags=flags, error_flags=err)
+        res.append((r["out"], W.view(torch.int16), m))
+    assert int(err.item()) == 0
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)

@@ -107,3 +107,37 @@ def test_counts_beyond_f16_exact_integers(meta_in_forward):
     f16, so both directions fall back to f32 arithmetic."""
     cfg, batch = _saturated_batch(2500)
     _check(cfg, batch, meta_in_forward=meta_in_forward, expect_saturated=True, expect_wide=True)
+
+
+@pytest.mark.parametrize("meta_in_forward", [True, False])
+def test_fused_check_counts_bad_indices_as_row_zero(meta_in_forward):
+    """TBE_FLAG_CHECK on the small-table path: indices outside the 64 rows
+    count as row 0 in both directions and set the error word."""
+    from dataclasses import replace
+    import bwd_tbe_pooled_amd as tbe
+    batch = make_batch(CONFIGS[5], B=256)
+    cfg = batch.cfg
+    rng = np.random.default_rng(5)
+    pos = rng.choice(batch.indices.size, size=40, replace=False)
+    bad = batch.indices.copy()
+    bad[pos] = np.array([64, 65, 1000, -1, -64], dtype=np.int32)[pos % 5]
+    fixed = batch.indices.copy()
+    fixed[pos] = 0
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    W, m = fresh_params(cfg)
+    W0, m0 = W.clone(), m.clone()
+    keys, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, fixed, batch.offsets)
+    uk = np.unique(keys)
+    Wrows, mrows = host_rows(W0, m0, uk)
+    r = run_library(cfg, replace(batch, indices=bad), W, m, meta_in_forward=meta_in_forward,
+                    flags=tbe.TBE_FLAG_CHECK, error_flags=err)
+    assert int(err.item()) == tbe.TBE_ERROR_INDEX
+    assert r["path"] == 1
+    fb = replace(batch, indices=fixed)
+    pre, out, bw = oracle_all(cfg, fb, Wrows, mrows, uk)
+    assert rel_err(r["out"].cpu().numpy(), out) <= TOL[cfg.dtype]
+    H = oracle.histogram(cfg.T, cfg.B, 64, cfg.rows, fixed, batch.offsets)
+    np.testing.assert_array_equal(r["meta"]["hist"].cpu().numpy().reshape(cfg.T, cfg.B, 64),
+                                  np.minimum(H, 255))
+    assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], "small checked")
+    assert_untouched_unchanged(W0, W, m0, m, uk)
