@@ -67,19 +67,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // A lookup's row: without a bounds check (err null) the index is masked to
 // the 64 rows the buffers hold; with one (TBE_FLAG_CHECK) an index outside
 // the table's Et rows counts as row 0 and is reported.
-__device__ __forceinline__ uint32_t count_row(int32_t v, uint32_t Et, const int32_t* err,
-                                              bool& bad) {
-  if (!err) return (uint32_t)v & (kSmallE - 1);
+template <bool CHECK>
+__device__ __forceinline__ uint32_t count_row(int32_t v, uint32_t Et, bool& bad) {
+  if constexpr (!CHECK) return (uint32_t)v & (kSmallE - 1);
   const bool out = (uint32_t)v >= Et;
   bad |= out;
   return out ? 0u : (uint32_t)v;
 }
 
-template <int INFLIGHT = 4>
-__device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
-                           const int32_t* __restrict__ indices,
-                           const int32_t* __restrict__ offsets, int64_t bag0, int nb,
-                           uint32_t Et, int32_t* __restrict__ err) {
+template <bool CHECK, int INFLIGHT = 4>
+__device__ void count_tile_impl(uint32_t (*H)[kHStride], int32_t* s_off,
+                                const int32_t* __restrict__ indices,
+                                const int32_t* __restrict__ offsets, int64_t bag0, int nb,
+                                uint32_t Et, int32_t* __restrict__ err) {
   constexpr int NBW = kBagTile / kWaves;
   __syncthreads();  // earlier readers of H and s_off are done
   uint4* h4 = reinterpret_cast<uint4*>(&H[0][0]);
@@ -103,7 +103,7 @@ __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
     }
 #pragma unroll
     for (int u = 0; u < INFLIGHT; ++u)
-      if (ok[u]) atomicAdd(&H[bw0 + u0 + u][count_row(v[u], Et, err, bad)], 1u);
+      if (ok[u]) atomicAdd(&H[bw0 + u0 + u][count_row<CHECK>(v[u], Et, bad)], 1u);
   }
   for (int u = 0; u < NBW; ++u) {
     const int bl = bw0 + u;
@@ -119,11 +119,23 @@ __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (c + q * kWave + lane < len) atomicAdd(&H[bl][count_row(x[q], Et, err, bad)], 1u);
+        if (c + q * kWave + lane < len) atomicAdd(&H[bl][count_row<CHECK>(x[q], Et, bad)], 1u);
     }
   }
-  if (err && __ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
+  if constexpr (CHECK) {
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
+  }
   __syncthreads();
+}
+
+// The recounting kernels are off the common path: one body, checked or not
+// by the call's flag.
+__device__ __forceinline__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
+                                           const int32_t* __restrict__ indices,
+                                           const int32_t* __restrict__ offsets, int64_t bag0,
+                                           int nb, uint32_t Et, int32_t* __restrict__ err) {
+  if (err) count_tile_impl<true>(H, s_off, indices, offsets, bag0, nb, Et, err);
+  else count_tile_impl<false>(H, s_off, indices, offsets, bag0, nb, Et, err);
 }
 
 // Saturating uint8 counts of kCountTiles consecutive 64-bag tiles of one
@@ -133,6 +145,7 @@ __device__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_off,
 // the first 64 lookups of its bags in tile k+1 are loaded (one coalesced
 // load per bag) before it counts tile k with LDS atomics; the thread that
 // packs a count row into hist also clears it for the next tile.
+template <bool CHECK>
 __global__ __launch_bounds__(kThreads) void small_count_kernel(
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
     uint8_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t B,
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
     if (k + 1 < kCountTiles) load_first(k + 1);
 #pragma unroll
     for (int u = 0; u < NBW; ++u)
-      if (cok[u]) atomicAdd(&H[wave * NBW + u][count_row(cv[u], Et, err, bad)], 1u);
+      if (cok[u]) atomicAdd(&H[wave * NBW + u][count_row<CHECK>(cv[u], Et, bad)], 1u);
     // lookups past the 64th of each bag, eight loads in flight
     for (int u = 0; u < NBW; ++u) {
       const int bl = wave * NBW + u;
@@ -198,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if (c + q * kWave + lane < len) atomicAdd(&H[bl][count_row(x[q], Et, err, bad)], 1u);
+          if (c + q * kWave + lane < len) atomicAdd(&H[bl][count_row<CHECK>(x[q], Et, bad)], 1u);
       }
     }
     __syncthreads();
@@ -216,7 +229,9 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
     }
     __syncthreads();
   }
-  if (err && __ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
+  if constexpr (CHECK) {
+    if (__ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
+  }
   mx = wave_max_u32(mx);
   if (lane == 0) s_wmax[wave] = mx;
   __syncthreads();
@@ -668,10 +683,13 @@ hipError_t launch_small_count(const Problem& p, const int32_t* indices, const in
   hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(64), 0, s, counts);
   if (p.B > 0) {
     const int64_t count_bags = (int64_t)kBagTile * kCountTiles;
-    hipLaunchKernelGGL(small_count_kernel,
-                       dim3((unsigned)((p.B + count_bags - 1) / count_bags), (unsigned)p.T),
-                       dim3(kThreads), 0, s, indices, offsets, hist, counts, p.B, tinfo + p.T,
-                       p.err);
+    const dim3 grid((unsigned)((p.B + count_bags - 1) / count_bags), (unsigned)p.T);
+    if (p.err)
+      hipLaunchKernelGGL(small_count_kernel<true>, grid, dim3(kThreads), 0, s, indices, offsets,
+                         hist, counts, p.B, tinfo + p.T, p.err);
+    else
+      hipLaunchKernelGGL(small_count_kernel<false>, grid, dim3(kThreads), 0, s, indices, offsets,
+                         hist, counts, p.B, tinfo + p.T, p.err);
   }
   return hipGetLastError();
 }
