@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--check", choices=["none", "fused", "validate"], default="none",
                     help="index checking: none (default), fused into the kernels "
                          "(TBE_FLAG_CHECK), or the separate synchronous pass (TBE_FLAG_VALIDATE)")
+    ap.add_argument("--preprocess", choices=["forward", "backward"], default="forward",
+                    help="where the transpose (sort, RLE, routing) runs: in the forward "
+                         "(default; the pages' hoisting) or inside the backward (their baseline)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -191,19 +194,26 @@ def main():
     flags = {"none": 0, "fused": tbe.TBE_FLAG_CHECK, "validate": tbe.TBE_FLAG_VALIDATE}[args.check]
     desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, flags=flags, error_flags=err)
     meta = tbe.Meta(desc, N, True, with_pos=False)   # the backward needs no positions
-    ws_f = tbe.workspace(desc, N, True, tbe.TBE_OP_FORWARD_PREPROCESS)
-    ws_b = tbe.workspace(desc, N, True, tbe.TBE_OP_BACKWARD)
+    in_fwd = args.preprocess == "forward"
+    ws_f = tbe.workspace(desc, N, True, tbe.TBE_OP_FORWARD_PREPROCESS if in_fwd else tbe.TBE_OP_FORWARD)
+    ws_b = tbe.workspace(desc, N, True, tbe.TBE_OP_BACKWARD if in_fwd else tbe.TBE_OP_BACKWARD_SELF)
     if args.profile_copy:
         profile_copy(torch, dev)
     torch.cuda.synchronize()
 
     def step():
-        tbe.tbe_forward(desc, W, idx, off, psw, out, meta, ws_f)
-        tbe.tbe_backward_adagrad(desc, W, m, grad, idx, off, psw, meta, cfg.lr, cfg.eps, ws_b)
+        if in_fwd:
+            tbe.tbe_forward(desc, W, idx, off, psw, out, meta, ws_f)
+            tbe.tbe_backward_adagrad(desc, W, m, grad, idx, off, psw, meta, cfg.lr, cfg.eps, ws_b)
+        else:   # the backward preprocesses into its own workspace
+            tbe.tbe_forward(desc, W, idx, off, psw, out, None, ws_f)
+            tbe.tbe_backward_adagrad(desc, W, m, grad, idx, off, psw, None, cfg.lr, cfg.eps, ws_b)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
+    if not in_fwd:   # run structure for the byte counts below
+        tbe.tbe_preprocess(desc, idx, off, psw, meta, tbe.workspace(desc, N, True, tbe.TBE_OP_PREPROCESS))
     torch.cuda.synchronize()
     counts = meta["counts"][:4].cpu().numpy()
     U, n_short, n_long, n_chunks = (int(x) for x in counts)
@@ -256,7 +266,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "T=32 E=2M D=128 bf16 B=131072 Poisson(20) Zipf-Mandelbrot weighted, "
-                               "preprocessing in forward"
+                               f"preprocessing in {args.preprocess}"
                                + ("" if args.check == "none" else f", index check: {args.check}"),
                    "T": cfg.T, "E": cfg.rows[0], "D": cfg.D, "B": cfg.B, "N": N, "U": U,
                    "long_runs": n_long, "chunks": n_chunks, "long_lookups": long_lookups,

@@ -143,6 +143,7 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
   if (L.has_meta) {
     int64_t caps[TBE_META_NUM_ARRAYS];
     meta_caps(p, caps);
+    caps[TBE_META_SORTED_POS] = 0;  // the backward never reads positions: none sorted
     for (int i = 0; i < TBE_META_NUM_ARRAYS; ++i)
       L.meta[i] = caps[i] ? take(meta_elem_bytes(i) * (size_t)caps[i]) : 0;
   }
@@ -247,8 +248,8 @@ tbe_meta carve_meta(void* ws, const WsLayout& L) {
   m.chunk_run = (int32_t*)ptr(TBE_META_CHUNK_RUN);
   m.chunk_start = (int32_t*)ptr(TBE_META_CHUNK_START);
   m.hist = (uint8_t*)ptr(TBE_META_HIST);
-  // Unused psw slot on unweighted problems still needs a non-null pointer for
-  // nothing; leave NULL.
+  // Arrays the path does not use (positions, the psw of unweighted problems,
+  // the generic arrays on the small-table path and the reverse) stay NULL.
   return m;
 }
 
