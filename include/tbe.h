@@ -18,7 +18,9 @@
  *   pointers marked "host" are ordinary host memory, read during the call only.
  * - The caller owns every buffer. The library never allocates or frees device
  *   memory and keeps no state between calls (a timer, when passed, is the
- *   caller's object). Calls on different streams with disjoint buffers may run
+ *   caller's object) beyond two host-side caches: the text behind
+ *   tbe_last_error (per calling thread) and each device's compute-unit count,
+ *   queried once. Calls on different streams with disjoint buffers may run
  *   concurrently.
  * - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it
  *   and the call returns without waiting, except under TBE_FLAG_VALIDATE.
