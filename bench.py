@@ -30,7 +30,6 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
-WORKLOAD = 4
 
 
 def log(msg):
@@ -172,11 +171,11 @@ def main():
         sys.exit(2)
     sys.path.insert(0, ROOT)
     import bwd_tbe_pooled_amd as tbe
-    from workloads import CONFIGS, init_state, init_weights, make_batch
+    from workloads import WORKLOADS, TINY, DEMO3, MEDIUM, LARGE, SMALL_TABLE, init_state, init_weights, make_batch
 
     if args.workload == "small":
         return main_small(args, torch, tbe)
-    cfg = CONFIGS[WORKLOAD]
+    cfg = LARGE
     log("generating the batch")
     batch = make_batch(cfg)
     N = batch.indices.size
@@ -294,8 +293,8 @@ def main():
 
 
 def main_small(args, torch, tbe):
-    from workloads import CONFIGS, init_state, init_weights, make_batch
-    cfg = CONFIGS[5]
+    from workloads import WORKLOADS, TINY, DEMO3, MEDIUM, LARGE, SMALL_TABLE, init_state, init_weights, make_batch
+    cfg = SMALL_TABLE
     log("generating the small-table batch")
     batch = make_batch(cfg)
     N = batch.indices.size

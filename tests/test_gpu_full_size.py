@@ -18,7 +18,7 @@ import torch
 import oracle
 from tests.gpu_common import (TOL, assert_rows_match, assert_untouched_unchanged, fresh_params,
                               host_rows, meta_host, rel_err, run_library)
-from workloads import CONFIGS, make_batch
+from workloads import WORKLOADS, TINY, DEMO3, MEDIUM, LARGE, SMALL_TABLE, make_batch
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -54,7 +54,7 @@ def _sampled_backward(cfg, batch, keys, bags, W, m, Wrows_all, mrows_all, uk, sa
 
 
 def test_large_skewed_workload_full_size():
-    cfg = CONFIGS[4]
+    cfg = LARGE
     print("\n[full] generating the T=32 B=131072 workload", flush=True)
     batch = make_batch(cfg)
     keys, bags = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
@@ -108,7 +108,7 @@ def test_large_skewed_workload_full_size():
 
 
 def test_small_table_workload_full_size():
-    cfg = CONFIGS[5]
+    cfg = SMALL_TABLE
     print("\n[full] generating the T=64 B=32768 small-table workload", flush=True)
     batch = make_batch(cfg)
     W, m = fresh_params(cfg)

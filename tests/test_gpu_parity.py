@@ -12,7 +12,7 @@ from tests.gpu_common import (TOL, assert_meta_equal, assert_rows_match,
                               assert_untouched_unchanged, fresh_params, host_rows,
                               make_desc, meta_host, oracle_all, rel_err, run_library)
 from tests.helpers import TOL as _TOL  # noqa: F401
-from workloads import CONFIGS, Config, make_batch
+from workloads import WORKLOADS, TINY, DEMO3, MEDIUM, LARGE, SMALL_TABLE, Config, make_batch
 
 pytestmark = pytest.mark.gpu
 
@@ -46,49 +46,50 @@ def _full_check(cfg, batch, *, meta_in_forward, backward_meta=True, S=0, C=0, m0
     return r, pre
 
 
-@pytest.mark.parametrize("k", [1, 2, 3])
-def test_config_generic_full(k):
-    cfg = CONFIGS[k]
+@pytest.mark.parametrize("name", ["tiny_t2_e1k_d16_f32", "demo3_d16_f32_b4k",
+                                  "t16_e1m_d128_f16_b16k"])
+def test_generic_workload_full(name):
+    cfg = WORKLOADS[name]
     batch = make_batch(cfg)
     _full_check(cfg, batch, meta_in_forward=False, backward_meta=False)
 
 
-def test_config1_metadata_reused_from_preprocess():
-    cfg = CONFIGS[1]
+def test_tiny_metadata_reused_from_preprocess():
+    cfg = TINY
     _full_check(cfg, make_batch(cfg), meta_in_forward=False, backward_meta=True)
 
 
-def test_config4_reduced_batch_full_compare():
-    cfg = CONFIGS[4]
+def test_large_skewed_reduced_batch_full_compare():
+    cfg = LARGE
     batch = make_batch(cfg, B=2048)
     _full_check(batch.cfg, batch, meta_in_forward=True, backward_meta=True)
 
 
-@pytest.mark.parametrize("k", [2, 3])
-def test_metadata_without_positions(k):
+@pytest.mark.parametrize("name", ["demo3_d16_f32_b4k", "t16_e1m_d128_f16_b16k"])
+def test_metadata_without_positions(name):
     """sorted_pos left NULL: the sort carries only bags and weights, which must
     still match the oracle's stable order bit for bit."""
-    cfg = CONFIGS[k]
+    cfg = WORKLOADS[name]
     batch = make_batch(cfg, B=2048)
     _full_check(batch.cfg, batch, meta_in_forward=True, with_pos=False)
 
 
-def test_config4_reduced_batch_without_positions():
-    cfg = CONFIGS[4]
+def test_large_skewed_reduced_batch_without_positions():
+    cfg = LARGE
     batch = make_batch(cfg, B=1024)
     _full_check(batch.cfg, batch, meta_in_forward=True, with_pos=False)
 
 
-def test_config2_fp64_partials_with_small_chunks():
+def test_demo3_fp64_partials_with_small_chunks():
     """f32 weights accumulate and keep chunk partials in f64; small S/C put
     many runs on the chunked path."""
-    cfg = CONFIGS[2]
+    cfg = DEMO3
     batch = make_batch(cfg, B=1024)
     _full_check(batch.cfg, batch, meta_in_forward=True, S=4, C=3)
 
 
 def test_nonzero_initial_state():
-    cfg = CONFIGS[3]
+    cfg = MEDIUM
     batch = make_batch(cfg, B=256)
     _full_check(batch.cfg, batch, meta_in_forward=True, m0="uniform")
 
@@ -164,7 +165,7 @@ def test_odd_dimensions(D):
 
 
 def test_unit_weights_equal_unweighted_bitwise():
-    cfg = CONFIGS[3]
+    cfg = MEDIUM
     batch = make_batch(cfg, B=512)
     outs = []
     for psw in (None, np.ones(batch.indices.size, dtype=np.float32)):
@@ -179,7 +180,7 @@ def test_unit_weights_equal_unweighted_bitwise():
 
 
 def test_runs_are_deterministic():
-    cfg = CONFIGS[4]
+    cfg = LARGE
     batch = make_batch(cfg, B=4096)
     res = []
     for _ in range(2):
@@ -192,7 +193,7 @@ def test_runs_are_deterministic():
 
 def test_validate_flag_reports_bad_input_before_other_work():
     import bwd_tbe_pooled_amd as tbe
-    cfg = CONFIGS[1]
+    cfg = TINY
     batch = make_batch(cfg)
     desc = make_desc(cfg, flags=tbe.TBE_FLAG_VALIDATE)
     W, m = fresh_params(cfg)
@@ -217,7 +218,7 @@ def test_validate_flag_reports_bad_input_before_other_work():
 
 def test_stage_timer_counts_each_stage():
     import bwd_tbe_pooled_amd as tbe
-    cfg = CONFIGS[3]
+    cfg = MEDIUM
     batch = make_batch(cfg, B=1024)
     timer = tbe.Timer(8)
     desc = make_desc(batch.cfg, timer=timer)
@@ -258,12 +259,14 @@ def _plant_bad_indices(batch, seed, count=24):
     return replace(batch, indices=bad), replace(batch, indices=fixed)
 
 
-@pytest.mark.parametrize("k,B,meta_fwd", [(3, 512, True), (4, 1024, True), (4, 1024, False)])
-def test_fused_check_reads_bad_indices_as_row_zero(k, B, meta_fwd):
+@pytest.mark.parametrize("name,B,meta_fwd", [("t16_e1m_d128_f16_b16k", 512, True),
+                                             ("t32_e2m_d128_bf16_b128k", 1024, True),
+                                             ("t32_e2m_d128_bf16_b128k", 1024, False)])
+def test_fused_check_reads_bad_indices_as_row_zero(name, B, meta_fwd):
     import bwd_tbe_pooled_amd as tbe
-    batch = make_batch(CONFIGS[k], B=B)
+    batch = make_batch(WORKLOADS[name], B=B)
     cfg = batch.cfg
-    bad, fixed = _plant_bad_indices(batch, seed=k + B)
+    bad, fixed = _plant_bad_indices(batch, seed=len(name) + B + int(meta_fwd))
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     W, m = fresh_params(cfg)
     W0, m0 = W.clone(), m.clone()
@@ -282,7 +285,7 @@ def test_fused_check_reads_bad_indices_as_row_zero(k, B, meta_fwd):
 
 def test_fused_check_is_silent_and_bitwise_neutral_on_valid_input():
     import bwd_tbe_pooled_amd as tbe
-    batch = make_batch(CONFIGS[4], B=1024)
+    batch = make_batch(LARGE, B=1024)
     cfg = batch.cfg
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     res = []

@@ -8,7 +8,7 @@ import torch
 import oracle
 from tests.gpu_common import (TOL, assert_rows_match, assert_untouched_unchanged, fresh_params,
                               host_rows, oracle_all, rel_err, run_library)
-from workloads import CONFIGS, Batch, Config, make_batch
+from workloads import WORKLOADS, TINY, DEMO3, MEDIUM, LARGE, SMALL_TABLE, Batch, Config, make_batch
 
 pytestmark = pytest.mark.gpu
 
@@ -50,8 +50,8 @@ def _cfg(T, B, D, E, L, seed):
                   preprocess_in_forward=False, seed=seed)
 
 
-def test_config5_reduced_batch():
-    cfg = CONFIGS[5]
+def test_small_table_reduced_batch():
+    cfg = SMALL_TABLE
     batch = make_batch(cfg, B=512)
     _check(batch.cfg, batch)
 
@@ -59,13 +59,13 @@ def test_config5_reduced_batch():
 def test_forward_without_metadata_then_preprocess():
     """Forward given no metadata keeps its counts in the workspace; the
     metadata then comes from tbe_preprocess."""
-    cfg = CONFIGS[5]
+    cfg = SMALL_TABLE
     batch = make_batch(cfg, B=700)
     _check(batch.cfg, batch, meta_in_forward=False)
 
 
 def test_backward_without_saved_counts():
-    cfg = CONFIGS[5]
+    cfg = SMALL_TABLE
     batch = make_batch(cfg, B=300)
     _check(batch.cfg, batch, meta_in_forward=True, backward_meta=False)
 
@@ -115,7 +115,7 @@ def test_fused_check_counts_bad_indices_as_row_zero(meta_in_forward):
     count as row 0 in both directions and set the error word."""
     from dataclasses import replace
     import bwd_tbe_pooled_amd as tbe
-    batch = make_batch(CONFIGS[5], B=256)
+    batch = make_batch(SMALL_TABLE, B=256)
     cfg = batch.cfg
     rng = np.random.default_rng(5)
     pos = rng.choice(batch.indices.size, size=40, replace=False)
