@@ -36,8 +36,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(cfg, N, U, n_chunks, long_lookups, weighted):
-    """Bytes each part of the method must move at least once per step."""
+def algorithmic_bytes(cfg, N, U, n_chunks, long_lookups, weighted, n_long=0):
+    """Bytes each part of the method must move at least once per step. The
+    fused long kernel also re-reads the partials and updates the long rows."""
     w = 2 if cfg.dtype in ("f16", "bf16") else 4
     a = 8 if cfg.dtype == "f32" else 4
     D, nb = cfg.D, cfg.T * cfg.B
@@ -45,7 +46,8 @@ def algorithmic_bytes(cfg, N, U, n_chunks, long_lookups, weighted):
     fwd = N * (D * w + 4 + psw) + 4 * (nb + 1) + 4 * nb * D
     bwd = N * (4 * D + 4 + psw) + U * (2 * D * w + 16) + 2 * n_chunks * D * a
     long_kernel = long_lookups * (4 * D + 4 + psw) + n_chunks * (D * a + 12)
-    return dict(fwd=fwd, bwd=bwd, bwd_long=long_kernel)
+    fused = long_kernel + n_chunks * D * a + n_long * (2 * D * w + 8)
+    return dict(fwd=fwd, bwd=bwd, bwd_long=long_kernel, bwd_long_fused=fused)
 
 
 def small_table_bytes(cfg, N):
@@ -157,6 +159,9 @@ def main():
     ap.add_argument("--preprocess", choices=["forward", "backward"], default="forward",
                     help="where the transpose (sort, RLE, routing) runs: in the forward "
                          "(default; the pages' hoisting) or inside the backward (their baseline)")
+    ap.add_argument("--long", choices=["two_launch", "fused"], default="two_launch",
+                    help="long runs: chunk partials then a separate apply (default), or one "
+                         "launch whose last chunk per run reduces and applies (TBE_FLAG_FUSED_LONG)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -191,6 +196,9 @@ def main():
     timer = tbe.Timer(capacity=args.steps + 1)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     flags = {"none": 0, "fused": tbe.TBE_FLAG_CHECK, "validate": tbe.TBE_FLAG_VALIDATE}[args.check]
+    fused_long = args.long == "fused"
+    if fused_long:
+        flags |= tbe.TBE_FLAG_FUSED_LONG
     desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, flags=flags, error_flags=err)
     meta = tbe.Meta(desc, N, True, with_pos=False)   # the backward needs no positions
     in_fwd = args.preprocess == "forward"
@@ -236,11 +244,12 @@ def main():
     fwd_ms = avg["fwd_pool"]
     pre_ms = avg["linearize"] + avg["sort"] + avg["rle_route"]
     bwd_ms = avg["bwd_short"] + avg["long_schedule"] + avg["bwd_long"] + avg["bwd_apply"]
-    by = algorithmic_bytes(cfg, N, U, n_chunks, long_lookups, True)
+    by = algorithmic_bytes(cfg, N, U, n_chunks, long_lookups, True, n_long)
     fwd_gbps = by["fwd"] / (fwd_ms * 1e6)
     bwd_gbps = by["bwd"] / (bwd_ms * 1e6)
     # dominant single kernel: the longest of the one-kernel stages
-    cand = {"fwd_pool": (avg["fwd_pool"], by["fwd"]), "bwd_long": (avg["bwd_long"], by["bwd_long"])}
+    long_name = "bwd_long_fused" if fused_long else "bwd_long"
+    cand = {"fwd_pool": (avg["fwd_pool"], by["fwd"]), long_name: (avg["bwd_long"], by[long_name])}
     dom = max(cand, key=lambda k: cand[k][0])
     dom_ms, dom_bytes = cand[dom]
     achieved = dom_bytes / (dom_ms * 1e6)
@@ -266,7 +275,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "T=32 E=2M D=128 bf16 B=131072 Poisson(20) Zipf-Mandelbrot weighted, "
                                f"preprocessing in {args.preprocess}"
-                               + ("" if args.check == "none" else f", index check: {args.check}"),
+                               + ("" if args.check == "none" else f", index check: {args.check}")
+                               + (", long runs in one launch" if fused_long else ""),
                    "T": cfg.T, "E": cfg.rows[0], "D": cfg.D, "B": cfg.B, "N": N, "U": U,
                    "long_runs": n_long, "chunks": n_chunks, "long_lookups": long_lookups,
                    "parallelism": "single GPU"},

@@ -44,7 +44,9 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   if (!d || !p || !d->rows) return TBE_ERR_ARG;
   if (d->T < 1 || d->D < 1 || d->B < 0 || N < 0) return TBE_ERR_ARG;
   if (d->wdtype != TBE_F32 && d->wdtype != TBE_F16 && d->wdtype != TBE_BF16) return TBE_ERR_UNSUPPORTED;
-  if (d->flags & ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC | TBE_FLAG_CHECK)) return TBE_ERR_ARG;
+  if (d->flags &
+      ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC | TBE_FLAG_CHECK | TBE_FLAG_FUSED_LONG))
+    return TBE_ERR_ARG;
   if ((d->flags & TBE_FLAG_CHECK) && !d->error_flags) return TBE_ERR_ARG;
   if (d->short_max < 0 || d->chunk < 0) return TBE_ERR_ARG;
   int64_t sum = 0, mx = 0;
@@ -81,6 +83,7 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   p->cap_chunks = p->cap_long ? N / p->C + p->cap_long : 0;
   p->small_splits = small_splits_for(d->T, d->B);
   p->err = (d->flags & TBE_FLAG_CHECK) ? d->error_flags : nullptr;
+  p->fused_long = (d->flags & TBE_FLAG_FUSED_LONG) != 0;
   return TBE_OK;
 }
 
@@ -456,6 +459,12 @@ tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
   TBE_TRY_HIP(launch_long_schedule(p, m, at<int32_t>(ws, L.sched), s));
   timer_end(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
   timer_begin(desc->timer, TBE_STAGE_BWD_LONG, s);
+  if (p.fused_long) {
+    TBE_TRY_HIP(launch_bwd_long_fused(p, W, momentum, grad_out, m, parts,
+                                      at<int32_t>(ws, L.sched), lr, eps, s));
+    timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
+    return TBE_OK;
+  }
   TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, at<int32_t>(ws, L.sched), s));
   timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
   timer_begin(desc->timer, TBE_STAGE_BWD_APPLY, s);

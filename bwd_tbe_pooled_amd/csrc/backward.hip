@@ -274,6 +274,56 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
   }
 }
 
+// Sum of the partials of chunks [c0, c1) of one long run, then its Adagrad
+// step. Slot s sums chunks c0+s, c0+s+NS, ... in ascending order and the
+// slots are combined by a fixed butterfly, so the order is the same every
+// call; the apply kernel and the fused long kernel both reduce through this
+// function with the same row shape, so they give the same bits.
+template <typename WT, typename ACC, int V, int PMAX>
+__device__ __forceinline__ void reduce_apply_run(WT* __restrict__ W, float* __restrict__ mom,
+                                                 const ACC* __restrict__ partials, int32_t c0,
+                                                 int32_t c1, int32_t key, int32_t D, int G,
+                                                 int log2G, int P, ACC lr, ACC eps) {
+  const int lane = lane_id();
+  const int slot = lane >> log2G;
+  const int col = lane & (G - 1);
+  const int NS = kWave >> log2G;
+  using RAW = typename raw_vec<ACC, V>::type;
+  constexpr int UNROLL = 4;  // chunks in flight per slot: a run's chain of loads is the latency
+  ACC acc[PMAX][V];
+  zero_acc<ACC, V, PMAX>(acc);
+  for (int32_t cb = c0 + slot; cb < c1; cb += NS * UNROLL) {
+    RAW buf[UNROLL][PMAX];
+#pragma unroll
+    for (int uu = 0; uu < UNROLL; ++uu) {
+      const int32_t c = cb + uu * NS;
+      const ACC* src = partials + (int64_t)(c < c1 ? c : c0) * D;
+#pragma unroll
+      for (int p = 0; p < PMAX; ++p) {
+        const int e = (p * G + col) * V;
+        if (p < P && e < D) buf[uu][p] = load_vec<ACC, V>(src + e);
+        else buf[uu][p] = RAW{};  // columns past the row stay zero (they enter the sum of squares)
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < UNROLL; ++uu) {
+      if (cb + uu * NS >= c1) break;
+#pragma unroll
+      for (int p = 0; p < PMAX; ++p) {
+        const ACC* x = reinterpret_cast<const ACC*>(&buf[uu][p]);
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[p][v] += x[v];
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[p][v] = across_slots_sum<ACC>(acc[p][v], G);
+  if (slot == 0)
+    adagrad_row<WT, ACC, V, PMAX>(W + (int64_t)key * D, mom + key, acc, col, G, P, D, lr, eps);
+}
+
 template <typename WT, int V, int PMAX>
 __global__ __launch_bounds__(kThreads) void bwd_apply_kernel(
     WT* __restrict__ W, float* __restrict__ mom, const int32_t* __restrict__ counts,
@@ -282,39 +332,77 @@ __global__ __launch_bounds__(kThreads) void bwd_apply_kernel(
     int32_t D, int32_t G, int32_t log2G, int32_t P, typename acc_of<WT>::type lr,
     typename acc_of<WT>::type eps) {
   using ACC = typename acc_of<WT>::type;
-  const int lane = lane_id();
-  const int slot = lane >> log2G;
-  const int col = lane & (G - 1);
-  const int NS = kWave >> log2G;
   const int64_t n_long = counts[2];
   const int64_t gwave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   for (int64_t l = gwave; l < n_long; l += nwaves) {
-    const int32_t c0 = long_chunk_begin[l];
-    const int32_t c1 = long_chunk_begin[l + 1];
+    reduce_apply_run<WT, ACC, V, PMAX>(W, mom, partials, long_chunk_begin[l],
+                                       long_chunk_begin[l + 1], run_keys[long_runs[l]], D, G,
+                                       log2G, P, lr, eps);
+  }
+}
+
+// The long path in one launch: each chunk writes its partial, makes it visible
+// device-wide (agent-scope release) and counts itself in on its run; the wave
+// that arrives last (acquire) reduces the run's partials and applies Adagrad.
+// No wave waits for another, so the kernel cannot stall on a missing chunk.
+// arrivals[first chunk of the run] must be zero at launch. On gfx950 the
+// agent-scope release writes back the XCD's L2 and the acquire invalidates it.
+template <typename WT, int V, int PMAX, bool WEIGHTED>
+__global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
+    WT* __restrict__ W, float* __restrict__ mom, const float* __restrict__ grad,
+    const int32_t* __restrict__ chunk_run, const int32_t* __restrict__ chunk_start,
+    const int32_t* __restrict__ run_offsets, const int32_t* __restrict__ run_keys,
+    const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ list_begin,
+    typename acc_of<WT>::type* __restrict__ partials, int32_t* __restrict__ arrivals, int32_t T,
+    int32_t B, int32_t D, int32_t C, int32_t G, int32_t log2G, int32_t P,
+    typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
+  using ACC = typename acc_of<WT>::type;
+  const int lane = lane_id();
+  const int slot = lane >> log2G;
+  const int col = lane & (G - 1);
+  const int x = blockIdx.x % kXcds;
+  const int64_t first = list_begin[x];
+  const int64_t n_items = list_begin[x + 1] - first;
+  const int64_t gwave = (int64_t)(blockIdx.x / kXcds) * kWaves + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)(gridDim.x / kXcds) * kWaves;
+
+  for (int64_t it = gwave; it < n_items; it += nwaves) {
+    const int32_t c = order[first + it];
+    const int32_t u = chunk_run[c];
+    const int32_t k0 = chunk_start[c];
+    const int32_t ks = run_offsets[u];
+    const int32_t kend = run_offsets[u + 1];
+    const int32_t k1 = k0 + C < kend ? k0 + C : kend;
     ACC acc[PMAX][V];
-    zero_acc<ACC, V, PMAX>(acc);
-    // slot s sums chunks c0+s, c0+s+NS, ... in ascending order; the slots are
-    // then combined by a fixed butterfly, so the order is the same every run.
-    for (int32_t c = c0 + slot; c < c1; c += NS) {
-      const ACC* src = partials + (int64_t)c * D;
+    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, T, B, D, G,
+                                            log2G, P, acc);
+    if (slot == 0) {
+      ACC* out = partials + (int64_t)c * D;
 #pragma unroll
       for (int p = 0; p < PMAX; ++p) {
         const int e = (p * G + col) * V;
         if (p < P && e < D) {
 #pragma unroll
-          for (int v = 0; v < V; ++v) acc[p][v] += src[e + v];
+          for (int v = 0; v < V; ++v) out[e + v] = acc[p][v];
         }
       }
     }
-#pragma unroll
-    for (int p = 0; p < PMAX; ++p)
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[p][v] = across_slots_sum<ACC>(acc[p][v], G);
-    if (slot == 0) {
-      const int32_t key = run_keys[long_runs[l]];
-      adagrad_row<WT, ACC, V, PMAX>(W + (int64_t)key * D, mom + key, acc, col, G, P, D, lr, eps);
-    }
+    // The whole wave executes the fence, so every lane's partial stores are
+    // complete and visible device-wide before lane 0's increment is issued.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int32_t c_first = c - (k0 - ks) / C;
+    const int32_t nch = (kend - ks + C - 1) / C;
+    int32_t prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(arrivals + c_first, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0);
+    if (prev != nch - 1) continue;  // another chunk of the run is still to come
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    reduce_apply_run<WT, ACC, V, PMAX>(W, mom, partials, c_first, c_first + nch, run_keys[u], D,
+                                       G, log2G, P, lr, eps);
   }
 }
 
@@ -329,10 +417,11 @@ __global__ void sched_zero_kernel(int32_t* __restrict__ p, int n) {
 __global__ __launch_bounds__(256) void sched_count_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ chunk_start,
     const int32_t* __restrict__ sorted_bag, int32_t B, int32_t T, int shift,
-    int32_t* __restrict__ hist, int32_t* __restrict__ bucket_of) {
+    int32_t* __restrict__ hist, int32_t* __restrict__ bucket_of, int32_t* __restrict__ arrivals) {
   const int64_t n = counts[3];
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
        c += (int64_t)gridDim.x * blockDim.x) {
+    arrivals[c] = 0;  // arrival counters of the fused long kernel
     const int32_t bag = sorted_bag[chunk_start[c]];
     const int32_t t = bag / B, b = bag - t * B;
     const int x = (int)(((int64_t)t * kXcds) / T);
@@ -393,20 +482,24 @@ hipError_t short_typed(const Problem& p, const RowShape& rs, void* W, float* m, 
   return hipGetLastError();
 }
 
+// Two workgroups (eight waves) per CU. More chunks in flight widen the
+// window of bags whose gradient rows the XCD's L2 must hold at once: with
+// T=32, E=2M, D=128, B=131072 and Zipf-Mandelbrot rows (287,766 chunks),
+// 1, 2, 3, 4 and 8 workgroups per CU took 4.87, 3.21, 3.43, 3.80 and
+// 4.01 ms on one MI355X.
+inline dim3 long_grid(const Problem& p) {
+  const int64_t per_xcd = 2 * std::max(1, device_cu_count() / kXcds);
+  int64_t blocks = (persistent_blocks(p.cap_chunks) + kXcds - 1) / kXcds * kXcds;
+  if (blocks > per_xcd * kXcds) blocks = per_xcd * kXcds;
+  return dim3((unsigned)blocks);
+}
+
 template <typename ACC, int V, int PMAX>
 hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, const tbe_meta& meta,
                       void* partials, const int32_t* sched, hipStream_t s) {
   const int32_t* order = sched;
   const int32_t* list_begin = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets;
-  // Two workgroups (eight waves) per CU. More chunks in flight widen the
-  // window of bags whose gradient rows the XCD's L2 must hold at once: with
-  // T=32, E=2M, D=128, B=131072 and Zipf-Mandelbrot rows (287,766 chunks),
-  // 1, 2, 3, 4 and 8 workgroups per CU took 4.87, 3.21, 3.43, 3.80 and
-  // 4.01 ms on one MI355X.
-  const int64_t per_xcd = 2 * std::max(1, device_cu_count() / kXcds);
-  int64_t blocks = (persistent_blocks(p.cap_chunks) + kXcds - 1) / kXcds * kXcds;
-  if (blocks > per_xcd * kXcds) blocks = per_xcd * kXcds;
-  const dim3 grid((unsigned)blocks);
+  const dim3 grid = long_grid(p);
   if (p.weighted)
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, true>), grid, dim3(kThreads), 0, s, grad,
                        meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
@@ -417,6 +510,30 @@ hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, c
                        meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
                        meta.sorted_psw, order, list_begin, (ACC*)partials, p.T, p.B, p.D, p.C,
                        rs.G, rs.log2G, rs.P);
+  return hipGetLastError();
+}
+
+template <typename WT, int V, int PMAX>
+hipError_t long_fused_typed(const Problem& p, const RowShape& rs, void* W, float* m,
+                            const float* grad, const tbe_meta& meta, void* partials,
+                            int32_t* sched, double lr, double eps, hipStream_t s) {
+  using ACC = typename acc_of<WT>::type;
+  const int32_t* order = sched;
+  const int32_t* list_begin = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets;
+  int32_t* arrivals = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets + kXcds + 1;
+  const dim3 grid = long_grid(p);
+  if (p.weighted)
+    hipLaunchKernelGGL((bwd_long_fused_kernel<WT, V, PMAX, true>), grid, dim3(kThreads), 0, s,
+                       (WT*)W, m, grad, meta.chunk_run, meta.chunk_start, meta.run_offsets,
+                       meta.run_keys, meta.sorted_bag, meta.sorted_psw, order, list_begin,
+                       (ACC*)partials, arrivals, p.T, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
+                       (ACC)lr, (ACC)eps);
+  else
+    hipLaunchKernelGGL((bwd_long_fused_kernel<WT, V, PMAX, false>), grid, dim3(kThreads), 0, s,
+                       (WT*)W, m, grad, meta.chunk_run, meta.chunk_start, meta.run_offsets,
+                       meta.run_keys, meta.sorted_bag, meta.sorted_psw, order, list_begin,
+                       (ACC*)partials, arrivals, p.T, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
+                       (ACC)lr, (ACC)eps);
   return hipGetLastError();
 }
 
@@ -485,9 +602,22 @@ hipError_t long_for(const Problem& p, const float* grad, const tbe_meta& meta, v
 }
 
 template <typename WT>
+hipError_t long_fused_for(const Problem& p, void* W, float* m, const float* grad,
+                          const tbe_meta& meta, void* partials, int32_t* sched, double lr,
+                          double eps, hipStream_t s) {
+  const RowShape rs = grad_row_shape(p.D);
+#define CALL(VV, PP) \
+  long_fused_typed<WT, VV, PP>(p, rs, W, m, grad, meta, partials, sched, lr, eps, s)
+  TBE_DISPATCH_V(rs, CALL);
+#undef CALL
+}
+
+// The apply reduces with the row shape of the long kernel, so that the fused
+// long kernel (which reduces in the same wave that accumulated) matches it.
+template <typename WT>
 hipError_t apply_for(const Problem& p, void* W, float* m, const tbe_meta& meta,
                      const void* partials, double lr, double eps, hipStream_t s) {
-  const RowShape rs = row_shape(p.D, 8);
+  const RowShape rs = grad_row_shape(p.D);
 #define CALL(VV, PP) apply_typed<WT, VV, PP>(p, rs, W, m, meta, partials, lr, eps, s)
   TBE_DISPATCH_V(rs, CALL);
 #undef CALL
@@ -517,9 +647,10 @@ hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t*
   int32_t* bucket_of = order + p.cap_chunks;
   int32_t* hist = bucket_of + p.cap_chunks;
   int32_t* list_begin = hist + kXcds * kSchedBuckets;
+  int32_t* arrivals = list_begin + kXcds + 1;
   hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, hist, kXcds * kSchedBuckets);
   hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
-                     meta.sorted_bag, p.B, p.T, shift, hist, bucket_of);
+                     meta.sorted_bag, p.B, p.T, shift, hist, bucket_of, arrivals);
   hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, hist, list_begin);
   hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, bucket_of,
                      hist, order);
@@ -533,8 +664,21 @@ hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& 
   return long_for<float>(p, grad, meta, partials, sched, s);
 }
 
+hipError_t launch_bwd_long_fused(const Problem& p, void* W, float* m, const float* grad,
+                                 const tbe_meta& meta, void* partials, int32_t* sched, double lr,
+                                 double eps, hipStream_t s) {
+  if (p.cap_chunks == 0) return hipSuccess;
+  switch (p.wdtype) {
+    case TBE_F32: return long_fused_for<float>(p, W, m, grad, meta, partials, sched, lr, eps, s);
+    case TBE_F16: return long_fused_for<f16_t>(p, W, m, grad, meta, partials, sched, lr, eps, s);
+    case TBE_BF16: return long_fused_for<bf16_t>(p, W, m, grad, meta, partials, sched, lr, eps, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 size_t long_schedule_ints(const Problem& p) {
-  return 2 * (size_t)p.cap_chunks + kXcds * kSchedBuckets + kXcds + 1;
+  // order, bucket of each chunk, bucket counts, list starts, arrival counters
+  return 3 * (size_t)p.cap_chunks + kXcds * kSchedBuckets + kXcds + 1;
 }
 
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,

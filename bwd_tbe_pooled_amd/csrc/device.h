@@ -62,6 +62,7 @@ template <> struct vec_bytes<4> { using type = uint32_t; };
 template <> struct vec_bytes<8> { using type = uint2; };
 template <> struct vec_bytes<16> { using type = uint4; };
 template <> struct vec_bytes<32> { struct type { uint4 a, b; }; };
+template <> struct vec_bytes<64> { struct type { uint4 a, b, c, d; }; };
 
 template <typename T, int V>
 struct raw_vec {

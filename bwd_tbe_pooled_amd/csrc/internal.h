@@ -47,6 +47,8 @@ struct Problem {
   int small_splits;
   // TBE_FLAG_CHECK: where kernels that read indices report a bad one (else null)
   int32_t* err;
+  // TBE_FLAG_FUSED_LONG: long runs reduced and applied by the long kernel
+  bool fused_long;
 };
 
 tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p);
@@ -122,6 +124,9 @@ hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t*
                                 hipStream_t s);
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
                            void* partials, const int32_t* sched, hipStream_t s);
+hipError_t launch_bwd_long_fused(const Problem& p, void* W, float* m, const float* grad,
+                                 const tbe_meta& meta, void* partials, int32_t* sched, double lr,
+                                 double eps, hipStream_t s);
 size_t long_schedule_ints(const Problem& p);  // workspace ints of the chunk schedule
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
                             const void* partials, double lr, double eps, hipStream_t s);

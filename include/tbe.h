@@ -83,6 +83,16 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
                                         is read as row 0 and sets
                                         TBE_ERROR_INDEX in *desc->error_flags;
                                         no extra pass, no host synchronisation */
+#define TBE_FLAG_FUSED_LONG    0x8u  /* long runs in one launch (page 1,
+                                        backward section, the third of the
+                                        paths by segment length, figure 3):
+                                        each chunk publishes its partial with
+                                        a device-scope release and counts
+                                        itself in; the last chunk of a run
+                                        reduces the run's partials in chunk
+                                        order and applies Adagrad. Same bits
+                                        as the default two launches (chunk
+                                        partials, then apply). */
 
 /* Bits OR-ed into *tbe_desc.error_flags under TBE_FLAG_CHECK. */
 #define TBE_ERROR_INDEX 0x1u   /* some index was outside its table */
@@ -98,7 +108,9 @@ typedef enum {
     TBE_STAGE_SORT = 2,         /* radix passes                               */
     TBE_STAGE_RLE_ROUTE = 3,    /* run-length encoding and routing            */
     TBE_STAGE_BWD_SHORT = 4,    /* short runs: accumulate + Adagrad + store   */
-    TBE_STAGE_BWD_LONG = 5,     /* long-run chunks: partial sums to workspace */
+    TBE_STAGE_BWD_LONG = 5,     /* long-run chunks: partial sums to workspace
+                                   (under TBE_FLAG_FUSED_LONG also the reduce
+                                   and Adagrad of the long runs)             */
     TBE_STAGE_BWD_APPLY = 6,    /* long runs: reduce partials + Adagrad       */
     TBE_STAGE_SMALL_FWD = 7,    /* small-table contraction (forward output)   */
     TBE_STAGE_SMALL_BWD = 8,    /* small-table transposed contraction         */

@@ -16,6 +16,8 @@ from workloads import WORKLOADS, TINY, DEMO3, MEDIUM, LARGE, SMALL_TABLE, Config
 
 pytestmark = pytest.mark.gpu
 
+FUSED_LONG = 0x8  # TBE_FLAG_FUSED_LONG: long runs reduced and applied in the chunk kernel
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _need_gpu():
@@ -25,17 +27,17 @@ def _need_gpu():
 
 
 def _full_check(cfg, batch, *, meta_in_forward, backward_meta=True, S=0, C=0, m0="zeros",
-                with_pos=True):
+                with_pos=True, flags=0):
     print(f"\n[parity] {cfg.name} T={cfg.T} B={cfg.B} D={cfg.D} {cfg.dtype} N={batch.indices.size} "
-          f"S={S or 256} C={C or 256} meta_fwd={meta_in_forward} meta_bwd={backward_meta}",
-          flush=True)
+          f"S={S or 256} C={C or 256} meta_fwd={meta_in_forward} meta_bwd={backward_meta} "
+          f"flags={flags:#x}", flush=True)
     W, m = fresh_params(cfg, m0)
     W0, m0t = W.clone(), m.clone()
     keys_all, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
     uk = np.unique(keys_all)
     Wrows, mrows = host_rows(W0, m0t, uk)
     r = run_library(cfg, batch, W, m, meta_in_forward=meta_in_forward,
-                    backward_meta=backward_meta, S=S, C=C, with_pos=with_pos)
+                    backward_meta=backward_meta, S=S, C=C, with_pos=with_pos, flags=flags)
     pre, out, bw = oracle_all(cfg, batch, Wrows, mrows, uk, S or 256, C or 256)
     err = rel_err(r["out"].cpu().numpy(), out)
     assert err <= TOL[cfg.dtype], f"forward rel err {err:.3g}"
@@ -59,10 +61,11 @@ def test_tiny_metadata_reused_from_preprocess():
     _full_check(cfg, make_batch(cfg), meta_in_forward=False, backward_meta=True)
 
 
-def test_large_skewed_reduced_batch_full_compare():
+@pytest.mark.parametrize("flags", [0, FUSED_LONG], ids=["two_launch", "fused_long"])
+def test_large_skewed_reduced_batch_full_compare(flags):
     cfg = LARGE
     batch = make_batch(cfg, B=2048)
-    _full_check(batch.cfg, batch, meta_in_forward=True, backward_meta=True)
+    _full_check(batch.cfg, batch, meta_in_forward=True, backward_meta=True, flags=flags)
 
 
 @pytest.mark.parametrize("name", ["demo3_d16_f32_b4k", "t16_e1m_d128_f16_b16k"])
@@ -80,12 +83,13 @@ def test_large_skewed_reduced_batch_without_positions():
     _full_check(batch.cfg, batch, meta_in_forward=True, with_pos=False)
 
 
-def test_demo3_fp64_partials_with_small_chunks():
+@pytest.mark.parametrize("flags", [0, FUSED_LONG], ids=["two_launch", "fused_long"])
+def test_demo3_fp64_partials_with_small_chunks(flags):
     """f32 weights accumulate and keep chunk partials in f64; small S/C put
     many runs on the chunked path."""
     cfg = DEMO3
     batch = make_batch(cfg, B=1024)
-    _full_check(batch.cfg, batch, meta_in_forward=True, S=4, C=3)
+    _full_check(batch.cfg, batch, meta_in_forward=True, S=4, C=3, flags=flags)
 
 
 def test_nonzero_initial_state():
@@ -108,8 +112,9 @@ def _custom(T, B, D, rows, dtype, lengths, indices, psw=None, seed=0):
                       psw=None if psw is None else np.asarray(psw, dtype=np.float32), grad=grad)
 
 
+@pytest.mark.parametrize("flags", [0, FUSED_LONG], ids=["two_launch", "fused_long"])
 @pytest.mark.parametrize("sl", [255, 256, 257, 511, 512, 513])
-def test_segment_lengths_around_the_threshold(sl):
+def test_segment_lengths_around_the_threshold(sl, flags):
     """One hot row hit exactly sl times, spread over bags, among cold rows."""
     rng = np.random.default_rng(sl)
     T, B, D = 2, 600, 16
@@ -121,7 +126,7 @@ def test_segment_lengths_around_the_threshold(sl):
     idx[hot] = 4242
     cfg, batch = _custom(T, B, D, rows, "f16" if sl % 2 else "bf16", lengths, idx,
                          psw=rng.random(N), seed=sl)
-    r, pre = _full_check(cfg, batch, meta_in_forward=True)
+    r, pre = _full_check(cfg, batch, meta_in_forward=True, flags=flags)
     u = int(np.searchsorted(pre["run_keys"], 4242))
     assert pre["run_keys"][u] == 4242 and np.diff(pre["run_offsets"])[u] == sl
     assert (u in pre["long_runs"]) == (sl >= 256)
