@@ -77,6 +77,16 @@ _lib.tbe_backward_adagrad.restype = ctypes.c_int
 _lib.tbe_backward_adagrad.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, _P, _P,
                                       ctypes.c_int64, _P, ctypes.POINTER(tbe_meta),
                                       ctypes.c_double, ctypes.c_double, _P, ctypes.c_size_t, _P]
+_lib.tbe_workspace_bytes_i64.restype = ctypes.c_size_t
+_lib.tbe_workspace_bytes_i64.argtypes = [ctypes.POINTER(tbe_desc), ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int]
+_lib.tbe_forward_i64.restype = ctypes.c_int
+_lib.tbe_forward_i64.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, ctypes.c_int64, _P, _P,
+                                 _P, ctypes.c_size_t, _P]
+_lib.tbe_backward_adagrad_i64.restype = ctypes.c_int
+_lib.tbe_backward_adagrad_i64.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, _P, _P,
+                                          ctypes.c_int64, _P, ctypes.c_double, ctypes.c_double,
+                                          _P, ctypes.c_size_t, _P]
 _lib.tbe_timer_create.restype = ctypes.c_int
 _lib.tbe_timer_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
 _lib.tbe_timer_reset.restype = ctypes.c_int
@@ -226,6 +236,42 @@ def tbe_backward_adagrad(desc: Desc, W, momentum, grad_out, indices, offsets, ps
                                      _stream(stream)), "tbe_backward_adagrad")
 
 
+# --- int64 indices and offsets ----------------------------------------------------
+def tbe_workspace_bytes_i64(desc: Desc, N: int, weighted: bool, op: int) -> int:
+    return int(_lib.tbe_workspace_bytes_i64(desc.ref, int(N), int(bool(weighted)), int(op)))
+
+
+def workspace_i64(desc: Desc, N: int, weighted: bool, op: int, device="cuda"):
+    nbytes = tbe_workspace_bytes_i64(desc, N, weighted, op)
+    if nbytes == 0:
+        raise TbeError(TBE_ERR_ARG, "tbe_workspace_bytes_i64")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _need_i64(*tensors):
+    for t in tensors:
+        if t is not None and t.dtype != torch.int64:
+            raise TypeError(f"the _i64 entry points take int64 indices and offsets, got {t.dtype}")
+
+
+def tbe_forward_i64(desc: Desc, W, indices, offsets, psw, out, ws, stream=None):
+    _need_i64(indices, offsets)
+    N = indices.numel()
+    _check(_lib.tbe_forward_i64(desc.ref, _ptr(W), _ptr(indices), _ptr(offsets), N, _ptr(psw),
+                                _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)), "tbe_forward_i64")
+
+
+def tbe_backward_adagrad_i64(desc: Desc, W, momentum, grad_out, indices, offsets, psw,
+                             lr: float, eps: float, ws, stream=None):
+    _need_i64(indices, offsets)
+    N = indices.numel()
+    _check(_lib.tbe_backward_adagrad_i64(desc.ref, _ptr(W), _ptr(momentum), _ptr(grad_out),
+                                         _ptr(indices), _ptr(offsets), N, _ptr(psw), float(lr),
+                                         float(eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                         _stream(stream)), "tbe_backward_adagrad_i64")
+
+
 # --- stage timer -----------------------------------------------------------------
 class Timer:
     def __init__(self, capacity: int = 256):
@@ -252,5 +298,6 @@ class Timer:
 def exported_symbols() -> list:
     """Names the library exports from include/tbe.h (used by host tests)."""
     return ["tbe_status_str", "tbe_last_error", "tbe_select_path", "tbe_meta_capacity", "tbe_workspace_bytes",
-            "tbe_forward", "tbe_preprocess", "tbe_backward_adagrad", "tbe_timer_create",
+            "tbe_forward", "tbe_preprocess", "tbe_backward_adagrad", "tbe_workspace_bytes_i64",
+            "tbe_forward_i64", "tbe_backward_adagrad_i64", "tbe_timer_create",
             "tbe_timer_reset", "tbe_timer_read", "tbe_timer_destroy"]

@@ -29,6 +29,8 @@ RowShape row_shape(int D, int max_v) {
   return r;
 }
 
+constexpr int64_t kI32Lim = (int64_t(1) << 31) - 1;
+
 static bool small_eligible(const tbe_desc* d, int64_t N, int weighted, int64_t max_rows) {
   // Page 1, checklist item 2: E <= 64, 64 <= D <= 128, L >= 64, f16, unweighted.
   if (d->flags & TBE_FLAG_FORCE_GENERIC) return false;
@@ -40,8 +42,10 @@ static bool small_eligible(const tbe_desc* d, int64_t N, int weighted, int64_t m
   return N >= 64 * nbags;  // average bag length N / (T*B) >= 64
 }
 
-tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) {
-  if (!d || !p || !d->rows) return TBE_ERR_ARG;
+// Checks shared by the int32 and int64 entry points: everything but the
+// int32 size limits. Sets *sum and *mx to the sum and maximum of the rows.
+static tbe_status check_desc(const tbe_desc* d, int64_t N, int64_t* sum, int64_t* mx) {
+  if (!d || !d->rows) return TBE_ERR_ARG;
   if (d->T < 1 || d->D < 1 || d->B < 0 || N < 0) return TBE_ERR_ARG;
   if (d->wdtype != TBE_F32 && d->wdtype != TBE_F16 && d->wdtype != TBE_BF16) return TBE_ERR_UNSUPPORTED;
   if (d->flags &
@@ -49,17 +53,42 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
     return TBE_ERR_ARG;
   if ((d->flags & TBE_FLAG_CHECK) && !d->error_flags) return TBE_ERR_ARG;
   if (d->short_max < 0 || d->chunk < 0) return TBE_ERR_ARG;
-  int64_t sum = 0, mx = 0;
+  int64_t s = 0, m = 0;
   for (int32_t t = 0; t < d->T; ++t) {
     if (d->rows[t] < 1) return TBE_ERR_ARG;
-    sum += d->rows[t];
-    mx = std::max<int64_t>(mx, d->rows[t]);
-    if (sum >= (int64_t(1) << 31)) return TBE_ERR_UNSUPPORTED;  // int32 keys (checklist item 6)
+    if (d->rows[t] >= kI32Lim) return TBE_ERR_UNSUPPORTED;  // in-table rows stay int32
+    s += d->rows[t];
+    m = std::max<int64_t>(m, d->rows[t]);
   }
-  const int64_t lim = (int64_t(1) << 31) - 1;
-  if (N >= lim || (int64_t)d->T * d->B >= lim) return TBE_ERR_UNSUPPORTED;
   const RowShape rs = row_shape(d->D, 8);
   if (rs.P > 4) return TBE_ERR_UNSUPPORTED;
+  *sum = s;
+  *mx = m;
+  return TBE_OK;
+}
+
+// Sizes derived from T, D, B, N, nbags, sum_rows, max_rows, S and C.
+static void derive_sizes(Problem* p) {
+  int nbits = 0;
+  while ((int64_t(1) << nbits) < p->max_rows) ++nbits;
+  p->sort_passes = std::max(1, (nbits + 6) / 7);  // digits of at most 7 bits
+  p->sort_bits = std::max(1, (nbits + p->sort_passes - 1) / p->sort_passes);
+  p->sort_tiles_max = (p->N + kSortTile - 1) / kSortTile + p->T;
+  p->cap_runs = std::min<int64_t>(p->N, p->sum_rows);
+  p->cap_long = p->N / p->S;
+  p->cap_chunks = p->cap_long ? p->N / p->C + p->cap_long : 0;
+  p->small_splits = small_splits_for(p->T, p->B);
+  p->ld = (int64_t)p->T * p->D;
+}
+
+tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) {
+  if (!p) return TBE_ERR_ARG;
+  int64_t sum = 0, mx = 0;
+  const tbe_status st = check_desc(d, N, &sum, &mx);
+  if (st != TBE_OK) return st;
+  // int32 keys, positions and bags (checklist item 6); larger problems use
+  // the int64 entry points
+  if (sum >= kI32Lim || N >= kI32Lim || (int64_t)d->T * d->B >= kI32Lim) return TBE_ERR_UNSUPPORTED;
 
   p->T = d->T;
   p->D = d->D;
@@ -73,15 +102,7 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   p->S = d->short_max ? d->short_max : kDefaultShortMax;
   p->C = d->chunk ? d->chunk : kDefaultChunk;
   p->path = small_eligible(d, N, weighted, mx) ? TBE_PATH_SMALL_TABLE : TBE_PATH_GENERIC;
-  int nbits = 0;
-  while ((int64_t(1) << nbits) < mx) ++nbits;
-  p->sort_passes = std::max(1, (nbits + 6) / 7);  // digits of at most 7 bits
-  p->sort_bits = std::max(1, (nbits + p->sort_passes - 1) / p->sort_passes);
-  p->sort_tiles_max = (N + kSortTile - 1) / kSortTile + d->T;
-  p->cap_runs = std::min<int64_t>(N, sum);
-  p->cap_long = N / p->S;
-  p->cap_chunks = p->cap_long ? N / p->C + p->cap_long : 0;
-  p->small_splits = small_splits_for(d->T, d->B);
+  derive_sizes(p);
   p->err = (d->flags & TBE_FLAG_CHECK) ? d->error_flags : nullptr;
   p->fused_long = (d->flags & TBE_FLAG_FUSED_LONG) != 0;
   return TBE_OK;
@@ -312,6 +333,279 @@ tbe_status check_ws(const Problem& p, tbe_op op, void* ws, size_t ws_bytes, WsLa
   return TBE_OK;
 }
 
+tbe_status forward_impl(const tbe_desc* desc, const Problem& p, const void* W,
+                        const int32_t* indices, const int32_t* offsets, const float* psw,
+                        float* out, tbe_meta* meta, void* ws, size_t ws_bytes, hipStream_t s) {
+  tbe_status st;
+  const tbe_op op = meta ? TBE_OP_FORWARD_PREPROCESS : TBE_OP_FORWARD;
+  if (meta && !(p.path == TBE_PATH_SMALL_TABLE ? meta_ok_small(meta) : meta_ok_generic(meta, p.weighted)))
+    return TBE_ERR_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, op, ws, ws_bytes, &L)) != TBE_OK) return st;
+  if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
+  const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
+  if (p.path == TBE_PATH_SMALL_TABLE) {
+    int32_t* counts = meta ? meta->counts : at<int32_t>(ws, L.flags) + 8;
+    uint8_t* hist = meta ? meta->hist : at<uint8_t>(ws, L.hist);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+    TBE_TRY_HIP(launch_small_count(p, indices, offsets, tinfo, hist, counts, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    TBE_TRY_HIP(launch_small_pool(p, W, indices, offsets, tinfo, out, hist, counts, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
+    return TBE_OK;
+  }
+  timer_begin(desc->timer, TBE_STAGE_FWD_POOL, s);
+  TBE_TRY_HIP(launch_forward_pool(p, W, indices, offsets, psw, tinfo, out, s));
+  timer_end(desc->timer, TBE_STAGE_FWD_POOL, s);
+  if (meta) return run_preprocess(desc, p, indices, offsets, psw, *meta, ws, L, s);
+  return TBE_OK;
+}
+
+
+tbe_status backward_impl(const tbe_desc* desc, const Problem& p, void* W, float* momentum,
+                         const float* grad_out, const int32_t* indices, const int32_t* offsets,
+                         const float* psw, const tbe_meta* meta, double lr, double eps, void* ws,
+                         size_t ws_bytes, hipStream_t s) {
+  tbe_status st;
+  const tbe_op op = meta ? TBE_OP_BACKWARD : TBE_OP_BACKWARD_SELF;
+  if (meta && !(p.path == TBE_PATH_SMALL_TABLE ? meta_ok_small(meta) : meta_ok_generic(meta, p.weighted)))
+    return TBE_ERR_ARG;
+  WsLayout L;
+  if ((st = check_ws(p, op, ws, ws_bytes, &L)) != TBE_OK) return st;
+  if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
+  const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
+  tbe_meta m = meta ? *meta : carve_meta(ws, L);
+
+  if (p.path == TBE_PATH_SMALL_TABLE) {
+    if (!meta) {
+      timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+      TBE_TRY_HIP(launch_small_count(p, indices, offsets, tinfo, m.hist, m.counts, s));
+      timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
+    }
+    float* parts = at<float>(ws, L.partials);
+    int32_t* pcounts = at<int32_t>(ws, L.part_counts);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_BWD, s);
+    TBE_TRY_HIP(launch_small_backward(p, grad_out, m.hist, m.counts, indices, offsets, parts,
+                                      pcounts, tinfo, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_BWD, s);
+    timer_begin(desc->timer, TBE_STAGE_SMALL_APPLY, s);
+    TBE_TRY_HIP(launch_small_apply(p, W, momentum, tinfo, parts, pcounts, lr, eps, s));
+    timer_end(desc->timer, TBE_STAGE_SMALL_APPLY, s);
+    return TBE_OK;
+  }
+
+  if (!meta) {
+    if ((st = run_preprocess(desc, p, indices, offsets, psw, m, ws, L, s)) != TBE_OK) return st;
+  }
+  void* parts = at<void>(ws, L.partials);
+  timer_begin(desc->timer, TBE_STAGE_BWD_SHORT, s);
+  TBE_TRY_HIP(launch_bwd_short(p, W, momentum, grad_out, m, tinfo, lr, eps, s));
+  timer_end(desc->timer, TBE_STAGE_BWD_SHORT, s);
+  timer_begin(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
+  TBE_TRY_HIP(launch_long_schedule(p, m, at<int32_t>(ws, L.sched), s));
+  timer_end(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
+  timer_begin(desc->timer, TBE_STAGE_BWD_LONG, s);
+  if (p.fused_long) {
+    TBE_TRY_HIP(launch_bwd_long_fused(p, W, momentum, grad_out, m, parts,
+                                      at<int32_t>(ws, L.sched), lr, eps, s));
+    timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
+    return TBE_OK;
+  }
+  TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, at<int32_t>(ws, L.sched), s));
+  timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
+  timer_begin(desc->timer, TBE_STAGE_BWD_APPLY, s);
+  TBE_TRY_HIP(launch_bwd_apply(p, W, momentum, m, parts, lr, eps, s));
+  timer_end(desc->timer, TBE_STAGE_BWD_APPLY, s);
+  return TBE_OK;
+}
+
+
+// --- int64 indices and offsets ---------------------------------------------
+// A call with int64 index arrays runs as a sequence of calls over groups of
+// consecutive tables, each small enough for int32 keys, positions and bags
+// (page 1, checklist item 6: int32 wherever the linearized range allows it).
+// Every step of the method works table by table, so the split changes no
+// result. The groups follow from where each table's lookups begin, which the
+// host reads back (T+1 values, one synchronisation per call).
+
+struct TableGroup {
+  int32_t t0, t1;     // tables [t0, t1)
+  int64_t base, n;    // lookups [base, base + n)
+};
+
+bool small_possible(const tbe_desc* d, int weighted) {
+  if ((d->flags & TBE_FLAG_FORCE_GENERIC) || weighted || d->wdtype != TBE_F16) return false;
+  if (d->D < 64 || d->D > 128) return false;
+  for (int32_t t = 0; t < d->T; ++t)
+    if (d->rows[t] <= kSmallE) return true;
+  return false;
+}
+
+// A problem at least as large, in every size the workspace depends on, as
+// any group of this call.
+Problem bound_problem(const tbe_desc* d, int64_t N, int weighted, int64_t sum, int64_t mx,
+                      int path) {
+  Problem p{};
+  p.T = d->T;
+  p.D = d->D;
+  p.B = d->B;
+  p.N = std::min<int64_t>(N, kI32Lim - 1);
+  p.nbags = std::min<int64_t>((int64_t)d->T * d->B, kI32Lim - 1);
+  p.sum_rows = std::min<int64_t>(sum, kI32Lim - 1);
+  p.max_rows = mx;
+  p.wdtype = d->wdtype;
+  p.weighted = weighted != 0;
+  p.S = d->short_max ? d->short_max : kDefaultShortMax;
+  p.C = d->chunk ? d->chunk : kDefaultChunk;
+  p.path = path;
+  derive_sizes(&p);
+  p.sort_bits = 7;  // a group with fewer rows can take fewer, wider digits
+  if (path == TBE_PATH_SMALL_TABLE) {  // split partials: T_g * splits(T_g) at most
+    int64_t parts = 0;
+    for (int32_t tg = 1; tg <= d->T; ++tg)
+      parts = std::max<int64_t>(parts, (int64_t)tg * small_splits_for(tg, d->B));
+    p.small_splits = (int)((parts + d->T - 1) / d->T);
+  }
+  return p;
+}
+
+struct I64Layout {
+  size_t bounds, idx32, off32, group, total;
+};
+
+I64Layout i64_layout(const tbe_desc* d, int64_t N, int weighted, tbe_op op, int64_t sum,
+                     int64_t mx) {
+  I64Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  };
+  L.bounds = take(sizeof(int64_t) * ((size_t)d->T + 1));
+  L.idx32 = take(sizeof(int32_t) * (size_t)std::min<int64_t>(N, kI32Lim - 1));
+  L.off32 = take(sizeof(int32_t) * ((size_t)std::min<int64_t>((int64_t)d->T * d->B, kI32Lim - 1) + 1));
+  size_t g = ws_layout(bound_problem(d, N, weighted, sum, mx, TBE_PATH_GENERIC), op).total;
+  if (small_possible(d, weighted))
+    g = std::max(g, ws_layout(bound_problem(d, N, weighted, sum, mx, TBE_PATH_SMALL_TABLE), op).total);
+  L.group = take(g);
+  L.total = off;
+  return L;
+}
+
+tbe_status plan_groups(const tbe_desc* d, const std::vector<int64_t>& tb, int64_t N,
+                       std::vector<TableGroup>* out) {
+  const int32_t T = d->T;
+  if (tb[0] != 0 || tb[T] != N) return TBE_ERR_INDEX_RANGE;
+  TableGroup g{0, 0, 0, 0};
+  int64_t rows = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    const int64_t n = tb[t + 1] - tb[t];
+    if (n < 0) return TBE_ERR_INDEX_RANGE;
+    if (n >= kI32Lim || (int64_t)d->B >= kI32Lim) return TBE_ERR_UNSUPPORTED;
+    const bool fits = rows + d->rows[t] < kI32Lim && g.n + n < kI32Lim &&
+                      (int64_t)(g.t1 - g.t0 + 1) * d->B < kI32Lim;
+    if (g.t1 > g.t0 && !fits) {
+      out->push_back(g);
+      g = TableGroup{t, t, tb[t], 0};
+      rows = 0;
+    }
+    g.t1 = t + 1;
+    g.n += n;
+    rows += d->rows[t];
+  }
+  out->push_back(g);
+  return TBE_OK;
+}
+
+// The description of one group, and its problem with the whole call's row
+// stride for the pooled output and the upstream gradient.
+tbe_status group_problem(const tbe_desc* d, const TableGroup& g, int weighted, tbe_desc* sub,
+                         Problem* p) {
+  *sub = *d;
+  sub->T = g.t1 - g.t0;
+  sub->rows = d->rows + g.t0;
+  tbe_status st = make_problem(sub, g.n, weighted, p);
+  if (st != TBE_OK) return st;
+  // the small-table backward keeps 8-row gradient offsets in int32
+  if (p->path == TBE_PATH_SMALL_TABLE && (int64_t)d->T * d->D >= (int64_t(1) << 27)) {
+    sub->flags |= TBE_FLAG_FORCE_GENERIC;
+    if ((st = make_problem(sub, g.n, weighted, p)) != TBE_OK) return st;
+  }
+  p->ld = (int64_t)d->T * d->D;
+  return TBE_OK;
+}
+
+tbe_status run_i64(bool backward, const tbe_desc* d, void* W, float* momentum,
+                   const float* grad_out, const int64_t* indices, const int64_t* offsets,
+                   int64_t N, const float* psw, float* out, double lr, double eps, void* ws,
+                   size_t ws_bytes, hipStream_t s) {
+  int64_t sum = 0, mx = 0;
+  tbe_status st = check_desc(d, N, &sum, &mx);
+  if (st != TBE_OK) return st;
+  const int weighted = psw != nullptr;
+  const int64_t nbags = (int64_t)d->T * d->B;
+  if (!W || !offsets || (!indices && N > 0)) return TBE_ERR_ARG;
+  if (backward && (!momentum || (!grad_out && nbags > 0) || !(lr >= 0.0) || !(eps >= 0.0)))
+    return TBE_ERR_ARG;
+  if (!backward && !out && nbags > 0) return TBE_ERR_ARG;
+  const tbe_op op = backward ? TBE_OP_BACKWARD_SELF : TBE_OP_FORWARD;
+  const I64Layout L = i64_layout(d, N, weighted, op, sum, mx);
+  if (!ws || ws_bytes < L.total) return TBE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return TBE_ERR_ARG;
+
+  (void)hipGetLastError();
+  int64_t* dbounds = at<int64_t>(ws, L.bounds);
+  TBE_TRY_HIP(launch_table_bounds(offsets, d->T, d->B, dbounds, s));
+  std::vector<int64_t> tb((size_t)d->T + 1);
+  TBE_TRY_HIP(hipMemcpyAsync(tb.data(), dbounds, sizeof(int64_t) * tb.size(),
+                             hipMemcpyDeviceToHost, s));
+  TBE_TRY_HIP(hipStreamSynchronize(s));
+  std::vector<TableGroup> groups;
+  if ((st = plan_groups(d, tb, N, &groups)) != TBE_OK) return st;
+  std::vector<int64_t> roff((size_t)d->T + 1, 0);
+  for (int32_t t = 0; t < d->T; ++t) roff[t + 1] = roff[t] + d->rows[t];
+
+  int32_t* idx32 = at<int32_t>(ws, L.idx32);
+  int32_t* off32 = at<int32_t>(ws, L.off32);
+  void* gws = at<char>(ws, L.group);
+  const size_t gws_bytes = L.total - L.group;
+  auto narrow = [&](const TableGroup& g, int32_t Tg) {
+    return launch_narrow(indices ? indices + g.base : nullptr, g.n, offsets + (int64_t)g.t0 * d->B,
+                         (int64_t)Tg * d->B + 1, g.base, idx32, off32, s);
+  };
+  if (d->flags & TBE_FLAG_VALIDATE) {  // every group is checked before any work
+    for (const TableGroup& g : groups) {
+      tbe_desc sub;
+      Problem p;
+      if ((st = group_problem(d, g, weighted, &sub, &p)) != TBE_OK) return st;
+      TBE_TRY_HIP(narrow(g, sub.T));
+      WsLayout Lg;
+      if ((st = check_ws(p, op, gws, gws_bytes, &Lg)) != TBE_OK) return st;
+      if ((st = prologue(&sub, p, idx32, off32, gws, Lg, s)) != TBE_OK) return st;
+    }
+  }
+  const size_t wbytes = d->wdtype == TBE_F32 ? 4 : 2;
+  for (const TableGroup& g : groups) {
+    tbe_desc sub;
+    Problem p;
+    if ((st = group_problem(d, g, weighted, &sub, &p)) != TBE_OK) return st;
+    sub.flags &= ~TBE_FLAG_VALIDATE;
+    TBE_TRY_HIP(narrow(g, sub.T));
+    char* Wg = static_cast<char*>(W) + roff[g.t0] * d->D * (int64_t)wbytes;
+    const float* psw_g = psw ? psw + g.base : nullptr;
+    if (backward)
+      st = backward_impl(&sub, p, Wg, momentum + roff[g.t0], grad_out + (int64_t)g.t0 * d->D,
+                         idx32, off32, psw_g, nullptr, lr, eps, gws, gws_bytes, s);
+    else
+      st = forward_impl(&sub, p, Wg, idx32, off32, psw_g, out + (int64_t)g.t0 * d->D, nullptr,
+                        gws, gws_bytes, s);
+    if (st != TBE_OK) return st;
+  }
+  return TBE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,30 +654,8 @@ tbe_status tbe_forward(const tbe_desc* desc, const void* W, const int32_t* indic
   tbe_status st = make_problem(desc, N, psw != nullptr, &p);
   if (st != TBE_OK) return st;
   if (!W || !offsets || (!indices && N > 0) || (!out && p.nbags > 0)) return TBE_ERR_ARG;
-  const tbe_op op = meta ? TBE_OP_FORWARD_PREPROCESS : TBE_OP_FORWARD;
-  if (meta && !(p.path == TBE_PATH_SMALL_TABLE ? meta_ok_small(meta) : meta_ok_generic(meta, p.weighted)))
-    return TBE_ERR_ARG;
-  WsLayout L;
-  if ((st = check_ws(p, op, ws, ws_bytes, &L)) != TBE_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
-  const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
-  if (p.path == TBE_PATH_SMALL_TABLE) {
-    int32_t* counts = meta ? meta->counts : at<int32_t>(ws, L.flags) + 8;
-    uint8_t* hist = meta ? meta->hist : at<uint8_t>(ws, L.hist);
-    timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
-    TBE_TRY_HIP(launch_small_count(p, indices, offsets, tinfo, hist, counts, s));
-    timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
-    timer_begin(desc->timer, TBE_STAGE_SMALL_FWD, s);
-    TBE_TRY_HIP(launch_small_pool(p, W, indices, offsets, tinfo, out, hist, counts, s));
-    timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
-    return TBE_OK;
-  }
-  timer_begin(desc->timer, TBE_STAGE_FWD_POOL, s);
-  TBE_TRY_HIP(launch_forward_pool(p, W, indices, offsets, psw, tinfo, out, s));
-  timer_end(desc->timer, TBE_STAGE_FWD_POOL, s);
-  if (meta) return run_preprocess(desc, p, indices, offsets, psw, *meta, ws, L, s);
-  return TBE_OK;
+  return forward_impl(desc, p, W, indices, offsets, psw, out, meta, ws, ws_bytes,
+                      static_cast<hipStream_t>(stream));
 }
 
 tbe_status tbe_preprocess(const tbe_desc* desc, const int32_t* indices, const int32_t* offsets,
@@ -420,57 +692,31 @@ tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
   if (!W || !momentum || (!grad_out && p.nbags > 0) || !offsets || (!indices && N > 0))
     return TBE_ERR_ARG;
   if (!(lr >= 0.0) || !(eps >= 0.0)) return TBE_ERR_ARG;
-  const tbe_op op = meta ? TBE_OP_BACKWARD : TBE_OP_BACKWARD_SELF;
-  if (meta && !(p.path == TBE_PATH_SMALL_TABLE ? meta_ok_small(meta) : meta_ok_generic(meta, p.weighted)))
-    return TBE_ERR_ARG;
-  WsLayout L;
-  if ((st = check_ws(p, op, ws, ws_bytes, &L)) != TBE_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = prologue(desc, p, indices, offsets, ws, L, s)) != TBE_OK) return st;
-  const int32_t* tinfo = at<int32_t>(ws, L.tinfo);
-  tbe_meta m = meta ? *meta : carve_meta(ws, L);
+  return backward_impl(desc, p, W, momentum, grad_out, indices, offsets, psw, meta, lr, eps, ws,
+                       ws_bytes, static_cast<hipStream_t>(stream));
+}
 
-  if (p.path == TBE_PATH_SMALL_TABLE) {
-    if (!meta) {
-      timer_begin(desc->timer, TBE_STAGE_SMALL_COUNT, s);
-      TBE_TRY_HIP(launch_small_count(p, indices, offsets, tinfo, m.hist, m.counts, s));
-      timer_end(desc->timer, TBE_STAGE_SMALL_COUNT, s);
-    }
-    float* parts = at<float>(ws, L.partials);
-    int32_t* pcounts = at<int32_t>(ws, L.part_counts);
-    timer_begin(desc->timer, TBE_STAGE_SMALL_BWD, s);
-    TBE_TRY_HIP(launch_small_backward(p, grad_out, m.hist, m.counts, indices, offsets, parts,
-                                      pcounts, tinfo, s));
-    timer_end(desc->timer, TBE_STAGE_SMALL_BWD, s);
-    timer_begin(desc->timer, TBE_STAGE_SMALL_APPLY, s);
-    TBE_TRY_HIP(launch_small_apply(p, W, momentum, tinfo, parts, pcounts, lr, eps, s));
-    timer_end(desc->timer, TBE_STAGE_SMALL_APPLY, s);
-    return TBE_OK;
-  }
+size_t tbe_workspace_bytes_i64(const tbe_desc* desc, int64_t N, int32_t weighted, tbe_op op) {
+  if (op != TBE_OP_FORWARD && op != TBE_OP_BACKWARD_SELF) return 0;
+  int64_t sum = 0, mx = 0;
+  if (check_desc(desc, N, &sum, &mx) != TBE_OK) return 0;
+  return i64_layout(desc, N, weighted, op, sum, mx).total;
+}
 
-  if (!meta) {
-    if ((st = run_preprocess(desc, p, indices, offsets, psw, m, ws, L, s)) != TBE_OK) return st;
-  }
-  void* parts = at<void>(ws, L.partials);
-  timer_begin(desc->timer, TBE_STAGE_BWD_SHORT, s);
-  TBE_TRY_HIP(launch_bwd_short(p, W, momentum, grad_out, m, tinfo, lr, eps, s));
-  timer_end(desc->timer, TBE_STAGE_BWD_SHORT, s);
-  timer_begin(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
-  TBE_TRY_HIP(launch_long_schedule(p, m, at<int32_t>(ws, L.sched), s));
-  timer_end(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
-  timer_begin(desc->timer, TBE_STAGE_BWD_LONG, s);
-  if (p.fused_long) {
-    TBE_TRY_HIP(launch_bwd_long_fused(p, W, momentum, grad_out, m, parts,
-                                      at<int32_t>(ws, L.sched), lr, eps, s));
-    timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
-    return TBE_OK;
-  }
-  TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, at<int32_t>(ws, L.sched), s));
-  timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
-  timer_begin(desc->timer, TBE_STAGE_BWD_APPLY, s);
-  TBE_TRY_HIP(launch_bwd_apply(p, W, momentum, m, parts, lr, eps, s));
-  timer_end(desc->timer, TBE_STAGE_BWD_APPLY, s);
-  return TBE_OK;
+tbe_status tbe_forward_i64(const tbe_desc* desc, const void* W, const int64_t* indices,
+                           const int64_t* offsets, int64_t N, const float* psw, float* out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  return run_i64(false, desc, const_cast<void*>(W), nullptr, nullptr, indices, offsets, N, psw,
+                 out, 0.0, 0.0, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+tbe_status tbe_backward_adagrad_i64(const tbe_desc* desc, void* W, float* momentum,
+                                    const float* grad_out, const int64_t* indices,
+                                    const int64_t* offsets, int64_t N, const float* psw,
+                                    double lr, double eps, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return run_i64(true, desc, W, momentum, grad_out, indices, offsets, N, psw, nullptr, lr, eps,
+                 ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 tbe_status tbe_timer_create(int32_t capacity, tbe_timer** out) {

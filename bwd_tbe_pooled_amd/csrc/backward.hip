@@ -67,7 +67,7 @@ template <int V, int PMAX, typename ACC, bool WEIGHTED>
 __device__ __forceinline__ void wave_accumulate(const float* __restrict__ grad,
                                                 const int32_t* __restrict__ sorted_bag,
                                                 const float* __restrict__ sorted_psw, int32_t k0,
-                                                int32_t k1, int32_t T, int32_t B, int32_t D,
+                                                int32_t k1, int64_t ld, int32_t B, int32_t D,
                                                 int G, int log2G, int P, ACC (&acc)[PMAX][V]) {
   using GRAW = typename raw_vec<float, V>::type;
   constexpr int UNROLL = PMAX <= 2 ? 4 : 1;
@@ -98,7 +98,7 @@ __device__ __forceinline__ void wave_accumulate(const float* __restrict__ grad,
         } else {
           sc[uu] = ok ? 1.f : 0.f;
         }
-        const float* row = gt + (int64_t)(ok ? bag - tB : 0) * T * D;
+        const float* row = gt + (int64_t)(ok ? bag - tB : 0) * ld;
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
           const int e = (p * G + col) * V;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
     WT* __restrict__ W, float* __restrict__ mom, const float* __restrict__ grad,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ short_runs,
     const int32_t* __restrict__ run_keys, const int32_t* __restrict__ run_offsets,
-    const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw, int32_t T,
+    const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw, int64_t ld,
     int32_t B, int32_t D, int32_t G, int32_t log2G, int32_t P,
     typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
   using ACC = typename acc_of<WT>::type;
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
       GRAW buf[kTinyMax][PMAX];
 #pragma unroll
       for (int r = 0; r < kTinyMax; ++r) {
-        const float* row = gt + (int64_t)(bag[r] - t * B) * T * D;
+        const float* row = gt + (int64_t)(bag[r] - t * B) * ld;
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
           const int ee = (p * G + col) * V;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
       RowState<WT, V, PMAX> st;
       if (slot == 0) load_row_state<WT, V, PMAX>(W + (int64_t)rkey * D, mom + rkey, col, G, P, D, st);
       ACC acc[PMAX][V];
-      wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, a, e, T, B, D, G,
+      wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, a, e, ld, B, D, G,
                                               log2G, P, acc);
       if (slot == 0)
         apply_row_state<WT, ACC, V, PMAX>(W + (int64_t)rkey * D, mom + rkey, st, acc, col, G, P,
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ run_offsets,
     const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw,
     const int32_t* __restrict__ order, const int32_t* __restrict__ list_begin,
-    ACC* __restrict__ partials, int32_t T, int32_t B, int32_t D, int32_t C, int32_t G,
+    ACC* __restrict__ partials, int64_t ld, int32_t B, int32_t D, int32_t C, int32_t G,
     int32_t log2G, int32_t P) {
   const int lane = lane_id();
   const int slot = lane >> log2G;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
     const int32_t kend = run_offsets[u + 1];
     const int32_t k1 = k0 + C < kend ? k0 + C : kend;
     ACC acc[PMAX][V];
-    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, T, B, D, G,
+    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, ld, B, D, G,
                                             log2G, P, acc);
     if (slot == 0) {
       ACC* out = partials + (int64_t)c * D;
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
     const int32_t* __restrict__ run_offsets, const int32_t* __restrict__ run_keys,
     const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw,
     const int32_t* __restrict__ order, const int32_t* __restrict__ list_begin,
-    typename acc_of<WT>::type* __restrict__ partials, int32_t* __restrict__ arrivals, int32_t T,
+    typename acc_of<WT>::type* __restrict__ partials, int32_t* __restrict__ arrivals, int64_t ld,
     int32_t B, int32_t D, int32_t C, int32_t G, int32_t log2G, int32_t P,
     typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
   using ACC = typename acc_of<WT>::type;
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
     const int32_t kend = run_offsets[u + 1];
     const int32_t k1 = k0 + C < kend ? k0 + C : kend;
     ACC acc[PMAX][V];
-    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, T, B, D, G,
+    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, ld, B, D, G,
                                             log2G, P, acc);
     if (slot == 0) {
       ACC* out = partials + (int64_t)c * D;
@@ -472,12 +472,12 @@ hipError_t short_typed(const Problem& p, const RowShape& rs, void* W, float* m, 
   if (p.weighted)
     hipLaunchKernelGGL((bwd_short_kernel<WT, V, PMAX, true>), grid, dim3(kThreads), 0, s, (WT*)W, m,
                        grad, meta.counts, meta.short_runs, meta.run_keys, meta.run_offsets,
-                       meta.sorted_bag, meta.sorted_psw, p.T, p.B, p.D, rs.G, rs.log2G, rs.P,
+                       meta.sorted_bag, meta.sorted_psw, p.ld, p.B, p.D, rs.G, rs.log2G, rs.P,
                        (ACC)lr, (ACC)eps);
   else
     hipLaunchKernelGGL((bwd_short_kernel<WT, V, PMAX, false>), grid, dim3(kThreads), 0, s, (WT*)W,
                        m, grad, meta.counts, meta.short_runs, meta.run_keys, meta.run_offsets,
-                       meta.sorted_bag, meta.sorted_psw, p.T, p.B, p.D, rs.G, rs.log2G, rs.P,
+                       meta.sorted_bag, meta.sorted_psw, p.ld, p.B, p.D, rs.G, rs.log2G, rs.P,
                        (ACC)lr, (ACC)eps);
   return hipGetLastError();
 }
@@ -503,12 +503,12 @@ hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, c
   if (p.weighted)
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, true>), grid, dim3(kThreads), 0, s, grad,
                        meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
-                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.T, p.B, p.D, p.C,
+                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.ld, p.B, p.D, p.C,
                        rs.G, rs.log2G, rs.P);
   else
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, false>), grid, dim3(kThreads), 0, s, grad,
                        meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
-                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.T, p.B, p.D, p.C,
+                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.ld, p.B, p.D, p.C,
                        rs.G, rs.log2G, rs.P);
   return hipGetLastError();
 }
@@ -526,13 +526,13 @@ hipError_t long_fused_typed(const Problem& p, const RowShape& rs, void* W, float
     hipLaunchKernelGGL((bwd_long_fused_kernel<WT, V, PMAX, true>), grid, dim3(kThreads), 0, s,
                        (WT*)W, m, grad, meta.chunk_run, meta.chunk_start, meta.run_offsets,
                        meta.run_keys, meta.sorted_bag, meta.sorted_psw, order, list_begin,
-                       (ACC*)partials, arrivals, p.T, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
+                       (ACC*)partials, arrivals, p.ld, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
                        (ACC)lr, (ACC)eps);
   else
     hipLaunchKernelGGL((bwd_long_fused_kernel<WT, V, PMAX, false>), grid, dim3(kThreads), 0, s,
                        (WT*)W, m, grad, meta.chunk_run, meta.chunk_start, meta.run_offsets,
                        meta.run_keys, meta.sorted_bag, meta.sorted_psw, order, list_begin,
-                       (ACC*)partials, arrivals, p.T, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
+                       (ACC*)partials, arrivals, p.ld, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
                        (ACC)lr, (ACC)eps);
   return hipGetLastError();
 }

@@ -37,7 +37,8 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
     const WT* __restrict__ W, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, const float* __restrict__ psw,
     const int32_t* __restrict__ toff, float* __restrict__ out, int32_t T, int32_t B, int32_t D,
-    int32_t G, int32_t log2G, int32_t P, int64_t nbags, int64_t nblocks, int32_t* __restrict__ err) {
+    int32_t G, int32_t log2G, int32_t P, int64_t nbags, int64_t nblocks, int64_t ld,
+    int32_t* __restrict__ err) {
   using ACC = typename acc_of<WT>::type;
   using RAW = typename raw_vec<WT, V>::type;
   constexpr int UNROLL = PMAX == 1 ? 4 : 1;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
     if (__ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
   }
   if (!has_bag) return;
-  float* o = out + (int64_t)b * T * D + (int64_t)t * D;
+  float* o = out + (int64_t)b * ld + (int64_t)t * D;
 #pragma unroll
   for (int p = 0; p < PMAX; ++p) {
     const int e = (p * G + col) * V;
@@ -152,7 +153,7 @@ hipError_t launch_typed(const Problem& p, const RowShape& rs, const void* W, con
 #define TBE_FWD(WGT, CHK)                                                                      \
   hipLaunchKernelGGL((fwd_pool_kernel<WT, V, PMAX, WGT, CHK>), grid, dim3(kFwdThreads), 0, s,  \
                      (const WT*)W, indices, offsets, psw, toff, out, p.T, p.B, p.D, rs.G,      \
-                     rs.log2G, rs.P, p.nbags, nblocks, p.err)
+                     rs.log2G, rs.P, p.nbags, nblocks, p.ld, p.err)
   if (psw) {
     if (p.err) TBE_FWD(true, true);
     else TBE_FWD(true, false);

@@ -49,6 +49,10 @@ struct Problem {
   int32_t* err;
   // TBE_FLAG_FUSED_LONG: long runs reduced and applied by the long kernel
   bool fused_long;
+  // Row stride (floats) of the pooled output and of the upstream gradient:
+  // T*D, or the whole problem's T*D when this problem is one group of tables
+  // of a larger call.
+  int64_t ld;
 };
 
 tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p);
@@ -130,6 +134,14 @@ hipError_t launch_bwd_long_fused(const Problem& p, void* W, float* m, const floa
 size_t long_schedule_ints(const Problem& p);  // workspace ints of the chunk schedule
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
                             const void* partials, double lr, double eps, hipStream_t s);
+
+// int64 index arrays: table start offsets (T+1) and int32 copies of one
+// group of tables.
+hipError_t launch_table_bounds(const int64_t* offsets, int32_t T, int32_t B, int64_t* out,
+                               hipStream_t s);
+hipError_t launch_narrow(const int64_t* indices, int64_t n_idx, const int64_t* offsets,
+                         int64_t n_off, int64_t base, int32_t* idx32, int32_t* off32,
+                         hipStream_t s);
 
 hipError_t launch_small_count(const Problem& p, const int32_t* indices, const int32_t* offsets,
                               const int32_t* tinfo, uint8_t* hist, int32_t* counts,

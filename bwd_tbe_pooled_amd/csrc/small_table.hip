@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void small_pool_kernel(
     const f16_t* __restrict__ W, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ toff,
     const int32_t* __restrict__ trows, float* __restrict__ out, int32_t T, int32_t B,
-    int32_t D) {
+    int32_t D, int64_t ld) {
   __shared__ __align__(16) _Float16 Ws[kSmallE][kWStride];
   if (counts[4] != 0) return;
   const int32_t t = blockIdx.x % T;   // tables vary fastest: the resident
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void small_pool_kernel(
   load_w_operands(W + (int64_t)toff[t] * D, trows[t], D, Ws, bw,
                   [](int ks, int kb_, int j) { return kb_ * 32 + ks * 8 + j; });
   float* ot = out + (int64_t)t * D;
-  const int64_t ostride = (int64_t)T * D;
+  const int64_t ostride = ld;
   const int32_t tb0 = bx * kPoolTiles * kBagTile;
   auto load_counts = [&](int32_t b0, uint4& h0, uint4& h1) {
     const int32_t b = b0 + mt * 32 + i;
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
     const f16_t* __restrict__ W, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ toff, const int32_t* __restrict__ trows, float* __restrict__ out,
-    int32_t T, int32_t B, int32_t D, int32_t* __restrict__ err) {
+    int32_t T, int32_t B, int32_t D, int64_t ld, int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
   __shared__ int32_t s_off[kBagTile + 1];
   __shared__ uint32_t s_wmax[kWaves];
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
   const int32_t Et = trows[t];
   const f16_t* Wt = W + (int64_t)toff[t] * D;
   float* ot = out + (int64_t)t * D;
-  const int64_t ostride = (int64_t)T * D;
+  const int64_t ostride = ld;
   half8 bw[kSmallE / 16][2];
   load_w_operands(Wt, Et, D, reinterpret_cast<_Float16(*)[kWStride]>(&H[0][0]), bw,
                   [](int ks, int kb_, int j) { return ks * 16 + kb_ * 8 + j; });
@@ -438,8 +438,9 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     const float* __restrict__ grad, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, float* __restrict__ partials,
-    int32_t* __restrict__ part_counts, int32_t T, int32_t B, int32_t D, int32_t splits,
-    int32_t bags_per_split, const int32_t* __restrict__ trows, int32_t* __restrict__ err) {
+    int32_t* __restrict__ part_counts, int32_t T, int32_t B, int32_t D, int64_t ld,
+    int32_t splits, int32_t bags_per_split, const int32_t* __restrict__ trows,
+    int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];     // recounted counts
   __shared__ __align__(16) _Float16 HT[kSmallE][kTStride];     // counts, row-major by table row
   __shared__ int32_t s_off[kBagTile + 1];
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
   const int d = nt * 32 + i;
   const bool has_col = nt < NT && d < D;
   const float* gt = grad + (int64_t)t * D;
-  const int64_t gstride = (int64_t)T * D;
+  const int64_t gstride = ld;
   // offset of (bag kb*8, column d) from a 16-bag group's first row; columns
   // past D read column D-1 and are zeroed after the load
   const int32_t lane_off = kb * 8 * (int32_t)gstride + (d < D ? d : D - 1);
@@ -584,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void small_backward_wide_kernel(
     const float* __restrict__ grad, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
     float* __restrict__ partials, int32_t* __restrict__ part_counts, int32_t T, int32_t B,
-    int32_t D, int32_t splits, int32_t bags_per_split, const int32_t* __restrict__ trows,
-    int32_t* __restrict__ err) {
+    int32_t D, int64_t ld, int32_t splits, int32_t bags_per_split,
+    const int32_t* __restrict__ trows, int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
   __shared__ int32_t s_off[kBagTile + 1];
   if (counts[5] == 0) return;
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_wide_kernel(
   const int d = threadIdx.x % kMaxD;
   const int e0 = (threadIdx.x / kMaxD) * (kSmallE / 2);  // rows e0 .. e0+31
   const float* gt = grad + (int64_t)t * D;
-  const int64_t gstride = (int64_t)T * D;
+  const int64_t gstride = ld;
   float acc[kSmallE / 2];
 #pragma unroll
   for (int r = 0; r < kSmallE / 2; ++r) acc[r] = 0.f;
@@ -704,12 +705,12 @@ hipError_t launch_small_pool(const Problem& p, const void* W, const int32_t* ind
   const int64_t pool_bags = (int64_t)kBagTile * kPoolTiles;
   hipLaunchKernelGGL(small_pool_kernel, dim3((unsigned)((p.B + pool_bags - 1) / pool_bags * p.T)),
                      dim3(kThreads), 0, s, (const f16_t*)W, hist, counts, toff, trows, out, p.T,
-                     p.B, p.D);
+                     p.B, p.D, p.ld);
   const int64_t re_bags = (int64_t)kBagTile * kFwdTiles;
   hipLaunchKernelGGL(small_recount_forward_kernel,
                      dim3((unsigned)((p.B + re_bags - 1) / re_bags), (unsigned)p.T), dim3(kThreads), 0,
                      s, (const f16_t*)W, indices, offsets, counts, toff, trows, out, p.T, p.B, p.D,
-                     p.err);
+                     p.ld, p.err);
   return hipGetLastError();
 }
 
@@ -722,11 +723,11 @@ hipError_t launch_small_backward(const Problem& p, const float* grad, const uint
   const dim3 grid((unsigned)splits, (unsigned)p.T);
   // Exactly one of the two does the work, chosen on the device by counts[5].
   hipLaunchKernelGGL(small_backward_kernel, grid, dim3(kThreads), 0, s, grad, hist, counts, indices,
-                     offsets, partials, part_counts, p.T, p.B, p.D, splits, per, tinfo + p.T,
-                     p.err);
+                     offsets, partials, part_counts, p.T, p.B, p.D, p.ld, splits, per,
+                     tinfo + p.T, p.err);
   hipLaunchKernelGGL(small_backward_wide_kernel, grid, dim3(kThreads), 0, s, grad, counts, indices,
-                     offsets, partials, part_counts, p.T, p.B, p.D, splits, per, tinfo + p.T,
-                     p.err);
+                     offsets, partials, part_counts, p.T, p.B, p.D, p.ld, splits, per,
+                     tinfo + p.T, p.err);
   return hipGetLastError();
 }
 

@@ -91,4 +91,63 @@ hipError_t launch_validate(const Problem& p, const int32_t* indices, const int32
   return hipGetLastError();
 }
 
+// --- int64 index arrays (page 1, checklist item 6): a call is split into
+// groups of whole tables whose linearized rows and lookups each stay below
+// 2^31, and each group runs on int32 copies of its indices and offsets. ----
+
+constexpr int64_t kI32Max = 0x7fffffff;
+
+// out[t] = offsets[t*B] for t = 0..T: where each table's lookups begin.
+__global__ void table_bounds_kernel(const int64_t* __restrict__ offsets, int32_t T, int32_t B,
+                                    int64_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t <= T) out[t] = offsets[t * B];
+}
+
+// In-table rows narrowed to int32. A value outside [0, 2^31 - 1) becomes
+// 2^31 - 1, which lies outside every table (each has fewer rows), so the
+// bounds checks report it instead of a wrapped row.
+__global__ __launch_bounds__(256) void narrow_indices_kernel(const int64_t* __restrict__ src,
+                                                             int64_t n, int32_t* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t v = src[i];
+    dst[i] = (v >= 0 && v < kI32Max) ? (int32_t)v : (int32_t)kI32Max;
+  }
+}
+
+// Offsets of a group's bags relative to its first lookup, saturated to
+// [-1, 2^31 - 1] so that a bad offset stays bad (the group has fewer lookups).
+__global__ __launch_bounds__(256) void narrow_offsets_kernel(const int64_t* __restrict__ src,
+                                                             int64_t n, int64_t base,
+                                                             int32_t* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t v = src[i] - base;
+    dst[i] = v < 0 ? -1 : (v > kI32Max ? (int32_t)kI32Max : (int32_t)v);
+  }
+}
+
+hipError_t launch_table_bounds(const int64_t* offsets, int32_t T, int32_t B, int64_t* out,
+                               hipStream_t s) {
+  const unsigned blocks = (unsigned)(((int64_t)T + 1 + 255) / 256);
+  hipLaunchKernelGGL(table_bounds_kernel, dim3(blocks), dim3(256), 0, s, offsets, T, B, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow(const int64_t* indices, int64_t n_idx, const int64_t* offsets,
+                         int64_t n_off, int64_t base, int32_t* idx32, int32_t* off32,
+                         hipStream_t s) {
+  const int64_t per_block = 256 * 8;
+  if (n_idx > 0) {
+    const int64_t blocks = std::min<int64_t>(16384, (n_idx + per_block - 1) / per_block);
+    hipLaunchKernelGGL(narrow_indices_kernel, dim3((unsigned)blocks), dim3(256), 0, s, indices,
+                       n_idx, idx32);
+  }
+  const int64_t blocks = std::min<int64_t>(16384, std::max<int64_t>(1, (n_off + per_block - 1) / per_block));
+  hipLaunchKernelGGL(narrow_offsets_kernel, dim3((unsigned)blocks), dim3(256), 0, s, offsets,
+                     n_off, base, off32);
+  return hipGetLastError();
+}
+
 }  // namespace tbe

@@ -31,7 +31,8 @@
  *   No C++ exception crosses this boundary.
  * - Indices, offsets and linearized keys are int32: the library requires the
  *   total row count sum(E_t) and the lookup count N to be below 2^31
- *   (checklist item 6 of page 1), else TBE_ERR_UNSUPPORTED.
+ *   (checklist item 6 of page 1), else TBE_ERR_UNSUPPORTED. The _i64 entry
+ *   points take int64 indices and offsets and lift both limits.
  *
  * Data layout (device)
  * --------------------
@@ -285,6 +286,43 @@ tbe_status tbe_backward_adagrad(const tbe_desc* desc, void* W, float* momentum,
                                 const int32_t* offsets, int64_t N, const float* psw,
                                 const tbe_meta* meta, double lr, double eps,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * int64 indices and offsets (page 1, checklist item 6: int32 index arrays
+ * halve index storage and sort-key width while the linearized range stays
+ * below 2^31; beyond it they must be 64-bit). `indices` and `offsets` are
+ * int64 device arrays with the same meaning and layout as above; everything
+ * else is as for tbe_forward / tbe_backward_adagrad. The sum of the rows and
+ * N may reach 2^63 - 1. Each table must have fewer than 2^31 - 1 rows and
+ * fewer than 2^31 - 1 lookups, and B must be below 2^31 - 1; otherwise
+ * TBE_ERR_UNSUPPORTED.
+ *
+ * The call runs as a sequence of int32 calls over groups of consecutive
+ * tables whose rows, lookups and bags each stay below 2^31 - 1. Every step of
+ * the method is per table, so the result is that of one call. To form the
+ * groups the host reads where each table's lookups begin (T+1 offsets: one
+ * synchronisation of `stream` per call). offsets[0] must be 0 and
+ * offsets[T*B] must equal N, and the per-table counts must be >= 0; else
+ * TBE_ERR_INDEX_RANGE. An index outside [0, 2^31 - 1) is narrowed to
+ * 2^31 - 1, which lies outside every table, so TBE_FLAG_CHECK and
+ * TBE_FLAG_VALIDATE report it. Under TBE_FLAG_VALIDATE every group is checked
+ * before any group is computed.
+ *
+ * There is no metadata form: the backward preprocesses each group into the
+ * workspace (the int32 calls' meta == NULL behaviour). ws: device, 256-byte
+ * aligned, at least tbe_workspace_bytes_i64(op = TBE_OP_FORWARD or
+ * TBE_OP_BACKWARD_SELF), which bounds the workspace of every group
+ * (0 for other ops or a bad description).
+ */
+size_t tbe_workspace_bytes_i64(const tbe_desc* desc, int64_t N, int32_t weighted, tbe_op op);
+tbe_status tbe_forward_i64(const tbe_desc* desc, const void* W, const int64_t* indices,
+                           const int64_t* offsets, int64_t N, const float* psw, float* out,
+                           void* ws, size_t ws_bytes, void* stream);
+tbe_status tbe_backward_adagrad_i64(const tbe_desc* desc, void* W, float* momentum,
+                                    const float* grad_out, const int64_t* indices,
+                                    const int64_t* offsets, int64_t N, const float* psw,
+                                    double lr, double eps, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /*
  * Stage timer. When desc->timer is set, each stage a call runs is bracketed by

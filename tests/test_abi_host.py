@@ -6,7 +6,9 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GOLDEN = os.path.join(ROOT, "tests", "golden")
@@ -17,7 +19,7 @@ tbe = pytest.importorskip("bwd_tbe_pooled_amd", reason="libtbe.so not built")
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "tbe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"\b(tbe_[a-z_]+)\s*\(", src)
+    names = re.findall(r"\b(tbe_[a-z0-9_]+)\s*\(", src)
     return sorted(set(names))
 
 
@@ -146,3 +148,67 @@ def test_calls_reject_bad_arguments_before_any_launch():
     st = lib.tbe_forward(d.ref, fake, fake, fake, 10, None, fake, None, ctypes.c_void_p(4100),
                          1 << 30, None)
     assert st == tbe.TBE_ERR_ARG
+
+
+def test_int64_workspace_and_limits():
+    """The int64 entry points take totals beyond int32 (page 1, checklist item
+    6) but keep every table below 2^31 - 1 rows; only FORWARD and
+    BACKWARD_SELF have an int64 form."""
+    big = tbe.Desc(T=3, D=8, B=4096, rows=[1_200_000_000, 1_000_000_000, 500_000_000],
+                   dtype="bf16")
+    N = 3 * 4096 * 20
+    assert tbe.tbe_workspace_bytes(big, N, True, tbe.TBE_OP_BACKWARD_SELF) == 0   # int32: no
+    f = tbe.tbe_workspace_bytes_i64(big, N, True, tbe.TBE_OP_FORWARD)
+    b = tbe.tbe_workspace_bytes_i64(big, N, True, tbe.TBE_OP_BACKWARD_SELF)
+    assert 0 < f < b
+    for op in (tbe.TBE_OP_FORWARD_PREPROCESS, tbe.TBE_OP_PREPROCESS, tbe.TBE_OP_BACKWARD):
+        assert tbe.tbe_workspace_bytes_i64(big, N, True, op) == 0
+    huge_table = tbe.Desc(T=1, D=8, B=16, rows=[2 ** 31 - 1], dtype="f32")
+    assert tbe.tbe_workspace_bytes_i64(huge_table, 100, False, tbe.TBE_OP_FORWARD) == 0
+    # N beyond int32: the int32 form refuses, the int64 form sizes one group's worth
+    d = _desc()
+    n_big = 3 * 2 ** 30
+    assert tbe.tbe_workspace_bytes(d, n_big, False, tbe.TBE_OP_BACKWARD_SELF) == 0
+    w_big = tbe.tbe_workspace_bytes_i64(d, n_big, False, tbe.TBE_OP_BACKWARD_SELF)
+    w_cap = tbe.tbe_workspace_bytes_i64(d, 2 ** 31 - 2, False, tbe.TBE_OP_BACKWARD_SELF)
+    assert w_big == w_cap > 0    # every part is bounded by what one group can hold
+    # the int64 calls check their arguments on the host as well
+    lib = tbe._lib
+    fake = ctypes.c_void_p(256)
+    st = lib.tbe_forward_i64(d.ref, fake, fake, fake, 10, None, fake, fake, 1, None)
+    assert st == tbe.TBE_ERR_WORKSPACE
+    st = lib.tbe_backward_adagrad_i64(d.ref, fake, None, fake, fake, fake, 10, None, 0.01, 1e-8,
+                                      fake, 1 << 30, None)
+    assert st == tbe.TBE_ERR_ARG
+    with pytest.raises(TypeError):
+        tbe.tbe_forward_i64(d, None, torch.zeros(4, dtype=torch.int32),
+                            torch.zeros(3, dtype=torch.int64), None, None, None)
+
+
+def test_int64_workspace_bounds_every_group():
+    """The int64 workspace must hold the int32 workspace of any group of
+    consecutive tables the call may form (any lookup count up to N), for
+    each path and operation."""
+    rng = np.random.default_rng(7)
+    for case in range(300):
+        T = int(rng.integers(1, 7))
+        small = case % 3 == 0
+        rows = [int(x) for x in (rng.integers(1, 65, T) if small else
+                                 rng.integers(1, 2 ** int(rng.integers(4, 31)), T))]
+        D = int(rng.choice([64, 96, 128])) if small else int(rng.integers(1, 257))
+        B = int(rng.integers(1, 5000))
+        dtype = "f16" if small else str(rng.choice(["f32", "f16", "bf16"]))
+        weighted = bool(rng.integers(0, 2)) and not small
+        N = int(rng.integers(0, 64 * T * B + 2))
+        d = tbe.Desc(T=T, D=D, B=B, rows=rows, dtype=dtype)
+        for op in (tbe.TBE_OP_FORWARD, tbe.TBE_OP_BACKWARD_SELF):
+            total = tbe.tbe_workspace_bytes_i64(d, N, weighted, op)
+            assert total > 0
+            t0 = int(rng.integers(0, T))
+            t1 = int(rng.integers(t0 + 1, T + 1))
+            if sum(rows[t0:t1]) >= 2 ** 31 - 1:
+                t1 = t0 + 1            # a group holds fewer than 2^31 - 1 rows
+            sub = tbe.Desc(T=t1 - t0, D=D, B=B, rows=rows[t0:t1], dtype=dtype)
+            for Ng in (0, N, int(rng.integers(0, N + 1))):
+                need = tbe.tbe_workspace_bytes(sub, Ng, weighted, op)
+                assert 0 < need <= total, (case, T, rows, D, B, N, Ng, t0, t1, op)
