@@ -162,6 +162,9 @@ def main():
     ap.add_argument("--long", choices=["two_launch", "fused"], default="two_launch",
                     help="long runs: chunk partials then a separate apply (default), or one "
                          "launch whose last chunk per run reduces and applies (TBE_FLAG_FUSED_LONG)")
+    ap.add_argument("--index", choices=["int32", "int64"], default="int32",
+                    help="index arrays: int32 (default) or int64 through the _i64 entry points "
+                         "(which preprocess inside the backward, so --preprocess backward)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -201,15 +204,26 @@ def main():
         flags |= tbe.TBE_FLAG_FUSED_LONG
     desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, flags=flags, error_flags=err)
     meta = tbe.Meta(desc, N, True, with_pos=False)   # the backward needs no positions
+    wide = args.index == "int64"
+    if wide and args.preprocess == "forward":
+        args.preprocess = "backward"   # the int64 entry points keep no metadata
     in_fwd = args.preprocess == "forward"
-    ws_f = tbe.workspace(desc, N, True, tbe.TBE_OP_FORWARD_PREPROCESS if in_fwd else tbe.TBE_OP_FORWARD)
-    ws_b = tbe.workspace(desc, N, True, tbe.TBE_OP_BACKWARD if in_fwd else tbe.TBE_OP_BACKWARD_SELF)
+    if wide:
+        idx64, off64 = idx.long(), off.long()
+        ws_f = tbe.workspace_i64(desc, N, True, tbe.TBE_OP_FORWARD)
+        ws_b = tbe.workspace_i64(desc, N, True, tbe.TBE_OP_BACKWARD_SELF)
+    else:
+        ws_f = tbe.workspace(desc, N, True, tbe.TBE_OP_FORWARD_PREPROCESS if in_fwd else tbe.TBE_OP_FORWARD)
+        ws_b = tbe.workspace(desc, N, True, tbe.TBE_OP_BACKWARD if in_fwd else tbe.TBE_OP_BACKWARD_SELF)
     if args.profile_copy:
         profile_copy(torch, dev)
     torch.cuda.synchronize()
 
     def step():
-        if in_fwd:
+        if wide:
+            tbe.tbe_forward_i64(desc, W, idx64, off64, psw, out, ws_f)
+            tbe.tbe_backward_adagrad_i64(desc, W, m, grad, idx64, off64, psw, cfg.lr, cfg.eps, ws_b)
+        elif in_fwd:
             tbe.tbe_forward(desc, W, idx, off, psw, out, meta, ws_f)
             tbe.tbe_backward_adagrad(desc, W, m, grad, idx, off, psw, meta, cfg.lr, cfg.eps, ws_b)
         else:   # the backward preprocesses into its own workspace
@@ -276,7 +290,8 @@ def main():
         "config": {"workload": "T=32 E=2M D=128 bf16 B=131072 Poisson(20) Zipf-Mandelbrot weighted, "
                                f"preprocessing in {args.preprocess}"
                                + ("" if args.check == "none" else f", index check: {args.check}")
-                               + (", long runs in one launch" if fused_long else ""),
+                               + (", long runs in one launch" if fused_long else "")
+                               + (", int64 indices and offsets" if wide else ""),
                    "T": cfg.T, "E": cfg.rows[0], "D": cfg.D, "B": cfg.B, "N": N, "U": U,
                    "long_runs": n_long, "chunks": n_chunks, "long_lookups": long_lookups,
                    "parallelism": "single GPU"},
