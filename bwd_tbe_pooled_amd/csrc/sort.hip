@@ -124,7 +124,8 @@ __global__ __launch_bounds__(kThreads) void sort_upsweep_kernel(
     const int32_t* __restrict__ keys, const int4* __restrict__ tile_desc, int shift, int bits,
     int64_t tiles_max, int32_t* __restrict__ digit_counts, const int32_t* __restrict__ clamp_rows) {
   __shared__ uint32_t cnt[32][kThreads + 1];
-  const int64_t g = blockIdx.x;
+  const int64_t g = xcd_logical_block(tiles_max);
+  if (g < 0) return;
   const TileInfo ti = tile_info(g, tile_desc);
   if (!ti.valid) return;
   const int tid = threadIdx.x;
@@ -230,7 +231,8 @@ __global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
   __shared__ int32_t stage[kSortTile + 1];
   __shared__ int32_t scratch[4];
 
-  const int64_t g = blockIdx.x;
+  const int64_t g = xcd_logical_block(tiles_max);
+  if (g < 0) return;
   const TileInfo ti = tile_info(g, tile_desc);
   if (!ti.valid) return;
   const int wave = threadIdx.x / kWave;
@@ -435,7 +437,10 @@ hipError_t launch_sort(const Problem& p, const int32_t* indices, const int32_t* 
                        const tbe_meta& meta, hipStream_t s) {
   hipError_t err;
   if (p.N == 0) return hipSuccess;
-  const dim3 tgrid((unsigned)p.sort_tiles_max);
+  // Consecutive tiles run on one XCD: the digit counts of neighbouring tiles
+  // share cache lines, and so do the ends of their output buckets, which one
+  // L2 then merges instead of eight writing back partial lines.
+  const dim3 tgrid((unsigned)xcd_grid(p.sort_tiles_max));
   const int radix = 1 << p.sort_bits;
   const bool weighted = p.weighted;
   const bool with_pos = meta.sorted_pos != nullptr;
