@@ -50,8 +50,9 @@ __device__ __forceinline__ void find_heads(const int32_t* __restrict__ keys, int
 __global__ __launch_bounds__(kThreads) void rle_count_kernel(const int32_t* __restrict__ keys,
                                                              int64_t N, int32_t* __restrict__ tile_heads) {
   __shared__ int32_t wcount[4];
+  const int64_t tile = blockIdx.x;
   const int wave = threadIdx.x / kWave;
-  const int64_t wbase = (int64_t)blockIdx.x * kRleTile + (int64_t)wave * (kPer * kWave);
+  const int64_t wbase = tile * kRleTile + (int64_t)wave * (kPer * kWave);
   HeadScan h;
   find_heads(keys, N, wbase, h);
   int32_t c = 0;
@@ -59,17 +60,24 @@ __global__ __launch_bounds__(kThreads) void rle_count_kernel(const int32_t* __re
   for (int r = 0; r < kPer; ++r) c += __popcll(h.heads[r]);
   if (lane_id() == 0) wcount[wave] = c;
   __syncthreads();
-  if (threadIdx.x == 0) tile_heads[blockIdx.x] = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+  if (threadIdx.x == 0) tile_heads[tile] = wcount[0] + wcount[1] + wcount[2] + wcount[3];
 }
 
 // Single workgroup: exclusive scan of `ncols` interleaved arrays vals[c*n + i]
-// in place; totals[c] receives each sum.
+// in place; totals[c] receives each sum. With `items` set, only the tiles
+// that hold any of the *items elements are scanned (the rest are never read).
 __global__ __launch_bounds__(1024) void scan_tiles_kernel(int32_t* __restrict__ vals, int64_t n,
-                                                          int ncols, int32_t* __restrict__ totals) {
+                                                          int ncols, int32_t* __restrict__ totals,
+                                                          const int32_t* __restrict__ items) {
   __shared__ int32_t wsum[16];
+  int64_t m = n;
+  if (items) {
+    const int64_t used = ((int64_t)*items + kRleTile - 1) / kRleTile;
+    m = used < n ? used : n;
+  }
   for (int c = 0; c < ncols; ++c) {
     const int32_t tot =
-        block1024_scan_inplace(vals + (int64_t)c * n, n, wsum, [](int64_t, int32_t) {});
+        block1024_scan_inplace(vals + (int64_t)c * n, m, wsum, [](int64_t, int32_t) {});
     if (threadIdx.x == 0) totals[c] = tot;
   }
 }
@@ -90,9 +98,10 @@ __global__ __launch_bounds__(kThreads) void rle_write_kernel(const int32_t* __re
                                                              int32_t* __restrict__ run_keys,
                                                              int32_t* __restrict__ run_offsets) {
   __shared__ int32_t wcount[4];
+  const int64_t tile = blockIdx.x;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int64_t wbase = (int64_t)blockIdx.x * kRleTile + (int64_t)wave * (kPer * kWave);
+  const int64_t wbase = tile * kRleTile + (int64_t)wave * (kPer * kWave);
   HeadScan h;
   find_heads(keys, N, wbase, h);
   int32_t c = 0;
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void rle_write_kernel(const int32_t* __re
   for (int r = 0; r < kPer; ++r) c += __popcll(h.heads[r]);
   if (lane == 0) wcount[wave] = c;
   __syncthreads();
-  int32_t u = tile_base[blockIdx.x];
+  int32_t u = tile_base[tile];
   for (int w = 0; w < wave; ++w) u += wcount[w];
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
@@ -121,7 +130,12 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __
                                                                int32_t* __restrict__ tsum) {
   __shared__ int32_t scratch[4];
   const int64_t U = counts[0];
-  const int64_t base = (int64_t)blockIdx.x * kRleTile + (int64_t)threadIdx.x * kPer;
+  // Plain tile order: the grid covers the host's bound on the runs, and only
+  // its first ceil(U / TILE) tiles hold any (an XCD split would put them all
+  // on one XCD). Tiles past the runs are not scanned.
+  const int64_t tile = blockIdx.x;
+  if (tile * kRleTile >= U) return;
+  const int64_t base = tile * kRleTile + (int64_t)threadIdx.x * kPer;
   int32_t ns = 0, nl = 0, nc = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -137,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void route_count_kernel(const int32_t* __
   block256_exclusive_scan(nl, scratch, t1);
   block256_exclusive_scan(nc, scratch, t2);
   if (threadIdx.x == 0) {
-    tsum[blockIdx.x] = t0;
-    tsum[ntiles + blockIdx.x] = t1;
-    tsum[2 * ntiles + blockIdx.x] = t2;
+    tsum[tile] = t0;
+    tsum[ntiles + tile] = t1;
+    tsum[2 * ntiles + tile] = t2;
   }
 }
 
@@ -163,7 +177,8 @@ __global__ __launch_bounds__(kThreads) void route_write_kernel(
   __shared__ int32_t l_run[kRleTile];
   __shared__ int32_t l_cbeg[kRleTile + 1];
   const int64_t U = counts[0];
-  const int64_t tile0 = (int64_t)blockIdx.x * kRleTile;
+  const int64_t tile = blockIdx.x;
+  const int64_t tile0 = tile * kRleTile;
   if (tile0 >= U) return;
   const int64_t base = tile0 + (int64_t)threadIdx.x * kPer;
   int32_t sl[kPer];
@@ -181,9 +196,9 @@ __global__ __launch_bounds__(kThreads) void route_write_kernel(
   int32_t xs = block256_exclusive_scan(ns, scratch, tn);
   int32_t xl = block256_exclusive_scan(nl, scratch, tl);
   int32_t xc = block256_exclusive_scan(nc, scratch, tc);
-  const int32_t bs = tsum[blockIdx.x];
-  const int32_t bl = tsum[ntiles + blockIdx.x];
-  const int32_t bc = tsum[2 * ntiles + blockIdx.x];
+  const int32_t bs = tsum[tile];
+  const int32_t bl = tsum[ntiles + tile];
+  const int32_t bc = tsum[2 * ntiles + tile];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (sl[i] < 0) continue;
@@ -228,7 +243,8 @@ hipError_t launch_rle_route(const Problem& p, const int32_t* sorted_keys, int32_
                        p.N, heads);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(scan_tiles_kernel, dim3(1), dim3(1024), 0, s, heads, nt, 1, totals);
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3(1), dim3(1024), 0, s, heads, nt, 1, totals,
+                     (const int32_t*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(rle_finish_kernel, dim3(1), dim3(64), 0, s, totals, p.N, meta.counts,
                      meta.run_offsets);
@@ -247,7 +263,8 @@ hipError_t launch_rle_route(const Problem& p, const int32_t* sorted_keys, int32_
                        meta.run_offsets, meta.counts, p.S, p.C, rt, tsum);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(scan_tiles_kernel, dim3(1), dim3(1024), 0, s, tsum, rt, 3, rtot);
+  hipLaunchKernelGGL(scan_tiles_kernel, dim3(1), dim3(1024), 0, s, tsum, rt, 3, rtot,
+                     (const int32_t*)meta.counts);  // counts[0] = U runs
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(64), 0, s, rtot, meta.counts,
                      meta.long_chunk_begin);
