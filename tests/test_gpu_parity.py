@@ -158,15 +158,16 @@ def test_empty_bags_and_all_empty_batch():
     assert pre0["U"] == 0 and not r0["out"].any()
 
 
+@pytest.mark.parametrize("flags", [0, FUSED_LONG], ids=["two_launch", "fused_long"])
 @pytest.mark.parametrize("D", [1, 3, 24, 256, 1000])
-def test_odd_dimensions(D):
+def test_odd_dimensions(D, flags):
     rng = np.random.default_rng(D)
     T, B = 2, 300
     lengths = rng.poisson(6, size=T * B)
     idx = rng.integers(0, 30, size=lengths.sum())
     cfg, batch = _custom(T, B, D, [30, 50], "f16" if D % 2 == 0 else "f32", lengths, idx,
                          psw=rng.random(lengths.sum()), seed=D)
-    _full_check(cfg, batch, meta_in_forward=True, S=8, C=5)
+    _full_check(cfg, batch, meta_in_forward=True, S=8, C=5, flags=flags)
 
 
 def test_unit_weights_equal_unweighted_bitwise():
