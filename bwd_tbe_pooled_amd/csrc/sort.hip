@@ -215,8 +215,12 @@ __global__ __launch_bounds__(kThreads) void sort_scan_kernel(int32_t* __restrict
 // FIRST: keys_in = indices, the position of an element is its index, and its
 // bag is found among the tile's bag offsets. LAST: keys_out receives
 // toff[t] + row. WITH_POS: the original position travels as payload.
+// Without positions, four waves per SIMD (at most 128 VGPRs, a couple of them
+// spilled for the weighted form) beat three: the pass is latency-bound, and it
+// took the three passes from 1.70 to 1.63 ms at T=32, E=2M, B=131072. With
+// positions the fourth wave would cost about 30 spilled registers.
 template <bool FIRST, bool LAST, bool WEIGHTED, bool WITH_POS>
-__global__ __launch_bounds__(kThreads) void sort_downsweep_kernel(
+__global__ __launch_bounds__(kThreads, WITH_POS ? 3 : 4) void sort_downsweep_kernel(
     const int32_t* __restrict__ keys_in, const int32_t* __restrict__ pos_in,
     const int32_t* __restrict__ bag_in, const float* __restrict__ psw_in,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ keys_out,
