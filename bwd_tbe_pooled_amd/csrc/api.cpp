@@ -595,11 +595,13 @@ tbe_status run_i64(bool backward, const tbe_desc* d, void* W, float* momentum,
     TBE_TRY_HIP(narrow(g, sub.T));
     char* Wg = static_cast<char*>(W) + roff[g.t0] * d->D * (int64_t)wbytes;
     const float* psw_g = psw ? psw + g.base : nullptr;
+    // out and grad_out may be NULL when there are no bags
+    const int64_t col = (int64_t)g.t0 * d->D;
     if (backward)
-      st = backward_impl(&sub, p, Wg, momentum + roff[g.t0], grad_out + (int64_t)g.t0 * d->D,
+      st = backward_impl(&sub, p, Wg, momentum + roff[g.t0], grad_out ? grad_out + col : nullptr,
                          idx32, off32, psw_g, nullptr, lr, eps, gws, gws_bytes, s);
     else
-      st = forward_impl(&sub, p, Wg, idx32, off32, psw_g, out + (int64_t)g.t0 * d->D, nullptr,
+      st = forward_impl(&sub, p, Wg, idx32, off32, psw_g, out ? out + col : nullptr, nullptr,
                         gws, gws_bytes, s);
     if (st != TBE_OK) return st;
   }

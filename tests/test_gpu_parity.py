@@ -158,6 +158,36 @@ def test_empty_bags_and_all_empty_batch():
     assert pre0["U"] == 0 and not r0["out"].any()
 
 
+def test_zero_bags():
+    """B = 0: no bags, no lookups, an empty output; every call (int32 and
+    int64, metadata and not) succeeds and leaves the weights alone."""
+    import bwd_tbe_pooled_amd as tbe
+    from tests.gpu_common import make_desc
+    cfg = Config("zero_bags", T=3, B=0, D=16, rows=(10, 20, 30), dtype="f32", bag=("fixed", 0),
+                 index=("uniform",), weighted=False, preprocess_in_forward=True, seed=0)
+    W, m = fresh_params(cfg)
+    W0, m0 = W.clone(), m.clone()
+    idx = torch.zeros(0, dtype=torch.int32, device="cuda")
+    off = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((0, cfg.T * cfg.D), dtype=torch.float32, device="cuda")
+    grad = torch.empty((0, cfg.T * cfg.D), dtype=torch.float32, device="cuda")
+    desc = make_desc(cfg)
+    meta = tbe.Meta(desc, 0, False)
+    tbe.tbe_forward(desc, W, idx, off, None, out, meta,
+                    tbe.workspace(desc, 0, False, tbe.TBE_OP_FORWARD_PREPROCESS))
+    tbe.tbe_backward_adagrad(desc, W, m, grad, idx, off, None, meta, cfg.lr, cfg.eps,
+                             tbe.workspace(desc, 0, False, tbe.TBE_OP_BACKWARD))
+    tbe.tbe_backward_adagrad(desc, W, m, grad, idx, off, None, None, cfg.lr, cfg.eps,
+                             tbe.workspace(desc, 0, False, tbe.TBE_OP_BACKWARD_SELF))
+    tbe.tbe_forward_i64(desc, W, idx.long(), off.long(), None, out,
+                        tbe.workspace_i64(desc, 0, False, tbe.TBE_OP_FORWARD))
+    tbe.tbe_backward_adagrad_i64(desc, W, m, grad, idx.long(), off.long(), None, cfg.lr, cfg.eps,
+                                 tbe.workspace_i64(desc, 0, False, tbe.TBE_OP_BACKWARD_SELF))
+    torch.cuda.synchronize()
+    assert int(meta["counts"][0].item()) == 0
+    assert torch.equal(W, W0) and torch.equal(m, m0)
+
+
 @pytest.mark.parametrize("flags", [0, FUSED_LONG], ids=["two_launch", "fused_long"])
 @pytest.mark.parametrize("D", [1, 3, 24, 256, 1000])
 def test_odd_dimensions(D, flags):
