@@ -5,7 +5,7 @@ run-length encoding + routing) and the backward with row-wise Adagrad runs in
 the library's HIP kernels. The functions carry the C ABI's names
 (include/tbe.h) and take torch tensors, passing their device pointers and the
 current HIP stream. There is no CPU fallback: importing this package fails if
-the library has not been built (python -m bwd_tbe_pooled_amd.build).
+the library has not been built (python bwd_tbe_pooled_amd/build.py).
 """
 from __future__ import annotations
 
@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("TBE_LIBRARY") or os.path.join(_HERE, "libtbe.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m bwd_tbe_pooled_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python bwd_tbe_pooled_amd/build.py`")
 
 # torch first: the library then binds to the HIP runtime torch has loaded,
 # so tensors, streams and kernels share one runtime in the process (loading

@@ -1,6 +1,6 @@
 """Build libtbe.so (HIP kernels for gfx950 + the C ABI) in-tree.
 
-    python -m bwd_tbe_pooled_amd.build
+    python bwd_tbe_pooled_amd/build.py
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instructions
 disabled (the compiler would otherwise pair float operations into
