@@ -27,10 +27,12 @@
 //   Random 512-byte rows served from L2 move about twice as fast this way as
 //   with 32 bytes per lane split over two instructions.
 // - Long-run chunks are executed in a schedule, not in chunk order: chunks are
-//   bucketed per XCD (a contiguous block of tables per XCD) and ordered by the
-//   batch position of their first lookup. Lookups of a run are in batch order,
-//   so concurrent chunks on one XCD read gradient rows of nearby bags, which
-//   its L2 keeps. Each chunk still writes its own partial, so the result does
+//   bucketed per XCD (a contiguous block of tables per XCD), and within an
+//   XCD's list taken two tables at a time, each pair ordered by the batch
+//   position of the chunk's first lookup. Lookups of a run are in batch order,
+//   so concurrent chunks on one XCD read gradient rows of nearby bags (and
+//   the two tables' rows of one bag are adjacent in memory), which its L2
+//   keeps. Each chunk still writes its own partial, so the result does
 //   not depend on the schedule.
 #include <algorithm>
 #include "adagrad.h"
@@ -63,14 +65,16 @@ __device__ __forceinline__ void wave_lds_sync() {
 // t: slot s takes k0+s, k0+s+NS, ...; bag ids and weights of 64 slots at a
 // time are loaded coalesced and handed to the slots with shuffles. On return
 // every slot holds the wave's sum (fixed butterfly over the slots).
-template <int V, int PMAX, typename ACC, bool WEIGHTED>
+// Rows in flight per slot: UNROLL = 4 at D = 128. With the long kernel's two
+// workgroups per CU, 8 and 16 took it from 3.18 to 3.38 and 3.51 ms (T=32,
+// B=131072, D=128, one MI355X): its time follows L2 misses, not latency.
+template <int V, int PMAX, typename ACC, bool WEIGHTED, int UNROLL = (PMAX <= 2 ? 4 : 1)>
 __device__ __forceinline__ void wave_accumulate(const float* __restrict__ grad,
                                                 const int32_t* __restrict__ sorted_bag,
                                                 const float* __restrict__ sorted_psw, int32_t k0,
                                                 int32_t k1, int64_t ld, int32_t B, int32_t D,
                                                 int G, int log2G, int P, ACC (&acc)[PMAX][V]) {
   using GRAW = typename raw_vec<float, V>::type;
-  constexpr int UNROLL = PMAX <= 2 ? 4 : 1;
   const int lane = lane_id();
   const int slot = lane >> log2G;
   const int col = lane & (G - 1);
@@ -79,11 +83,20 @@ __device__ __forceinline__ void wave_accumulate(const float* __restrict__ grad,
   const float* __restrict__ gt = grad + (int64_t)t * D;
   const int32_t tB = t * B;
   zero_acc<ACC, V, PMAX>(acc);
+  // bag ids and weights of the next 64 slots are loaded while the current
+  // 64 rows are gathered
+  int32_t nx_bag = k0 + lane < k1 ? sorted_bag[k0 + lane] : tB;
+  float nx_s = 0.f;
+  if constexpr (WEIGHTED) nx_s = k0 + lane < k1 ? sorted_psw[k0 + lane] : 0.f;
   for (int32_t base = k0; base < k1; base += kWave) {
     const int n = k1 - base < kWave ? k1 - base : kWave;
-    const int32_t my_bag = lane < n ? sorted_bag[base + lane] : tB;
-    float my_s = 0.f;
-    if constexpr (WEIGHTED) my_s = lane < n ? sorted_psw[base + lane] : 0.f;
+    const int32_t my_bag = nx_bag;
+    const float my_s = nx_s;
+    {
+      const int32_t nk = base + kWave + lane;
+      nx_bag = nk < k1 ? sorted_bag[nk] : tB;
+      if constexpr (WEIGHTED) nx_s = nk < k1 ? sorted_psw[nk] : 0.f;
+    }
     for (int r0 = 0; r0 < n; r0 += NS * UNROLL) {
       GRAW buf[UNROLL][PMAX];
       float sc[UNROLL];
@@ -406,9 +419,16 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
   }
 }
 
-// --- long-chunk schedule: bucket = (XCD of the chunk's table block, first
-// bag / 2^shift); counting sort of chunk ids into buckets. ----------------------
+// --- long-chunk schedule: bucket = (XCD of the chunk's table block, group of
+// kSchedTables tables within the block, first bag); counting sort of chunk ids
+// into buckets. An XCD thus walks its tables two at a time, each pair in bag
+// order. With T=32, E=2M, D=128, B=131072 and Zipf-Mandelbrot rows the long
+// kernel took 3.04 ms with pairs, 3.19 ms with the whole 4-table block at
+// once, 3.38 ms one table at a time, 4.1 ms when every XCD took an eighth of
+// each table's bags (tables in order) and 5.2 ms with an eighth of the bags
+// of all tables at once (one MI355X). ---------------------------------------
 constexpr int kSchedBuckets = 4096;  // per XCD
+constexpr int kSchedTables = 2;      // tables of a block walked together
 
 __global__ void sched_zero_kernel(int32_t* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
@@ -416,7 +436,7 @@ __global__ void sched_zero_kernel(int32_t* __restrict__ p, int n) {
 
 __global__ __launch_bounds__(256) void sched_count_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ chunk_start,
-    const int32_t* __restrict__ sorted_bag, int32_t B, int32_t T, int shift,
+    const int32_t* __restrict__ sorted_bag, int32_t B, int32_t T,
     int32_t* __restrict__ hist, int32_t* __restrict__ bucket_of, int32_t* __restrict__ arrivals) {
   const int64_t n = counts[3];
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
@@ -425,7 +445,12 @@ __global__ __launch_bounds__(256) void sched_count_kernel(
     const int32_t bag = sorted_bag[chunk_start[c]];
     const int32_t t = bag / B, b = bag - t * B;
     const int x = (int)(((int64_t)t * kXcds) / T);
-    const int bk = x * kSchedBuckets + (b >> shift);
+    const int t0 = (int)(((int64_t)x * T + kXcds - 1) / kXcds);  // first table of block x
+    const int t1 = (int)(((int64_t)(x + 1) * T + kXcds - 1) / kXcds);
+    const int ngrp = (t1 - t0 + kSchedTables - 1) / kSchedTables;
+    const int per = kSchedBuckets / ngrp;  // buckets per table group (0 past 4096 groups)
+    const int g = (t - t0) / kSchedTables;
+    const int bk = x * kSchedBuckets + g * per + (int)(((int64_t)b * per) / B);
     bucket_of[c] = bk;
     atomicAdd(&hist[bk], 1);
   }
@@ -641,8 +666,6 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
 hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t* sched,
                                 hipStream_t s) {
   if (p.cap_chunks == 0) return hipSuccess;
-  int shift = 0;
-  while (((int64_t)(p.B - 1) >> shift) >= kSchedBuckets) ++shift;
   int32_t* order = sched;
   int32_t* bucket_of = order + p.cap_chunks;
   int32_t* hist = bucket_of + p.cap_chunks;
@@ -650,7 +673,7 @@ hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t*
   int32_t* arrivals = list_begin + kXcds + 1;
   hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, hist, kXcds * kSchedBuckets);
   hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
-                     meta.sorted_bag, p.B, p.T, shift, hist, bucket_of, arrivals);
+                     meta.sorted_bag, p.B, p.T, hist, bucket_of, arrivals);
   hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, hist, list_begin);
   hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, bucket_of,
                      hist, order);
