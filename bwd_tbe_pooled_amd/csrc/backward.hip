@@ -65,9 +65,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // t: slot s takes k0+s, k0+s+NS, ...; bag ids and weights of 64 slots at a
 // time are loaded coalesced and handed to the slots with shuffles. On return
 // every slot holds the wave's sum (fixed butterfly over the slots).
-// Rows in flight per slot: UNROLL = 4 at D = 128. With the long kernel's two
-// workgroups per CU, 8 and 16 took it from 3.18 to 3.38 and 3.51 ms (T=32,
-// B=131072, D=128, one MI355X): its time follows L2 misses, not latency.
+// Rows in flight per slot: UNROLL (4 by default, 8 in the long kernels at
+// D = 128).
 template <int V, int PMAX, typename ACC, bool WEIGHTED, int UNROLL = (PMAX <= 2 ? 4 : 1)>
 __device__ __forceinline__ void wave_accumulate(const float* __restrict__ grad,
                                                 const int32_t* __restrict__ sorted_bag,
@@ -245,6 +244,23 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
   }
 }
 
+// Per-XCD work queue of the long kernels: a wave takes the next item of its
+// XCD's list, so the chunks in flight stay a narrow window of the list. A
+// fixed stride lets waves that draw slow chunks fall behind, which widens the
+// set of gradient rows the XCD's L2 must hold: at T=32, B=131072, D=128 the
+// long kernel took 3.05 ms with a fixed stride and 2.74 ms with the queue at
+// two workgroups per CU (one MI355X).
+constexpr int kQueueStride = 32;  // ints between the XCDs' counters: one 128-byte line each
+__device__ __forceinline__ int64_t next_item(int32_t* q) {
+  int32_t it = 0;
+  if (lane_id() == 0) it = __hip_atomic_fetch_add(q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (int64_t)__shfl(it, 0);
+}
+
+// Rows in flight per slot in the long kernels (the short kernel keeps 4).
+template <int PMAX>
+constexpr int kLongUnroll = PMAX <= 2 ? 8 : 1;
+
 // Workgroup w serves the schedule list of XCD (w mod 8); the grid is a
 // multiple of 8, so every list is served whatever the dispatch order.
 template <int V, int PMAX, typename ACC, bool WEIGHTED>
@@ -253,26 +269,25 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ run_offsets,
     const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw,
     const int32_t* __restrict__ order, const int32_t* __restrict__ list_begin,
-    ACC* __restrict__ partials, int64_t ld, int32_t B, int32_t D, int32_t C, int32_t G,
-    int32_t log2G, int32_t P) {
+    int32_t* __restrict__ queue, ACC* __restrict__ partials, int64_t ld, int32_t B, int32_t D,
+    int32_t C, int32_t G, int32_t log2G, int32_t P) {
   const int lane = lane_id();
   const int slot = lane >> log2G;
   const int col = lane & (G - 1);
   const int x = blockIdx.x % kXcds;
   const int64_t first = list_begin[x];
   const int64_t n_items = list_begin[x + 1] - first;
-  const int64_t gwave = (int64_t)(blockIdx.x / kXcds) * kWaves + threadIdx.x / kWave;
-  const int64_t nwaves = (int64_t)(gridDim.x / kXcds) * kWaves;
-
-  for (int64_t it = gwave; it < n_items; it += nwaves) {
+  for (;;) {
+    const int64_t it = next_item(queue + x * kQueueStride);
+    if (it >= n_items) break;
     const int32_t c = order[first + it];
     const int32_t u = chunk_run[c];
     const int32_t k0 = chunk_start[c];
     const int32_t kend = run_offsets[u + 1];
     const int32_t k1 = k0 + C < kend ? k0 + C : kend;
     ACC acc[PMAX][V];
-    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, ld, B, D, G,
-                                            log2G, P, acc);
+    wave_accumulate<V, PMAX, ACC, WEIGHTED, kLongUnroll<PMAX>>(grad, sorted_bag, sorted_psw, k0,
+                                                               k1, ld, B, D, G, log2G, P, acc);
     if (slot == 0) {
       ACC* out = partials + (int64_t)c * D;
 #pragma unroll
@@ -368,9 +383,9 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
     const int32_t* __restrict__ run_offsets, const int32_t* __restrict__ run_keys,
     const int32_t* __restrict__ sorted_bag, const float* __restrict__ sorted_psw,
     const int32_t* __restrict__ order, const int32_t* __restrict__ list_begin,
-    typename acc_of<WT>::type* __restrict__ partials, int32_t* __restrict__ arrivals, int64_t ld,
-    int32_t B, int32_t D, int32_t C, int32_t G, int32_t log2G, int32_t P,
-    typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
+    int32_t* __restrict__ queue, typename acc_of<WT>::type* __restrict__ partials,
+    int32_t* __restrict__ arrivals, int64_t ld, int32_t B, int32_t D, int32_t C, int32_t G,
+    int32_t log2G, int32_t P, typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
   using ACC = typename acc_of<WT>::type;
   const int lane = lane_id();
   const int slot = lane >> log2G;
@@ -378,10 +393,9 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
   const int x = blockIdx.x % kXcds;
   const int64_t first = list_begin[x];
   const int64_t n_items = list_begin[x + 1] - first;
-  const int64_t gwave = (int64_t)(blockIdx.x / kXcds) * kWaves + threadIdx.x / kWave;
-  const int64_t nwaves = (int64_t)(gridDim.x / kXcds) * kWaves;
-
-  for (int64_t it = gwave; it < n_items; it += nwaves) {
+  for (;;) {
+    const int64_t it = next_item(queue + x * kQueueStride);
+    if (it >= n_items) break;
     const int32_t c = order[first + it];
     const int32_t u = chunk_run[c];
     const int32_t k0 = chunk_start[c];
@@ -389,8 +403,8 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
     const int32_t kend = run_offsets[u + 1];
     const int32_t k1 = k0 + C < kend ? k0 + C : kend;
     ACC acc[PMAX][V];
-    wave_accumulate<V, PMAX, ACC, WEIGHTED>(grad, sorted_bag, sorted_psw, k0, k1, ld, B, D, G,
-                                            log2G, P, acc);
+    wave_accumulate<V, PMAX, ACC, WEIGHTED, kLongUnroll<PMAX>>(grad, sorted_bag, sorted_psw, k0,
+                                                               k1, ld, B, D, G, log2G, P, acc);
     if (slot == 0) {
       ACC* out = partials + (int64_t)c * D;
 #pragma unroll
@@ -426,7 +440,9 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
 // kernel took 3.04 ms with pairs, 3.19 ms with the whole 4-table block at
 // once, 3.38 ms one table at a time, 4.1 ms when every XCD took an eighth of
 // each table's bags (tables in order) and 5.2 ms with an eighth of the bags
-// of all tables at once (one MI355X). ---------------------------------------
+// of all tables at once (one MI355X, fixed-stride waves). With the work
+// queue: 2.29 ms with pairs, 2.62 ms with the block, 2.57 ms one table at a
+// time. ---------------------------------------------------------------------
 constexpr int kSchedBuckets = 4096;  // per XCD
 constexpr int kSchedTables = 2;      // tables of a block walked together
 
@@ -480,6 +496,24 @@ __global__ __launch_bounds__(256) void sched_scatter_kernel(const int32_t* __res
   }
 }
 
+// Layout of the long-chunk schedule in its workspace (int32 units): chunk
+// order, bucket of each chunk, bucket counts, list starts (padded), work-queue
+// counters, arrival counters of the fused kernel.
+struct SchedLayout {
+  int32_t *order, *bucket_of, *hist, *list_begin, *queue, *arrivals;
+};
+constexpr int kListPad = 64;
+inline SchedLayout sched_layout(int32_t* sched, int64_t cap) {
+  SchedLayout L;
+  L.order = sched;
+  L.bucket_of = L.order + cap;
+  L.hist = L.bucket_of + cap;
+  L.list_begin = L.hist + kXcds * kSchedBuckets;
+  L.queue = L.list_begin + kListPad;
+  L.arrivals = L.queue + kXcds * kQueueStride;
+  return L;
+}
+
 inline int64_t persistent_blocks(int64_t work_waves) {
   // Enough workgroups to fill 256 CUs several times over; the kernels stride.
   int64_t cap = 256 * 16;
@@ -507,13 +541,16 @@ hipError_t short_typed(const Problem& p, const RowShape& rs, void* W, float* m, 
   return hipGetLastError();
 }
 
-// Two workgroups (eight waves) per CU. More chunks in flight widen the
-// window of bags whose gradient rows the XCD's L2 must hold at once: with
-// T=32, E=2M, D=128, B=131072 and Zipf-Mandelbrot rows (287,766 chunks),
-// 1, 2, 3, 4 and 8 workgroups per CU took 4.87, 3.21, 3.43, 3.80 and
-// 4.01 ms on one MI355X.
+// Three workgroups (twelve waves) per CU. More chunks in flight widen the
+// window of bags whose gradient rows the XCD's L2 must hold at once; fewer
+// leave too few loads in flight. With T=32, E=2M, D=128, B=131072 and
+// Zipf-Mandelbrot rows (287,766 chunks) on one MI355X, with the work queue:
+// 2, 3 and 4 workgroups per CU took 2.74, 2.29 and 2.37 ms at 4 rows in
+// flight per slot; 3 per CU took 2.62, 2.29 and 2.25 ms at 2, 4 and 8 rows.
+// (Before the queue, with a fixed stride, 1, 2, 3, 4 and 8 per CU took
+// 4.87, 3.21, 3.43, 3.80 and 4.01 ms.)
 inline dim3 long_grid(const Problem& p) {
-  const int64_t per_xcd = 2 * std::max(1, device_cu_count() / kXcds);
+  const int64_t per_xcd = 3 * std::max(1, device_cu_count() / kXcds);
   int64_t blocks = (persistent_blocks(p.cap_chunks) + kXcds - 1) / kXcds * kXcds;
   if (blocks > per_xcd * kXcds) blocks = per_xcd * kXcds;
   return dim3((unsigned)blocks);
@@ -521,20 +558,19 @@ inline dim3 long_grid(const Problem& p) {
 
 template <typename ACC, int V, int PMAX>
 hipError_t long_typed(const Problem& p, const RowShape& rs, const float* grad, const tbe_meta& meta,
-                      void* partials, const int32_t* sched, hipStream_t s) {
-  const int32_t* order = sched;
-  const int32_t* list_begin = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets;
+                      void* partials, int32_t* sched, hipStream_t s) {
+  const SchedLayout L = sched_layout(sched, p.cap_chunks);
   const dim3 grid = long_grid(p);
   if (p.weighted)
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, true>), grid, dim3(kThreads), 0, s, grad,
                        meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
-                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.ld, p.B, p.D, p.C,
-                       rs.G, rs.log2G, rs.P);
+                       meta.sorted_psw, L.order, L.list_begin, L.queue, (ACC*)partials, p.ld, p.B,
+                       p.D, p.C, rs.G, rs.log2G, rs.P);
   else
     hipLaunchKernelGGL((bwd_long_kernel<V, PMAX, ACC, false>), grid, dim3(kThreads), 0, s, grad,
                        meta.chunk_run, meta.chunk_start, meta.run_offsets, meta.sorted_bag,
-                       meta.sorted_psw, order, list_begin, (ACC*)partials, p.ld, p.B, p.D, p.C,
-                       rs.G, rs.log2G, rs.P);
+                       meta.sorted_psw, L.order, L.list_begin, L.queue, (ACC*)partials, p.ld, p.B,
+                       p.D, p.C, rs.G, rs.log2G, rs.P);
   return hipGetLastError();
 }
 
@@ -543,21 +579,19 @@ hipError_t long_fused_typed(const Problem& p, const RowShape& rs, void* W, float
                             const float* grad, const tbe_meta& meta, void* partials,
                             int32_t* sched, double lr, double eps, hipStream_t s) {
   using ACC = typename acc_of<WT>::type;
-  const int32_t* order = sched;
-  const int32_t* list_begin = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets;
-  int32_t* arrivals = sched + 2 * p.cap_chunks + kXcds * kSchedBuckets + kXcds + 1;
+  const SchedLayout L = sched_layout(sched, p.cap_chunks);
   const dim3 grid = long_grid(p);
   if (p.weighted)
     hipLaunchKernelGGL((bwd_long_fused_kernel<WT, V, PMAX, true>), grid, dim3(kThreads), 0, s,
                        (WT*)W, m, grad, meta.chunk_run, meta.chunk_start, meta.run_offsets,
-                       meta.run_keys, meta.sorted_bag, meta.sorted_psw, order, list_begin,
-                       (ACC*)partials, arrivals, p.ld, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
+                       meta.run_keys, meta.sorted_bag, meta.sorted_psw, L.order, L.list_begin,
+                       L.queue, (ACC*)partials, L.arrivals, p.ld, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
                        (ACC)lr, (ACC)eps);
   else
     hipLaunchKernelGGL((bwd_long_fused_kernel<WT, V, PMAX, false>), grid, dim3(kThreads), 0, s,
                        (WT*)W, m, grad, meta.chunk_run, meta.chunk_start, meta.run_offsets,
-                       meta.run_keys, meta.sorted_bag, meta.sorted_psw, order, list_begin,
-                       (ACC*)partials, arrivals, p.ld, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
+                       meta.run_keys, meta.sorted_bag, meta.sorted_psw, L.order, L.list_begin,
+                       L.queue, (ACC*)partials, L.arrivals, p.ld, p.B, p.D, p.C, rs.G, rs.log2G, rs.P,
                        (ACC)lr, (ACC)eps);
   return hipGetLastError();
 }
@@ -619,7 +653,7 @@ hipError_t short_for(const Problem& p, void* W, float* m, const float* grad, con
 
 template <typename ACC>
 hipError_t long_for(const Problem& p, const float* grad, const tbe_meta& meta, void* partials,
-                    const int32_t* sched, hipStream_t s) {
+                    int32_t* sched, hipStream_t s) {
   const RowShape rs = grad_row_shape(p.D);
 #define CALL(VV, PP) long_typed<ACC, VV, PP>(p, rs, grad, meta, partials, sched, s)
   TBE_DISPATCH_V(rs, CALL);
@@ -666,22 +700,20 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
 hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t* sched,
                                 hipStream_t s) {
   if (p.cap_chunks == 0) return hipSuccess;
-  int32_t* order = sched;
-  int32_t* bucket_of = order + p.cap_chunks;
-  int32_t* hist = bucket_of + p.cap_chunks;
-  int32_t* list_begin = hist + kXcds * kSchedBuckets;
-  int32_t* arrivals = list_begin + kXcds + 1;
-  hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, hist, kXcds * kSchedBuckets);
+  const SchedLayout L = sched_layout(sched, p.cap_chunks);
+  // bucket counts, list starts and queue counters are contiguous: clear them together
+  hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, L.hist,
+                     (int)(L.arrivals - L.hist));
   hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
-                     meta.sorted_bag, p.B, p.T, hist, bucket_of, arrivals);
-  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, hist, list_begin);
-  hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, bucket_of,
-                     hist, order);
+                     meta.sorted_bag, p.B, p.T, L.hist, L.bucket_of, L.arrivals);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, L.hist, L.list_begin);
+  hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, L.bucket_of,
+                     L.hist, L.order);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
-                           void* partials, const int32_t* sched, hipStream_t s) {
+                           void* partials, int32_t* sched, hipStream_t s) {
   if (p.cap_chunks == 0) return hipSuccess;
   if (p.wdtype == TBE_F32) return long_for<double>(p, grad, meta, partials, sched, s);
   return long_for<float>(p, grad, meta, partials, sched, s);
@@ -700,8 +732,9 @@ hipError_t launch_bwd_long_fused(const Problem& p, void* W, float* m, const floa
 }
 
 size_t long_schedule_ints(const Problem& p) {
-  // order, bucket of each chunk, bucket counts, list starts, arrival counters
-  return 3 * (size_t)p.cap_chunks + kXcds * kSchedBuckets + kXcds + 1;
+  // order, bucket of each chunk, bucket counts, list starts, queue counters,
+  // arrival counters (sched_layout)
+  return 3 * (size_t)p.cap_chunks + kXcds * kSchedBuckets + kListPad + kXcds * kQueueStride;
 }
 
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,

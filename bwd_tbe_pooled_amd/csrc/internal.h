@@ -127,7 +127,7 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
 hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t* sched,
                                 hipStream_t s);
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
-                           void* partials, const int32_t* sched, hipStream_t s);
+                           void* partials, int32_t* sched, hipStream_t s);
 hipError_t launch_bwd_long_fused(const Problem& p, void* W, float* m, const float* grad,
                                  const tbe_meta& meta, void* partials, int32_t* sched, double lr,
                                  double eps, hipStream_t s);
