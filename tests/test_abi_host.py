@@ -212,3 +212,26 @@ def test_int64_workspace_bounds_every_group():
             for Ng in (0, N, int(rng.integers(0, N + 1))):
                 need = tbe.tbe_workspace_bytes(sub, Ng, weighted, op)
                 assert 0 < need <= total, (case, T, rows, D, B, N, Ng, t0, t1, op)
+
+
+def test_build_script_runs_without_the_library():
+    """A clean checkout has no libtbe.so, and importing the package refuses to
+    run without it; the build entry point must therefore load the build
+    script without importing the package."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import importlib.util, os, sys\n"
+        f"root = {root!r}\n"
+        "spec = importlib.util.spec_from_file_location('b', os.path.join(root, 'bwd_tbe_pooled_amd', 'build.py'))\n"
+        "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+        "assert callable(m.build) and 'bwd_tbe_pooled_amd' not in sys.modules\n"
+        "src = open(os.path.join(root, '__graft_entry__.py')).read()\n"
+        "body = src.split('def build()')[1].split('def ')[0]\n"
+        "assert 'spec_from_file_location' in body\n"
+        "assert body.index('hipbuild.build()') < body.index('import bwd_tbe_pooled_amd')\n"
+    )
+    env = dict(os.environ, TBE_LIBRARY=os.path.join(root, "no_such_libtbe.so"))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
