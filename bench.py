@@ -153,6 +153,25 @@ def profile_copy(torch, dev):
     del src, dst
 
 
+def stream_copy_gbps(torch, dev, reps=5):
+    """Context only: a plain 1 GiB device-to-device copy timed with events
+    (bytes read + written over its time), outside the timed steps."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return round(2 * (1 << 30) / (best * 1e6), 1)
+
+
 def graph_ms(torch, step, steps):
     """Milliseconds per step when the step is captured once in a HIP graph and
     replayed (no per-launch host cost); None if capture is not possible."""
@@ -195,6 +214,10 @@ def main():
     ap.add_argument("--long", choices=["two_launch", "fused"], default="two_launch",
                     help="long runs: chunk partials then a separate apply (default), or one "
                          "launch whose last chunk per run reduces and applies (TBE_FLAG_FUSED_LONG)")
+    ap.add_argument("--rows", choices=["zipf", "uniform"], default="zipf",
+                    help="row distribution of the large workload: Zipf-Mandelbrot (default, "
+                         "the headline) or uniform (a diagnostic without reuse, in which the "
+                         "effective and the counter-measured rates should agree)")
     ap.add_argument("--index", choices=["int32", "int64"], default="int32",
                     help="index arrays: int32 (default) or int64 through the _i64 entry points "
                          "(which preprocess inside the backward, so --preprocess backward)")
@@ -217,6 +240,9 @@ def main():
     if args.workload == "small":
         return main_small(args, torch, tbe)
     cfg = LARGE
+    if args.rows == "uniform":
+        import dataclasses
+        cfg = dataclasses.replace(LARGE, index=("uniform",))
     log("generating the batch")
     batch = make_batch(cfg)
     N = batch.indices.size
@@ -323,8 +349,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "T=32 E=2M D=128 bf16 B=131072 Poisson(20) Zipf-Mandelbrot weighted, "
-                               f"preprocessing in {args.preprocess}"
+        "config": {"workload": "T=32 E=2M D=128 bf16 B=131072 Poisson(20) "
+                               + ("Zipf-Mandelbrot" if args.rows == "zipf" else "uniform")
+                               + f" rows, weighted, preprocessing in {args.preprocess}"
                                + ("" if args.check == "none" else f", index check: {args.check}")
                                + (", long runs in one launch" if fused_long else "")
                                + (", int64 indices and offsets" if wide else ""),
@@ -347,6 +374,7 @@ def main():
                      "traffic": traffic, "bytes_per_launch": dom_bytes,
                      "avg_launch_ms": round(dom_ms, 4), **traffic_rate(traffic, dom_ms)},
         "cpu_baseline": cpu,
+        "stream_copy_GBps": stream_copy_gbps(torch, torch.device("cuda")),
         "context": "B200 figures on the pages (not this workload's hardware): combined "
                    "79.537 ms -> 66.183 ms with forward-side preprocessing",
     }
@@ -431,6 +459,7 @@ def main_small(args, torch, tbe):
                      "traffic": traffic, "bytes_per_launch": cand[dom][1],
                      "avg_launch_ms": round(cand[dom][0], 4), **traffic_rate(traffic, cand[dom][0])},
         "cpu_baseline": cpu,
+        "stream_copy_GBps": stream_copy_gbps(torch, torch.device("cuda")),
     }
     print(json.dumps(result), flush=True)
 
