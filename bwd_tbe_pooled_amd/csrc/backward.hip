@@ -29,7 +29,7 @@
 // - Long-run chunks are executed in a schedule, not in chunk order: chunks are
 //   bucketed per XCD (a contiguous block of tables per XCD), and within an
 //   XCD's list taken two tables at a time, each pair ordered by the batch
-//   position of the chunk's first lookup. Lookups of a run are in batch order,
+//   position of the middle of the chunk's lookups. Lookups of a run are in batch order,
 //   so concurrent chunks on one XCD read gradient rows of nearby bags (and
 //   the two tables' rows of one bag are adjacent in memory), which its L2
 //   keeps. Each chunk still writes its own partial, so the result does
@@ -434,15 +434,19 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
 }
 
 // --- long-chunk schedule: bucket = (XCD of the chunk's table block, group of
-// kSchedTables tables within the block, first bag); counting sort of chunk ids
-// into buckets. An XCD thus walks its tables two at a time, each pair in bag
-// order. With T=32, E=2M, D=128, B=131072 and Zipf-Mandelbrot rows the long
+// kSchedTables tables within the block, middle bag of the chunk); counting
+// sort of chunk ids into buckets. An XCD thus walks its tables two at a time,
+// each pair in bag order. A chunk is placed by the middle of its bag span:
+// a dense chunk's span is short either way, and a sparse one then runs while
+// the dense chunks around it read the middle of its rows, not its first ones
+// (2.04 ms against 2.26 ms by first bag, 2.24 ms by last bag and 2.08 ms at a
+// quarter of the span, with the queue below). With T=32, E=2M, D=128, B=131072 and Zipf-Mandelbrot rows the long
 // kernel took 3.04 ms with pairs, 3.19 ms with the whole 4-table block at
 // once, 3.38 ms one table at a time, 4.1 ms when every XCD took an eighth of
 // each table's bags (tables in order) and 5.2 ms with an eighth of the bags
-// of all tables at once (one MI355X, fixed-stride waves). With the work
-// queue: 2.29 ms with pairs, 2.62 ms with the block, 2.57 ms one table at a
-// time. ---------------------------------------------------------------------
+// of all tables at once (one MI355X, fixed-stride waves, first-bag order).
+// With the work queue and middle-bag order: 2.04 ms with pairs, 2.27 ms with
+// the block, 2.08 ms one table at a time. ------------------------------------
 constexpr int kSchedBuckets = 4096;  // per XCD
 constexpr int kSchedTables = 2;      // tables of a block walked together
 
@@ -452,13 +456,19 @@ __global__ void sched_zero_kernel(int32_t* __restrict__ p, int n) {
 
 __global__ __launch_bounds__(256) void sched_count_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ chunk_start,
-    const int32_t* __restrict__ sorted_bag, int32_t B, int32_t T,
+    const int32_t* __restrict__ sorted_bag, const int32_t* __restrict__ chunk_run,
+    const int32_t* __restrict__ run_offsets, int32_t C, int32_t B, int32_t T,
     int32_t* __restrict__ hist, int32_t* __restrict__ bucket_of, int32_t* __restrict__ arrivals) {
   const int64_t n = counts[3];
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
        c += (int64_t)gridDim.x * blockDim.x) {
     arrivals[c] = 0;  // arrival counters of the fused long kernel
-    const int32_t bag = sorted_bag[chunk_start[c]];
+    // the chunk's place in batch order: the middle of its bag span
+    const int32_t k0 = chunk_start[c];
+    const int32_t ke = run_offsets[chunk_run[c] + 1];
+    const int32_t klast = (k0 + C < ke ? k0 + C : ke) - 1;
+    const int32_t bag0 = sorted_bag[k0], bag1 = sorted_bag[klast];
+    const int32_t bag = bag0 + (bag1 - bag0) / 2;
     const int32_t t = bag / B, b = bag - t * B;
     const int x = (int)(((int64_t)t * kXcds) / T);
     const int t0 = (int)(((int64_t)x * T + kXcds - 1) / kXcds);  // first table of block x
@@ -546,7 +556,9 @@ hipError_t short_typed(const Problem& p, const RowShape& rs, void* W, float* m, 
 // leave too few loads in flight. With T=32, E=2M, D=128, B=131072 and
 // Zipf-Mandelbrot rows (287,766 chunks) on one MI355X, with the work queue:
 // 2, 3 and 4 workgroups per CU took 2.74, 2.29 and 2.37 ms at 4 rows in
-// flight per slot; 3 per CU took 2.62, 2.29 and 2.25 ms at 2, 4 and 8 rows.
+// flight per slot; 3 per CU took 2.62, 2.29 and 2.25 ms at 2, 4 and 8 rows
+// (first-bag order). In middle-bag order: 2.29, 2.04 and 2.07 ms at 2, 3 and
+// 4 per CU with 8 rows, and 2.09 ms at 3 per CU with 4 rows.
 // (Before the queue, with a fixed stride, 1, 2, 3, 4 and 8 per CU took
 // 4.87, 3.21, 3.43, 3.80 and 4.01 ms.)
 inline dim3 long_grid(const Problem& p) {
@@ -705,7 +717,8 @@ hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t*
   hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, L.hist,
                      (int)(L.arrivals - L.hist));
   hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
-                     meta.sorted_bag, p.B, p.T, L.hist, L.bucket_of, L.arrivals);
+                     meta.sorted_bag, meta.chunk_run, meta.run_offsets, p.C, p.B, p.T, L.hist,
+                     L.bucket_of, L.arrivals);
   hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, L.hist, L.list_begin);
   hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, L.bucket_of,
                      L.hist, L.order);
