@@ -278,6 +278,9 @@ class Timer:
         h = ctypes.c_void_p()
         _check(_lib.tbe_timer_create(int(capacity), ctypes.byref(h)), "tbe_timer_create")
         self.handle = h
+        # kept on the instance: at interpreter exit the module's globals may
+        # already be gone when the timer is collected
+        self._destroy = _lib.tbe_timer_destroy
 
     def reset(self):
         _check(_lib.tbe_timer_reset(self.handle), "tbe_timer_reset")
@@ -290,8 +293,9 @@ class Timer:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
-            _lib.tbe_timer_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h and destroy is not None:
+            destroy(h)
             self.handle = None
 
 
