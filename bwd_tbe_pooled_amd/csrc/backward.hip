@@ -251,6 +251,9 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
 // long kernel took 3.05 ms with a fixed stride and 2.74 ms with the queue at
 // two workgroups per CU (one MI355X).
 constexpr int kQueueStride = 32;  // ints between the XCDs' counters: one 128-byte line each
+// Every wave adds one more after the list is exhausted; a list within a few
+// hundred items of 2^31 would wrap the counter, so callers also stop on a
+// negative value (all valid items are below 2^31).
 __device__ __forceinline__ int64_t next_item(int32_t* q) {
   int32_t it = 0;
   if (lane_id() == 0) it = __hip_atomic_fetch_add(q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
   const int64_t n_items = list_begin[x + 1] - first;
   for (;;) {
     const int64_t it = next_item(queue + x * kQueueStride);
-    if (it >= n_items) break;
+    if (it < 0 || it >= n_items) break;  // past the end (or wrapped past 2^31)
     const int32_t c = order[first + it];
     const int32_t u = chunk_run[c];
     const int32_t k0 = chunk_start[c];
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
   const int64_t n_items = list_begin[x + 1] - first;
   for (;;) {
     const int64_t it = next_item(queue + x * kQueueStride);
-    if (it >= n_items) break;
+    if (it < 0 || it >= n_items) break;  // past the end (or wrapped past 2^31)
     const int32_t c = order[first + it];
     const int32_t u = chunk_run[c];
     const int32_t k0 = chunk_start[c];
