@@ -68,6 +68,18 @@ def test_large_skewed_reduced_batch_full_compare(flags):
     _full_check(batch.cfg, batch, meta_in_forward=True, backward_meta=True, flags=flags)
 
 
+@pytest.mark.parametrize("T", [5, 13])
+@pytest.mark.parametrize("flags", [0, FUSED_LONG], ids=["two_launch", "fused_long"])
+def test_uneven_table_blocks_with_many_chunks(T, flags):
+    """T not a multiple of the 8 XCDs: blocks of one or two tables, table
+    pairs that hold one table; small S and C put most lookups on the chunked
+    path, so every chunk of every per-XCD list must be served exactly once."""
+    import dataclasses
+    cfg = dataclasses.replace(LARGE, name=f"skewed_t{T}_e50k", T=T, rows=(50_000,) * T)
+    batch = make_batch(cfg, B=1024)
+    _full_check(batch.cfg, batch, meta_in_forward=True, S=16, C=8, flags=flags)
+
+
 @pytest.mark.parametrize("name", ["demo3_d16_f32_b4k", "t16_e1m_d128_f16_b16k"])
 def test_metadata_without_positions(name):
     """sorted_pos left NULL: the sort carries only bags and weights, which must
