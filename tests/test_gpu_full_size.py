@@ -3,6 +3,9 @@ configuration the benchmark times: T=32, E=2M, D=128 bf16, B=131072 weighted
 with preprocessing in the forward (about 84M lookups); and the small-table
 workload T=64, E=64, D=128 f16, B=32768, L=64 (134M lookups).
 
+The large workload is also run with uniform rows (the same shapes, no
+reuse, almost every run short).
+
 The oracle cannot redo 84M lookups in seconds, so:
 - the sort / RLE / routing metadata is checked by properties that define the
   stable sort uniquely (permutation; keys non-decreasing; equal keys in
@@ -53,9 +56,14 @@ def _sampled_backward(cfg, batch, keys, bags, W, m, Wrows_all, mrows_all, uk, sa
     assert_rows_match(cfg, W, m, r["run_keys"], bw["w_new"], bw["m_new"], "sampled rows")
 
 
-def test_large_skewed_workload_full_size():
-    cfg = LARGE
-    print("\n[full] generating the T=32 B=131072 workload", flush=True)
+@pytest.mark.parametrize("rows", ["zipf", "uniform"])
+def test_large_workload_full_size(rows):
+    """The benchmark's skewed batch, and the same shapes with uniform rows:
+    46.7M short runs, more than one round of the short-run kernel's grid
+    (65536 workgroups of four waves, 64 runs each), so its waves stride."""
+    import dataclasses
+    cfg = LARGE if rows == "zipf" else dataclasses.replace(LARGE, index=("uniform",))
+    print(f"\n[full] generating the T=32 B=131072 workload, {rows} rows", flush=True)
     batch = make_batch(cfg)
     keys, bags = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
     counts_all = np.bincount(keys, minlength=cfg.sum_rows)
@@ -101,6 +109,8 @@ def test_large_skewed_workload_full_size():
         np.testing.assert_array_equal(h[name], route[name], err_msg=name)
     print(f"[full] U={uk.size} long={route['long_runs'].size} chunks={route['chunk_run'].size}",
           flush=True)
+    if rows == "uniform":
+        assert route["short_runs"].size > 65536 * 4 * 64
 
     # backward on sampled rows, then untouched rows
     _sampled_backward(cfg, batch, keys, bags, W, m, Wrows, mrows, need, sample_keys)
