@@ -148,6 +148,42 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_TORCH_W = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _need(t, name, dtype, numel=None, shape=None):
+    """Raise TypeError unless `t` is a contiguous device tensor of `dtype`
+    (and `numel` elements / `shape`): the library reads raw device memory, so
+    a host tensor, an int64 array passed as int32 or a strided view would be
+    read as something else."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name}: must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise TypeError(f"{name}: expected {numel} elements, got {t.numel()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise TypeError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_args(desc: "Desc", idx_dtype, W=None, indices=None, offsets=None, psw=None, out=None,
+                grad_out=None, momentum=None):
+    _need(indices, "indices", idx_dtype)
+    N = indices.numel() if indices is not None else None
+    _need(offsets, "offsets", idx_dtype, numel=desc.T * desc.B + 1)
+    _need(psw, "psw", torch.float32, numel=N)
+    _need(W, "W", _TORCH_W[desc.dtype], numel=sum(desc.rows) * desc.D)
+    _need(momentum, "momentum", torch.float32, numel=sum(desc.rows))
+    _need(out, "out", torch.float32, shape=(desc.B, desc.T * desc.D))
+    _need(grad_out, "grad_out", torch.float32, shape=(desc.B, desc.T * desc.D))
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -213,6 +249,7 @@ def workspace(desc: Desc, N: int, weighted: bool, op: int, device="cuda"):
 
 # --- the three calls ------------------------------------------------------------
 def tbe_forward(desc: Desc, W, indices, offsets, psw, out, meta: Optional[Meta], ws, stream=None):
+    _check_args(desc, torch.int32, W=W, indices=indices, offsets=offsets, psw=psw, out=out)
     N = indices.numel()
     _check(_lib.tbe_forward(desc.ref, _ptr(W), _ptr(indices), _ptr(offsets), N, _ptr(psw),
                             _ptr(out), meta.ref if meta is not None else None, _ptr(ws),
@@ -220,6 +257,7 @@ def tbe_forward(desc: Desc, W, indices, offsets, psw, out, meta: Optional[Meta],
 
 
 def tbe_preprocess(desc: Desc, indices, offsets, psw, meta: Meta, ws, stream=None):
+    _check_args(desc, torch.int32, indices=indices, offsets=offsets, psw=psw)
     N = indices.numel()
     _check(_lib.tbe_preprocess(desc.ref, _ptr(indices), _ptr(offsets), N, _ptr(psw), meta.ref,
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
@@ -228,6 +266,8 @@ def tbe_preprocess(desc: Desc, indices, offsets, psw, meta: Meta, ws, stream=Non
 
 def tbe_backward_adagrad(desc: Desc, W, momentum, grad_out, indices, offsets, psw,
                          meta: Optional[Meta], lr: float, eps: float, ws, stream=None):
+    _check_args(desc, torch.int32, W=W, indices=indices, offsets=offsets, psw=psw,
+                grad_out=grad_out, momentum=momentum)
     N = indices.numel()
     _check(_lib.tbe_backward_adagrad(desc.ref, _ptr(W), _ptr(momentum), _ptr(grad_out),
                                      _ptr(indices), _ptr(offsets), N, _ptr(psw),
@@ -256,6 +296,7 @@ def _need_i64(*tensors):
 
 def tbe_forward_i64(desc: Desc, W, indices, offsets, psw, out, ws, stream=None):
     _need_i64(indices, offsets)
+    _check_args(desc, torch.int64, W=W, indices=indices, offsets=offsets, psw=psw, out=out)
     N = indices.numel()
     _check(_lib.tbe_forward_i64(desc.ref, _ptr(W), _ptr(indices), _ptr(offsets), N, _ptr(psw),
                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
@@ -265,6 +306,8 @@ def tbe_forward_i64(desc: Desc, W, indices, offsets, psw, out, ws, stream=None):
 def tbe_backward_adagrad_i64(desc: Desc, W, momentum, grad_out, indices, offsets, psw,
                              lr: float, eps: float, ws, stream=None):
     _need_i64(indices, offsets)
+    _check_args(desc, torch.int64, W=W, indices=indices, offsets=offsets, psw=psw,
+                grad_out=grad_out, momentum=momentum)
     N = indices.numel()
     _check(_lib.tbe_backward_adagrad_i64(desc.ref, _ptr(W), _ptr(momentum), _ptr(grad_out),
                                          _ptr(indices), _ptr(offsets), N, _ptr(psw), float(lr),

@@ -181,6 +181,7 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
       const size_t parts = (size_t)p.T * (size_t)p.small_splits * kSmallE;
       L.partials = take(sizeof(float) * parts * (size_t)p.D);
       L.part_counts = take(sizeof(int32_t) * parts);
+      L.part_wide = take(sizeof(int32_t) * (size_t)p.T * (size_t)p.small_splits);
     }
   }
   L.total = off;
@@ -387,7 +388,7 @@ tbe_status backward_impl(const tbe_desc* desc, const Problem& p, void* W, float*
     int32_t* pcounts = at<int32_t>(ws, L.part_counts);
     timer_begin(desc->timer, TBE_STAGE_SMALL_BWD, s);
     TBE_TRY_HIP(launch_small_backward(p, grad_out, m.hist, m.counts, indices, offsets, parts,
-                                      pcounts, tinfo, s));
+                                      pcounts, at<int32_t>(ws, L.part_wide), tinfo, s));
     timer_end(desc->timer, TBE_STAGE_SMALL_BWD, s);
     timer_begin(desc->timer, TBE_STAGE_SMALL_APPLY, s);
     TBE_TRY_HIP(launch_small_apply(p, W, momentum, tinfo, parts, pcounts, lr, eps, s));

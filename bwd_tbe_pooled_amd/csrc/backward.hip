@@ -110,11 +110,13 @@ __device__ __forceinline__ void wave_accumulate(const float* __restrict__ grad,
         } else {
           sc[uu] = ok ? 1.f : 0.f;
         }
+        // Slots past the end of the range load nothing: their zero weight
+        // would turn an Inf or NaN in some other bag's row into a NaN here.
         const float* row = gt + (int64_t)(ok ? bag - tB : 0) * ld;
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
           const int e = (p * G + col) * V;
-          if (p < P && e < D) buf[uu][p] = load_vec<float, V>(row + e);
+          if (ok && p < P && e < D) buf[uu][p] = load_vec<float, V>(row + e);
           else buf[uu][p] = GRAW{};
         }
       }
@@ -188,14 +190,17 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
       const int32_t a = __shfl(k0, src), e = __shfl(k1, src), rkey = __shfl(key, src);
       RowState<WT, V, PMAX> st;
       if (act) load_row_state<WT, V, PMAX>(W + (int64_t)rkey * D, mom + rkey, col, G, P, D, st);
+      // Only the run's own lookups are loaded: a run of one lookup issues one
+      // row load, not kTinyMax loads of the same row.
       int32_t bag[kTinyMax];
       float sc[kTinyMax];
+      bool ok[kTinyMax];
 #pragma unroll
       for (int r = 0; r < kTinyMax; ++r) {
-        const bool ok = act && a + r < e;
-        bag[r] = act ? sorted_bag[ok ? a + r : a] : 0;
-        if constexpr (WEIGHTED) sc[r] = ok ? sorted_psw[a + r] : 0.f;
-        else sc[r] = ok ? 1.f : 0.f;
+        ok[r] = act && a + r < e;
+        bag[r] = act ? sorted_bag[ok[r] ? a + r : a] : 0;
+        if constexpr (WEIGHTED) sc[r] = ok[r] ? sorted_psw[a + r] : 0.f;
+        else sc[r] = ok[r] ? 1.f : 0.f;
       }
       const int32_t t = bag[0] / (B > 0 ? B : 1);
       const float* __restrict__ gt = grad + (int64_t)t * D;
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void bwd_short_kernel(
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
           const int ee = (p * G + col) * V;
-          if (act && p < P && ee < D) buf[r][p] = load_vec<float, V>(row + ee);
+          if (ok[r] && p < P && ee < D) buf[r][p] = load_vec<float, V>(row + ee);
           else buf[r][p] = GRAW{};
         }
       }

@@ -78,6 +78,7 @@ struct WsLayout {
   // backward
   size_t partials;     // long-run chunk partials / small-table partials
   size_t part_counts;  // small-table per-split row counts
+  size_t part_wide;    // small-table per-split flag: gradients outside the f16 split's range
   size_t hist;         // small-table counts of a forward given no metadata
   size_t sched;        // long-chunk schedule (order, buckets, list bounds)
   bool has_pre, has_meta, has_partials;
@@ -152,7 +153,7 @@ hipError_t launch_small_pool(const Problem& p, const void* W, const int32_t* ind
 hipError_t launch_small_backward(const Problem& p, const float* grad, const uint8_t* hist,
                                  const int32_t* counts, const int32_t* indices,
                                  const int32_t* offsets, float* partials, int32_t* part_counts,
-                                 const int32_t* tinfo, hipStream_t s);
+                                 int32_t* wide, const int32_t* tinfo, hipStream_t s);
 hipError_t launch_small_apply(const Problem& p, void* W, float* m, const int32_t* tinfo,
                               const float* partials, const int32_t* part_counts, double lr,
                               double eps, hipStream_t s);

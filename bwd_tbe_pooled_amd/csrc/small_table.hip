@@ -9,7 +9,10 @@
 // accumulation). Counts are exact in f16 up to 2048. The backward splits the
 // f32 upstream gradient into hi = f16(g) and lo = f16((g - hi) * 2^11) and
 // contracts H with both (the lo product with H * 2^-11, exact in f16), which
-// compensates the f16 rounding of g to about 2^-22 relative. The forward saves
+// compensates the f16 rounding of g to about 2^-22 relative. The split needs
+// |g| < 65504 (f16's largest finite value): a workgroup that meets a larger
+// or non-finite gradient flags its (table, split), and the f32 kernel then
+// recomputes that partial. The forward saves
 // the counts (uint8, saturating at 255 with a flag) and the backward reuses
 // them; only the counts cross from forward to backward.
 //
@@ -433,14 +436,17 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
 // the split's bags, written to partials[(t*splits + s)][64][D], and the
 // split's per-row counts to part_counts[(t*splits + s)][64]. Wave w owns the
 // 32 columns w*32.. and both 32-row halves of G. Runs only when every count
-// is exact in f16 (counts[5] clear).
+// is exact in f16 (counts[5] clear). Every workgroup writes wide[t*splits + s]:
+// 1 when some gradient of its split is outside the hi/lo split's range
+// (|g| >= 65504, or not finite), so that the f32 kernel launched next
+// recomputes that partial; 0 otherwise.
 __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     const float* __restrict__ grad, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, float* __restrict__ partials,
-    int32_t* __restrict__ part_counts, int32_t T, int32_t B, int32_t D, int64_t ld,
-    int32_t splits, int32_t bags_per_split, const int32_t* __restrict__ trows,
-    int32_t* __restrict__ err) {
+    int32_t* __restrict__ part_counts, int32_t* __restrict__ wide, int32_t T, int32_t B,
+    int32_t D, int64_t ld, int32_t splits, int32_t bags_per_split,
+    const int32_t* __restrict__ trows, int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];     // recounted counts
   __shared__ __align__(16) _Float16 HT[kSmallE][kTStride];     // counts, row-major by table row
   __shared__ int32_t s_off[kBagTile + 1];
@@ -469,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
   uint32_t cnt[2] = {0u, 0u};  // count of row q*32 + i over this lane's half of the bags
+  bool big = false;            // some gradient this lane split is out of the f16 range
 
   // gradient of bag b0 + ks*16 + kb*8 + j at column d, in gn[ks*8 + j]
   float gn[kBagTile / 2];
@@ -510,6 +517,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float g = gn[ks * 8 + j];
+        big |= !(__builtin_fabsf(g) < 65504.f);  // also true for NaN
         const _Float16 h = (_Float16)g;
         hi[ks][j] = h;
         lo[ks][j] = (_Float16)((g - (float)h) * 2048.f);
@@ -559,8 +567,10 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     }
   }
 
+  const int any_big = __syncthreads_or(big ? 1 : 0);
+  if (threadIdx.x == 0) wide[(int64_t)t * splits + s] = any_big ? 1 : 0;
   float* pt = partials + ((int64_t)t * splits + s) * kSmallE * D;
-  if (has_col) {
+  if (has_col && !any_big) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -579,19 +589,22 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
 }
 
 // The same partial sums in plain f32 arithmetic, for problems where some
-// count exceeds 2048 (counts[5] set): counts are recounted from the indices
-// and each thread accumulates 32 (row, column) elements of G over the bags.
+// count exceeds 2048 (counts[5] set; every split), or for the splits whose
+// gradients the matrix-core kernel could not split into f16 halves
+// (wide[t*splits + s] set): counts are recounted from the indices and each
+// thread accumulates 32 (row, column) elements of G over the bags.
 __global__ __launch_bounds__(kThreads) void small_backward_wide_kernel(
     const float* __restrict__ grad, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
-    float* __restrict__ partials, int32_t* __restrict__ part_counts, int32_t T, int32_t B,
-    int32_t D, int64_t ld, int32_t splits, int32_t bags_per_split,
-    const int32_t* __restrict__ trows, int32_t* __restrict__ err) {
+    float* __restrict__ partials, int32_t* __restrict__ part_counts,
+    const int32_t* __restrict__ wide, int32_t T, int32_t B, int32_t D, int64_t ld,
+    int32_t splits, int32_t bags_per_split, const int32_t* __restrict__ trows,
+    int32_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t H[kBagTile][kHStride];
   __shared__ int32_t s_off[kBagTile + 1];
-  if (counts[5] == 0) return;
   const int32_t t = blockIdx.y;
   const int32_t s = blockIdx.x;
+  if (counts[5] == 0 && wide[(int64_t)t * splits + s] == 0) return;
   const int32_t sb0 = s * bags_per_split < B ? s * bags_per_split : B;
   const int32_t sb1 = sb0 + bags_per_split < B ? sb0 + bags_per_split : B;
   const int d = threadIdx.x % kMaxD;
@@ -717,16 +730,18 @@ hipError_t launch_small_pool(const Problem& p, const void* W, const int32_t* ind
 hipError_t launch_small_backward(const Problem& p, const float* grad, const uint8_t* hist,
                                  const int32_t* counts, const int32_t* indices,
                                  const int32_t* offsets, float* partials, int32_t* part_counts,
-                                 const int32_t* tinfo, hipStream_t s) {
+                                 int32_t* wide, const int32_t* tinfo, hipStream_t s) {
   const int splits = p.small_splits;
   int32_t per = (p.B + splits - 1) / splits;
   const dim3 grid((unsigned)splits, (unsigned)p.T);
-  // Exactly one of the two does the work, chosen on the device by counts[5].
+  // Chosen on the device: with counts[5] set only the f32 kernel works; else
+  // the matrix-core kernel computes every split and the f32 kernel redoes the
+  // splits it flagged in `wide` (none, for gradients within f16's range).
   hipLaunchKernelGGL(small_backward_kernel, grid, dim3(kThreads), 0, s, grad, hist, counts, indices,
-                     offsets, partials, part_counts, p.T, p.B, p.D, p.ld, splits, per,
+                     offsets, partials, part_counts, wide, p.T, p.B, p.D, p.ld, splits, per,
                      tinfo + p.T, p.err);
   hipLaunchKernelGGL(small_backward_wide_kernel, grid, dim3(kThreads), 0, s, grad, counts, indices,
-                     offsets, partials, part_counts, p.T, p.B, p.D, p.ld, splits, per,
+                     offsets, partials, part_counts, wide, p.T, p.B, p.D, p.ld, splits, per,
                      tinfo + p.T, p.err);
   return hipGetLastError();
 }
