@@ -87,6 +87,9 @@ _lib.tbe_backward_adagrad_i64.restype = ctypes.c_int
 _lib.tbe_backward_adagrad_i64.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, _P, _P,
                                           ctypes.c_int64, _P, ctypes.c_double, ctypes.c_double,
                                           _P, ctypes.c_size_t, _P]
+_lib.tbe_probe_row_gather.restype = ctypes.c_int
+_lib.tbe_probe_row_gather.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
+TBE_PROBE_SINK_FLOATS = 16384
 _lib.tbe_timer_create.restype = ctypes.c_int
 _lib.tbe_timer_create.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
 _lib.tbe_timer_reset.restype = ctypes.c_int
@@ -315,6 +318,20 @@ def tbe_backward_adagrad_i64(desc: Desc, W, momentum, grad_out, indices, offsets
                                          _stream(stream)), "tbe_backward_adagrad_i64")
 
 
+# --- measurement aid (include/tbe_probe.h) ---------------------------------------------
+def tbe_probe_row_gather(src, rows, sink, stream=None):
+    """Gather rows[i] of the float32 matrix src [R, F] (F = 64, 128 or 256)
+    with the library's load shape; one float per wave to sink."""
+    _need(src, "src", torch.float32)
+    _need(rows, "rows", torch.int32)
+    _need(sink, "sink", torch.float32, numel=TBE_PROBE_SINK_FLOATS)
+    if src.dim() != 2:
+        raise TypeError("src: expected a [rows, floats] matrix")
+    _check(_lib.tbe_probe_row_gather(_ptr(src), src.shape[0], src.shape[1], _ptr(rows),
+                                     rows.numel(), _ptr(sink), _stream(stream)),
+           "tbe_probe_row_gather")
+
+
 # --- stage timer -----------------------------------------------------------------
 class Timer:
     def __init__(self, capacity: int = 256):
@@ -346,5 +363,6 @@ def exported_symbols() -> list:
     """Names the library exports from include/tbe.h (used by host tests)."""
     return ["tbe_status_str", "tbe_last_error", "tbe_select_path", "tbe_meta_capacity", "tbe_workspace_bytes",
             "tbe_forward", "tbe_preprocess", "tbe_backward_adagrad", "tbe_workspace_bytes_i64",
-            "tbe_forward_i64", "tbe_backward_adagrad_i64", "tbe_timer_create",
+            "tbe_forward_i64", "tbe_backward_adagrad_i64", "tbe_probe_row_gather",
+            "tbe_timer_create",
             "tbe_timer_reset", "tbe_timer_read", "tbe_timer_destroy"]

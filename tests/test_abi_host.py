@@ -17,9 +17,13 @@ tbe = pytest.importorskip("bwd_tbe_pooled_amd", reason="libtbe.so not built")
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "tbe.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"\b(tbe_[a-z0-9_]+)\s*\(", src)
+    names = []
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"\b(tbe_[a-z0-9_]+)\s*\(", src)
     return sorted(set(names))
 
 
@@ -235,3 +239,4 @@ def test_build_script_runs_without_the_library():
     env = dict(os.environ, TBE_LIBRARY=os.path.join(root, "no_such_libtbe.so"))
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
