@@ -38,6 +38,7 @@ TBE_PATH_GENERIC, TBE_PATH_SMALL_TABLE = 0, 1
 STAGES = ["fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "bwd_long", "bwd_apply",
           "small_fwd", "small_bwd", "small_apply", "validate", "long_schedule", "small_count"]
 TBE_NUM_STAGES = len(STAGES)
+TBE_NOALLOC_SCRATCH_BYTES = 64 << 20   # built-in scratch of tbe_backward_adagrad_noalloc
 META_FIELDS = ["counts", "run_keys", "run_offsets", "sorted_pos", "sorted_bag", "sorted_psw",
                "short_runs", "long_runs", "long_chunk_begin", "chunk_run", "chunk_start", "hist"]
 TBE_META_NUM_ARRAYS = len(META_FIELDS)
@@ -87,6 +88,10 @@ _lib.tbe_backward_adagrad_i64.restype = ctypes.c_int
 _lib.tbe_backward_adagrad_i64.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, _P, _P,
                                           ctypes.c_int64, _P, ctypes.c_double, ctypes.c_double,
                                           _P, ctypes.c_size_t, _P]
+_lib.tbe_backward_adagrad_noalloc.restype = ctypes.c_int
+_lib.tbe_backward_adagrad_noalloc.argtypes = [ctypes.POINTER(tbe_desc), _P, _P, _P, _P, _P,
+                                              ctypes.c_int64, _P, ctypes.POINTER(tbe_meta),
+                                              ctypes.c_double, ctypes.c_double, _P]
 _lib.tbe_probe_row_gather.restype = ctypes.c_int
 _lib.tbe_probe_row_gather.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int64, _P, _P]
 TBE_PROBE_SINK_FLOATS = 16384
@@ -279,6 +284,21 @@ def tbe_backward_adagrad(desc: Desc, W, momentum, grad_out, indices, offsets, ps
                                      _stream(stream)), "tbe_backward_adagrad")
 
 
+def tbe_backward_adagrad_noalloc(desc: Desc, W, momentum, grad_out, indices, offsets, psw,
+                                 meta: Meta, lr: float, eps: float, stream=None):
+    """tbe_backward_adagrad with metadata and no workspace: the library's
+    built-in per-device scratch (TBE_NOALLOC_SCRATCH_BYTES) serves instead.
+    Calls on one device must not overlap."""
+    _check_args(desc, torch.int32, W=W, indices=indices, offsets=offsets, psw=psw,
+                grad_out=grad_out, momentum=momentum)
+    N = indices.numel()
+    _check(_lib.tbe_backward_adagrad_noalloc(desc.ref, _ptr(W), _ptr(momentum), _ptr(grad_out),
+                                             _ptr(indices), _ptr(offsets), N, _ptr(psw),
+                                             meta.ref if meta is not None else None, float(lr),
+                                             float(eps), _stream(stream)),
+           "tbe_backward_adagrad_noalloc")
+
+
 # --- int64 indices and offsets ----------------------------------------------------
 def tbe_workspace_bytes_i64(desc: Desc, N: int, weighted: bool, op: int) -> int:
     return int(_lib.tbe_workspace_bytes_i64(desc.ref, int(N), int(bool(weighted)), int(op)))
@@ -363,6 +383,6 @@ def exported_symbols() -> list:
     """Names the library exports from include/tbe.h (used by host tests)."""
     return ["tbe_status_str", "tbe_last_error", "tbe_select_path", "tbe_meta_capacity", "tbe_workspace_bytes",
             "tbe_forward", "tbe_preprocess", "tbe_backward_adagrad", "tbe_workspace_bytes_i64",
-            "tbe_forward_i64", "tbe_backward_adagrad_i64", "tbe_probe_row_gather",
-            "tbe_timer_create",
+            "tbe_forward_i64", "tbe_backward_adagrad_i64", "tbe_backward_adagrad_noalloc",
+            "tbe_probe_row_gather", "tbe_timer_create",
             "tbe_timer_reset", "tbe_timer_read", "tbe_timer_destroy"]

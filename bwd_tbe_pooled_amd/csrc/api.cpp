@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -609,9 +610,72 @@ tbe_status run_i64(bool backward, const tbe_desc* d, void* W, float* momentum,
   return TBE_OK;
 }
 
+// --- the backward without allocation ---------------------------------------
+// Scratch of tbe_backward_adagrad_noalloc, one copy per device, held until the
+// process ends. Host code never passes the name `scratch` itself to a kernel
+// or a copy: on the host it is only a stand-in for the device symbol. Each
+// device's address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[TBE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, or null after setting the last-error
+// text.
+void* device_scratch() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_failure(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    std::snprintf(g_last_error, sizeof g_last_error,
+                  "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      hip_failure(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+tbe_status tbe_backward_adagrad_noalloc(const tbe_desc* desc, void* W, float* momentum,
+                                        const float* grad_out, const int32_t* indices,
+                                        const int32_t* offsets, int64_t N, const float* psw,
+                                        const tbe_meta* meta, double lr, double eps,
+                                        void* stream) {
+  Problem p;
+  tbe_status st = make_problem(desc, N, psw != nullptr, &p);
+  if (st != TBE_OK) return st;
+  if (!meta || !W || !momentum || (!grad_out && p.nbags > 0) || !offsets || (!indices && N > 0))
+    return TBE_ERR_ARG;
+  if (!(lr >= 0.0) || !(eps >= 0.0)) return TBE_ERR_ARG;
+  const size_t need = ws_layout(p, TBE_OP_BACKWARD).total;
+  if (need > TBE_NOALLOC_SCRATCH_BYTES) {
+    std::snprintf(g_last_error, sizeof g_last_error,
+                  "the problem needs %zu bytes of scratch; the built-in scratch holds %zu",
+                  need, (size_t)TBE_NOALLOC_SCRATCH_BYTES);
+    return TBE_ERR_WORKSPACE;
+  }
+  void* ws = device_scratch();
+  if (!ws) return TBE_ERR_HIP;
+  return backward_impl(desc, p, W, momentum, grad_out, indices, offsets, psw, meta, lr, eps, ws,
+                       TBE_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
+}
 
 const char* tbe_last_error(void) { return g_last_error; }
 

@@ -18,10 +18,12 @@
  *   pointers marked "host" are ordinary host memory, read during the call only.
  * - The caller owns every buffer. The library never allocates or frees device
  *   memory and keeps no state between calls (a timer, when passed, is the
- *   caller's object) beyond two host-side caches: the text behind
- *   tbe_last_error (per calling thread) and each device's compute-unit count,
- *   queried once. Calls on different streams with disjoint buffers may run
- *   concurrently.
+ *   caller's object) beyond host-side caches: the text behind tbe_last_error
+ *   (per calling thread), each device's compute-unit count, queried once, and
+ *   each device's address of the built-in scratch of
+ *   tbe_backward_adagrad_noalloc (the one device array the library holds
+ *   itself). Calls on different streams with disjoint buffers may run
+ *   concurrently, except tbe_backward_adagrad_noalloc calls on one device.
  * - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it
  *   and the call returns without waiting, except under TBE_FLAG_VALIDATE.
  *   Buffers must stay alive until the stream has passed the call.
@@ -213,9 +215,11 @@ typedef enum {
 const char* tbe_status_str(tbe_status s);
 
 /*
- * After a call returned TBE_ERR_HIP: the HIP error and the step that failed,
- * as text owned by the library (per calling thread, valid until that
- * thread's next failing call; empty before any).
+ * After a call returned TBE_ERR_HIP: the HIP error and the step that failed;
+ * after tbe_backward_adagrad_noalloc returned TBE_ERR_WORKSPACE: the scratch
+ * the problem needs and the scratch there is. Text owned by the library (per
+ * calling thread, valid until that thread's next failing call; empty before
+ * any).
  */
 const char* tbe_last_error(void);
 
@@ -323,6 +327,38 @@ tbe_status tbe_backward_adagrad_i64(const tbe_desc* desc, void* W, float* moment
                                     const int64_t* offsets, int64_t N, const float* psw,
                                     double lr, double eps, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/*
+ * The backward with metadata (as tbe_backward_adagrad with meta != NULL), for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving or training loops, harnesses that forbid allocation. It
+ * takes no workspace: its scratch (table info, chunk partials, the long-run
+ * schedule and its work-queue counters, small-table split partials) is a
+ * static device array of TBE_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each device it runs on, from the first kernel launch of the library on
+ * that device until the process ends. The call allocates nothing, neither
+ * on the device nor on the host.
+ *
+ * Limits: the problem's backward workspace, tbe_workspace_bytes(desc, N,
+ * weighted, TBE_OP_BACKWARD), must be at most TBE_NOALLOC_SCRATCH_BYTES; a
+ * larger one returns TBE_ERR_WORKSPACE before anything is enqueued, with the
+ * sizes in tbe_last_error(). (Generic path at D = 128: about 14M lookups with
+ * f16/bf16 weights, 7M with f32 weights; the small-table path at T = 64,
+ * B = 32768, D = 128 takes 34 MB.) meta must not be NULL (TBE_ERR_ARG).
+ *
+ * All calls on one device share that device's scratch, and each call leaves
+ * its contents behind; the call rewrites or clears everything it reads
+ * before reading it. Two calls that may run at the same time on one device
+ * (different streams, or host threads) race on the scratch and give wrong
+ * results: the caller must order them, e.g. on one stream. Everything else
+ * is as for tbe_backward_adagrad, with the same results bit for bit.
+ */
+#define TBE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+tbe_status tbe_backward_adagrad_noalloc(const tbe_desc* desc, void* W, float* momentum,
+                                        const float* grad_out, const int32_t* indices,
+                                        const int32_t* offsets, int64_t N, const float* psw,
+                                        const tbe_meta* meta, double lr, double eps,
+                                        void* stream);
 
 /*
  * Stage timer. When desc->timer is set, each stage a call runs is bracketed by

@@ -240,3 +240,21 @@ def test_build_script_runs_without_the_library():
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
 
+
+def test_noalloc_refuses_beyond_its_scratch_before_any_work():
+    """The backward without allocation checks the problem's scratch against
+    its built-in array on the host, before any HIP call."""
+    lib = tbe._lib
+    d = _desc(T=2, D=128, B=8, rows=[1000, 1000], dtype="f16")
+    N = 40_000_000
+    assert tbe.tbe_workspace_bytes(d, N, False, tbe.TBE_OP_BACKWARD) > tbe.TBE_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(256)
+    meta = tbe.tbe_meta()
+    st = lib.tbe_backward_adagrad_noalloc(d.ref, fake, fake, fake, fake, fake, N, None,
+                                          ctypes.byref(meta), 0.01, 1e-8, None)
+    assert st == tbe.TBE_ERR_WORKSPACE
+    assert b"scratch" in lib.tbe_last_error()
+    # a missing metadata argument is an argument error
+    st = lib.tbe_backward_adagrad_noalloc(d.ref, fake, fake, fake, fake, fake, 10, None, None,
+                                          0.01, 1e-8, None)
+    assert st == tbe.TBE_ERR_ARG
