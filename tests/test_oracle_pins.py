@@ -425,3 +425,36 @@ def test_route_default_threshold_is_the_pages():
     np.testing.assert_array_equal(r["short_runs"], [0])
     np.testing.assert_array_equal(r["long_runs"], [1, 2])
     np.testing.assert_array_equal(r["long_chunk_begin"], [0, 1, 4])
+
+
+def test_compensated_f16_split_error_bound():
+    """The small-table backward contracts the f32 upstream gradient as two f16
+    halves, hi = f16(g) and lo = f16((g - hi) * 2^11) (the page's compensated
+    f16 high/low product to f32). Their sum recovers g to about 2^-22
+    relative: hi is within 2^-11 of g, the residual g - hi is exact in f32,
+    and lo carries it with another 2^-11 relative error (plus a subnormal
+    floor of 2^-25 / 2^11 = 2^-36 absolute). Checked with numpy's own f16
+    rounding, independent of the library, over the f16 normal range and at
+    the range's end, where hi overflows and the split no longer holds."""
+    rng = np.random.default_rng(2024)
+    mag = np.exp2(rng.uniform(-14.0, np.log2(65504.0), 400_000))
+    g = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    g = np.concatenate([g, np.float32([1.0, -1.0, 65504.0, -65504.0, 2.0 ** -14, 3.0e-5,
+                                       np.nextafter(np.float32(65504.0), np.float32(0))])])
+    hi = g.astype(np.float16)
+    r = g - hi.astype(np.float32)                       # exact in f32
+    lo = (r * np.float32(2048.0)).astype(np.float16)
+    back = hi.astype(np.float64) + lo.astype(np.float64) / 2048.0
+    err = np.abs(back - g.astype(np.float64))
+    assert np.all(np.isfinite(hi)) and np.all(np.isfinite(lo))
+    assert np.all(err <= 2.0 ** -22 * np.abs(g.astype(np.float64)) + 2.0 ** -36)
+    # the bound is tight to within a factor of a few: a plain f16 rounding of
+    # g alone is 2^11 times worse, so the lo half is doing the work
+    assert np.median(err / np.abs(g)) < 2.0 ** -24
+    plain = np.abs(hi.astype(np.float64) - g)
+    assert np.median(plain / np.abs(g)) > 2.0 ** -14
+    # beyond f16's largest finite value the high half overflows: such
+    # gradients cannot take this path (the library redoes them in f32)
+    big = np.float32([65520.0, 1.0e5, -3.0e9])
+    with np.errstate(over="ignore"):
+        assert np.all(np.isinf(big.astype(np.float16)))
