@@ -11,9 +11,11 @@ The oracle cannot redo 84M lookups in seconds, so:
   stable sort uniquely (permutation; keys non-decreasing; equal keys in
   increasing position), exact RLE of the sorted keys, and the oracle's routing
   of the GPU's run lengths compared element by element;
-- outputs and updated rows are checked on samples the oracle computes one by
-  one: random bags (forward) and the hottest plus random rows (backward, with
-  every lookup of each sampled row)."""
+- the forward is checked on 50,000 random bags spread over all tables;
+- the backward is checked on every long run (segment length >= 256: the
+  chunk path, its per-XCD schedule and work queue, and the apply) and on
+  short runs sampled evenly from each segment-length band (1, 2-4, 5-255),
+  each row with every one of its lookups, against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -39,7 +41,8 @@ def _mask(n, members):
     return mk
 
 
-def _sampled_backward(cfg, batch, keys, bags, W, m, Wrows_all, mrows_all, uk, sample_keys):
+def _sampled_backward(cfg, batch, keys, bags, W, m, Wrows_all, mrows_all, uk, sample_keys,
+                      label="sampled rows"):
     sel = _mask(cfg.sum_rows, sample_keys)[keys]
     pos = np.nonzero(sel)[0]
     sk = keys[pos]
@@ -49,11 +52,27 @@ def _sampled_backward(cfg, batch, keys, bags, W, m, Wrows_all, mrows_all, uk, sa
     sub_bags = bags[pos]
     sub_psw = None if batch.psw is None else batch.psw[pos]
     r = oracle.rle(sub_keys, np.arange(pos.size, dtype=np.int32), sub_bags, sub_psw)
+    del sel, sk, order, sub_keys, sub_bags, sub_psw
     at = np.searchsorted(uk, r["run_keys"])
     bw = oracle.backward_adagrad(cfg.T, cfg.B, cfg.D, cfg.dtype, r["run_keys"], r["run_offsets"],
                                  r["sorted_bag"], r["sorted_psw"], batch.grad, Wrows_all[at],
                                  mrows_all[at], cfg.lr, cfg.eps, wkeys=r["run_keys"])
-    assert_rows_match(cfg, W, m, r["run_keys"], bw["w_new"], bw["m_new"], "sampled rows")
+    err, ulps = assert_rows_match(cfg, W, m, r["run_keys"], bw["w_new"], bw["m_new"], label)
+    print(f"[full] {label}: {r['run_keys'].size} rows, {pos.size} lookups, rel err {err:.2e}, "
+          f"max {ulps} ulp", flush=True)
+    return r["run_keys"].size, pos.size
+
+
+def _backward_sample(counts, uk, rng, per_band=3000):
+    """Every key of a long run (segment length >= 256) and up to `per_band`
+    keys from each short band: 1, 2-4 and 5-255 lookups."""
+    long_keys = uk[counts >= 256]
+    bands = {}
+    for name, lo, hi in (("SL 1", 1, 1), ("SL 2-4", 2, 4), ("SL 5-255", 5, 255)):
+        cand = uk[(counts >= lo) & (counts <= hi)]
+        bands[name] = (rng.choice(cand, min(per_band, cand.size), replace=False)
+                       if cand.size else cand)
+    return long_keys, bands
 
 
 @pytest.mark.parametrize("rows", ["zipf", "uniform"])
@@ -72,9 +91,10 @@ def test_large_workload_full_size(rows):
     W, m = fresh_params(cfg)
     W0, m0 = W.clone(), m.clone()
     rng = np.random.default_rng(123)
-    hot = uk[np.argsort(counts)[-12:]]
-    sample_keys = np.unique(np.concatenate([hot, rng.choice(uk, 300, replace=False)]))
-    sample_bags = rng.choice(cfg.T * cfg.B, 3000, replace=False).astype(np.int32)
+    long_keys, bands = _backward_sample(counts, uk, rng)
+    sample_keys = np.unique(np.concatenate([long_keys, *bands.values()])).astype(np.int32)
+    sample_bags = rng.choice(cfg.T * cfg.B, 50_000, replace=False).astype(np.int32)
+    assert np.unique(sample_bags // cfg.B).size == cfg.T
     need = np.unique(np.concatenate([sample_keys, keys[_mask(cfg.T * cfg.B, sample_bags)[bags]]]))
     Wrows, mrows = host_rows(W0, m0, need)
     print("[full] running the library", flush=True)
@@ -89,6 +109,8 @@ def test_large_workload_full_size(rows):
               torch.from_numpy(t.astype(np.int64)).cuda()].cpu().numpy()
     err = rel_err(got, ob)
     assert err <= TOL[cfg.dtype], f"forward rel err {err:.3g}"
+    print(f"[full] forward: {sample_bags.size} bags of {cfg.T} tables, rel err {err:.2e}",
+          flush=True)
 
     # metadata by defining properties and the oracle's routing
     print("[full] checking metadata", flush=True)
@@ -112,8 +134,15 @@ def test_large_workload_full_size(rows):
     if rows == "uniform":
         assert route["short_runs"].size > 65536 * 4 * 64
 
-    # backward on sampled rows, then untouched rows
-    _sampled_backward(cfg, batch, keys, bags, W, m, Wrows, mrows, need, sample_keys)
+    # backward: every long run, then each short band, then untouched rows
+    if long_keys.size:
+        n_rows, n_look = _sampled_backward(cfg, batch, keys, bags, W, m, Wrows, mrows, need,
+                                           long_keys, "every long run")
+        assert n_rows == route["long_runs"].size
+        assert n_look == int(counts[counts >= 256].sum())
+    for name, band_keys in bands.items():
+        if band_keys.size:
+            _sampled_backward(cfg, batch, keys, bags, W, m, Wrows, mrows, need, band_keys, name)
     assert_untouched_unchanged(W0, W, m0, m, uk)
 
 
