@@ -549,6 +549,9 @@ def main():
     ap.add_argument("--rows", choices=["zipf", "uniform"], default="zipf",
                     help="row distribution of the large workload: Zipf-Mandelbrot (default) or "
                          "uniform (a diagnostic without reuse)")
+    ap.add_argument("--tables", type=int, default=32,
+                    help="tables of the large workload (diagnostic: other values keep every "
+                         "table's shape and distribution; 32 is the headline)")
     ap.add_argument("--index", choices=["int32", "int64"], default="int32",
                     help="index arrays: int32 (default) or int64 through the _i64 entry points "
                          "(which preprocess inside the backward)")
@@ -573,7 +576,7 @@ def main():
     dev = torch.device("cuda")
     scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     diagnostic = (args.check != "none" or args.preprocess != "forward" or args.long != "two_launch"
-                  or args.rows != "zipf" or args.index != "int32")
+                  or args.rows != "zipf" or args.index != "int32" or args.tables != 32)
 
     if args.workload == "small":
         cfg = SMALL_TABLE
@@ -586,6 +589,8 @@ def main():
         dtype = "f16"
     else:
         cfg = LARGE if args.rows == "zipf" else dataclasses.replace(LARGE, index=("uniform",))
+        if args.tables != 32:
+            cfg = dataclasses.replace(cfg, T=args.tables, rows=(cfg.rows[0],) * args.tables)
         log("generating the headline batch")
         batch = make_batch(cfg)
         head = measure_generic(torch, tbe, cfg, batch, args, scratch, headline=True)
@@ -683,7 +688,8 @@ def main():
                    + ("" if args.preprocess == "forward" else ", preprocessing in the backward")
                    + ("" if args.check == "none" else f", index check {args.check}")
                    + ("" if args.long == "two_launch" else ", long runs in one launch")
-                   + ("" if args.index == "int32" else ", int64 indices"),
+                   + ("" if args.index == "int32" else ", int64 indices")
+                   + ("" if args.tables == 32 else f", {args.tables} tables"),
                    **head["shape"], "parallelism": "single GPU"},
         "flushed_ms_per_step": head["flushed_ms_per_step"],
         "graph_ms_per_step": head["graph_ms_per_step"],

@@ -478,13 +478,25 @@ __global__ __launch_bounds__(256) void sched_count_kernel(
     const int32_t bag0 = sorted_bag[k0], bag1 = sorted_bag[klast];
     const int32_t bag = bag0 + (bag1 - bag0) / 2;
     const int32_t t = bag / B, b = bag - t * B;
-    const int x = (int)(((int64_t)t * kXcds) / T);
-    const int t0 = (int)(((int64_t)x * T + kXcds - 1) / kXcds);  // first table of block x
-    const int t1 = (int)(((int64_t)(x + 1) * T + kXcds - 1) / kXcds);
-    const int ngrp = (t1 - t0 + kSchedTables - 1) / kSchedTables;
-    const int per = kSchedBuckets / ngrp;  // buckets per table group (0 past 4096 groups)
-    const int g = (t - t0) / kSchedTables;
-    const int bk = x * kSchedBuckets + g * per + (int)(((int64_t)b * per) / B);
+    int bk;
+    if (T % kXcds == 0) {
+      // T/8 whole tables per XCD, walked kSchedTables at a time in bag order
+      const int x = (int)(((int64_t)t * kXcds) / T);
+      const int t0 = (int)(((int64_t)x * T + kXcds - 1) / kXcds);  // first table of block x
+      const int t1 = (int)(((int64_t)(x + 1) * T + kXcds - 1) / kXcds);
+      const int ngrp = (t1 - t0 + kSchedTables - 1) / kSchedTables;
+      const int per = kSchedBuckets / ngrp;  // buckets per table group (0 past 4096 groups)
+      const int g = (t - t0) / kSchedTables;
+      bk = x * kSchedBuckets + g * per + (int)(((int64_t)b * per) / B);
+    } else {
+      // Otherwise whole tables per XCD would leave XCDs idle (T < 8) or give
+      // some twice the work of others (e.g. 13 tables: blocks of 2 and 1).
+      // Each chunk gets a position on the tables laid end to end, t + b / B,
+      // scaled to 8 XCDs: XCD x takes positions [x, x + 1), so a table's bags
+      // are split over XCDs in proportion, walked in position order.
+      const int64_t pos = (((int64_t)t * B + b) * kXcds * kSchedBuckets) / ((int64_t)T * B);
+      bk = (int)pos;  // = x * kSchedBuckets + bucket within XCD x
+    }
     bucket_of[c] = bk;
     atomicAdd(&hist[bk], 1);
   }
