@@ -258,3 +258,15 @@ def test_noalloc_refuses_beyond_its_scratch_before_any_work():
     st = lib.tbe_backward_adagrad_noalloc(d.ref, fake, fake, fake, fake, fake, 10, None, None,
                                           0.01, 1e-8, None)
     assert st == tbe.TBE_ERR_ARG
+
+
+def test_binding_rejects_host_tensors():
+    """The wrappers pass raw device pointers: a host tensor is refused before
+    any call."""
+    d = _desc(T=2, D=16, B=4, rows=[100, 50], dtype="f32")
+    idx = torch.zeros(8, dtype=torch.int32)
+    off = torch.arange(0, 9, dtype=torch.int32)
+    W = torch.zeros((150, 16), dtype=torch.float32)
+    out = torch.zeros((4, 32), dtype=torch.float32)
+    with pytest.raises(TypeError, match="device"):
+        tbe.tbe_forward(d, W, idx, off, None, out, None, torch.zeros(1024, dtype=torch.uint8))

@@ -344,3 +344,35 @@ def test_fused_check_is_silent_and_bitwise_neutral_on_valid_input():
     assert int(err.item()) == 0
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a, b)
+
+
+def test_binding_rejects_mistyped_tensors():
+    """int64 indices given to the int32 calls, strided outputs, wrong weight
+    dtypes and wrong sizes are refused with a TypeError before any launch."""
+    import bwd_tbe_pooled_amd as tbe
+    cfg = TINY
+    batch = make_batch(cfg)
+    desc = make_desc(cfg)
+    dev = "cuda"
+    idx = torch.from_numpy(batch.indices).to(dev)
+    off = torch.from_numpy(batch.offsets).to(dev)
+    W, m = fresh_params(cfg)
+    out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device=dev)
+    ws = tbe.workspace(desc, idx.numel(), False, tbe.TBE_OP_FORWARD)
+    bad = [
+        dict(indices=idx.long()),                                   # int64 as int32
+        dict(offsets=off.long()),
+        dict(offsets=off[:-1]),                                     # T*B offsets, not T*B + 1
+        dict(W=W.half()),                                           # weight dtype
+        dict(out=torch.empty((cfg.T * cfg.D, cfg.B), device=dev).t()),  # strided view
+        dict(out=torch.empty((cfg.B, cfg.T * cfg.D + 1), device=dev)),
+    ]
+    for b in bad:
+        a = dict(W=W, indices=idx, offsets=off, out=out)
+        a.update(b)
+        with pytest.raises(TypeError):
+            tbe.tbe_forward(desc, a["W"], a["indices"], a["offsets"], None, a["out"], None, ws)
+    grad = torch.zeros((cfg.B, cfg.T * cfg.D), device=dev)
+    with pytest.raises(TypeError):
+        tbe.tbe_backward_adagrad(desc, W, m.double(), grad, idx, off, None, None, cfg.lr, cfg.eps,
+                                 tbe.workspace(desc, idx.numel(), False, tbe.TBE_OP_BACKWARD_SELF))
