@@ -6,13 +6,17 @@
 //     forward   out[b, t-block] = H_t[b, :] . W_t            ([B x 64] x [64 x D])
 //     backward  G_t = H_t^T . grad_t                         ([64 x B] x [B x D])
 // both on the matrix cores (v_mfma_f32_32x32x16_f16: f16 inputs, f32
-// accumulation). Counts are exact in f16 up to 2048. The backward splits the
-// f32 upstream gradient into hi = f16(g) and lo = f16((g - hi) * 2^11) and
-// contracts H with both (the lo product with H * 2^-11, exact in f16), which
-// compensates the f16 rounding of g to about 2^-22 relative. The split needs
-// |g| < 65504 (f16's largest finite value): a workgroup that meets a larger
-// or non-finite gradient flags its (table, split), and the f32 kernel then
-// recomputes that partial. The forward saves
+// accumulation). Counts are exact in f16 up to 2048. The backward scales each
+// gradient column by a power of two 2^s that brings its magnitudes near
+// [2^8, 2^9), splits the scaled value x into
+// hi = f16(x) and lo = f16((x - hi) * 2^11), contracts H with both (the lo
+// product with H * 2^-11, exact in f16) and unscales the sums by 2^-s at the
+// end. That compensates the f16 rounding to about 2^-22 relative for every
+// gradient down to 2^-23 of the column's first largest, whatever its magnitude.
+// The scale of a column is set by its first tile with a nonzero gradient; a
+// workgroup that meets a tile far outside it, or a non-finite gradient, flags
+// its (table, split), and the f32 kernel then recomputes that partial. The
+// forward saves
 // the counts (uint8, saturating at 255 with a flag) and the backward reuses
 // them; only the counts cross from forward to backward.
 //
@@ -437,9 +441,10 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
 // split's per-row counts to part_counts[(t*splits + s)][64]. Wave w owns the
 // 32 columns w*32.. and both 32-row halves of G. Runs only when every count
 // is exact in f16 (counts[5] clear). Every workgroup writes wide[t*splits + s]:
-// 1 when some gradient of its split is outside the hi/lo split's range
-// (|g| >= 65504, or not finite), so that the f32 kernel launched next
-// recomputes that partial; 0 otherwise.
+// 1 when some gradient of its split is not finite (the Inf or NaN then reaches
+// the rows as plain arithmetic carries it) or lies outside its column's
+// scaled range, so that the f32 kernel launched next recomputes that partial;
+// 0 otherwise.
 __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     const float* __restrict__ grad, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
@@ -475,7 +480,9 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
   uint32_t cnt[2] = {0u, 0u};  // count of row q*32 + i over this lane's half of the bags
-  bool big = false;            // some gradient this lane split is out of the f16 range
+  bool big = false;            // some gradient this lane split is not finite or out of scale
+  int sc = 0;                  // this column's scale: the sums are in units of 2^-sc
+  bool has_sc = false;         // set by the first tile with a nonzero gradient
 
   // gradient of bag b0 + ks*16 + kb*8 + j at column d, in gn[ks*8 + j]
   float gn[kBagTile / 2];
@@ -508,19 +515,44 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
   for (int32_t b0 = sb0; b0 < sb1; b0 += kBagTile) {
     const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
     const int64_t bag0 = (int64_t)t * B + b0;
-    // B operands: this tile's gradients split into hi = f16(g) and
-    // lo = f16((g - hi) * 2^11).
+    // B operands: this tile's gradients of column d times 2^sc, split into
+    // hi = f16(x) and lo = f16((x - hi) * 2^11). sc is a power-of-two scale
+    // per column (lanes i and i + 32 agree on it), set by the first tile with
+    // a nonzero gradient so that its largest magnitude lands in [2^8, 2^9):
+    // gradients far below 1 would otherwise fall into f16's subnormals, and
+    // above 65504 overflow. The sums are in units of 2^-sc, unscaled once at
+    // the end (exact). A later tile whose largest scaled magnitude leaves
+    // [2^-6, 2^15) (64 times the first tile's largest, or 2^14 times less)
+    // marks the split for the f32 kernel, like a non-finite one.
     load_grad(b0);
+    {
+      float gmax = 0.f;
+#pragma unroll
+      for (int q = 0; q < kBagTile / 2; ++q) {
+        const float a = __builtin_fabsf(gn[q]);
+        big |= !(a <= 3.402823466e38f);  // Inf or NaN
+        gmax = a > gmax && a <= 3.402823466e38f ? a : gmax;
+      }
+      gmax = fmaxf(gmax, __shfl_xor(gmax, 32));
+      if (gmax > 0.f) {
+        const int e = __builtin_amdgcn_frexp_expf(gmax);  // gmax in [2^(e-1), 2^e)
+        if (!has_sc) {
+          sc = 9 - e;
+          has_sc = true;
+        } else if (e + sc > 15 || e + sc < -5) {
+          big = true;
+        }
+      }
+    }
     half8 hi[kBagTile / 16], lo[kBagTile / 16];
 #pragma unroll
     for (int ks = 0; ks < kBagTile / 16; ++ks)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float g = gn[ks * 8 + j];
-        big |= !(__builtin_fabsf(g) < 65504.f);  // also true for NaN
-        const _Float16 h = (_Float16)g;
+        const float x = __builtin_ldexpf(gn[ks * 8 + j], sc);
+        const _Float16 h = (_Float16)x;
         hi[ks][j] = h;
-        lo[ks][j] = (_Float16)((g - (float)h) * 2048.f);
+        lo[ks][j] = (_Float16)((x - (float)h) * 2048.f);
       }
 
     if (recount) count_tile(H, s_off, indices, offsets, bag0, nb, (uint32_t)trows[t], err);
@@ -566,6 +598,10 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
       }
     }
   }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = __builtin_ldexpf(acc[mt][r], -sc);
 
   const int any_big = __syncthreads_or(big ? 1 : 0);
   if (threadIdx.x == 0) wide[(int64_t)t * splits + s] = any_big ? 1 : 0;
@@ -736,7 +772,7 @@ hipError_t launch_small_backward(const Problem& p, const float* grad, const uint
   const dim3 grid((unsigned)splits, (unsigned)p.T);
   // Chosen on the device: with counts[5] set only the f32 kernel works; else
   // the matrix-core kernel computes every split and the f32 kernel redoes the
-  // splits it flagged in `wide` (none, for gradients within f16's range).
+  // splits it flagged in `wide` (none, for finite gradients).
   hipLaunchKernelGGL(small_backward_kernel, grid, dim3(kThreads), 0, s, grad, hist, counts, indices,
                      offsets, partials, part_counts, wide, p.T, p.B, p.D, p.ld, splits, per,
                      tinfo + p.T, p.err);

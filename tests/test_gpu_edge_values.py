@@ -3,9 +3,11 @@ against the oracle:
 - an infinite gradient row of bag (t, 0) must reach only the rows that bag
   looks up: every other row stays finite and matches the oracle (the
   backward's gather lanes past the end of a run load nothing);
-- on the small-table path, gradients beyond f16's range (|g| >= 65504) do not
-  fit the compensated f16 hi/lo split: the splits that hold them are redone
-  in f32 arithmetic and every updated row matches the oracle."""
+- on the small-table path, the compensated f16 hi/lo split works on each
+  gradient column scaled by a power of two: gradients far below 1 (which
+  unscaled would fall into f16's subnormals and lose most of their bits) and
+  far above f16's largest value match the oracle, and a tile far outside its
+  column's scale is redone in f32 arithmetic."""
 import numpy as np
 import pytest
 import torch
@@ -57,6 +59,9 @@ def test_infinite_gradient_row_stays_in_its_own_rows(S, C):
 
 
 def test_small_table_gradients_beyond_f16_range():
+    """Entries above 65504 in a few bags: the first tile's 1e5 sets its
+    column's scale; 3e9 in a later tile is beyond that scale and its split is
+    redone in f32."""
     batch = make_batch(SMALL_TABLE, B=1024)
     cfg = batch.cfg
     grad = batch.grad.copy()
@@ -79,3 +84,42 @@ def test_small_table_gradients_beyond_f16_range():
     assert np.isfinite(bw["w_new"]).all()
     assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], "small-table wide g")
     assert rel_err(r["out"].cpu().numpy(), out) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("scale", [1e-6, 1e-15, 1e12])
+def test_small_table_gradient_magnitudes(scale):
+    """The whole upstream gradient times `scale`. At 1e-6 an unscaled f16 split
+    would keep about 15 bits of each gradient (f16's subnormals start at
+    6e-5), enough to put the Adagrad state off by several 1e-5."""
+    batch = make_batch(SMALL_TABLE, B=2048)
+    cfg = batch.cfg
+    batch.grad = (batch.grad.astype(np.float64) * scale).astype(np.float32)
+    print(f"\n[edge] small-table gradients times {scale:g}", flush=True)
+    W, m = fresh_params(cfg)
+    keys, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
+    uk = np.unique(keys)
+    Wrows, mrows = host_rows(W, m, uk)
+    r = run_library(cfg, batch, W, m, meta_in_forward=True)
+    assert r["path"] == 1
+    pre, _, bw = oracle_all(cfg, batch, Wrows, mrows, uk)
+    assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"],
+                      f"small-table g x {scale:g}")
+
+
+def test_small_table_gradient_magnitudes_per_bag():
+    """Each bag's gradient row times 10^u, u uniform in [-6, 0]: one column
+    mixes magnitudes six decades apart, within the split's scaled range."""
+    batch = make_batch(SMALL_TABLE, B=2048)
+    cfg = batch.cfg
+    rng = np.random.default_rng(19)
+    f = 10.0 ** rng.uniform(-6, 0, size=(cfg.B, 1))
+    batch.grad = (batch.grad.astype(np.float64) * f).astype(np.float32)
+    W, m = fresh_params(cfg)
+    keys, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, batch.indices, batch.offsets)
+    uk = np.unique(keys)
+    Wrows, mrows = host_rows(W, m, uk)
+    r = run_library(cfg, batch, W, m, meta_in_forward=True)
+    assert r["path"] == 1
+    pre, _, bw = oracle_all(cfg, batch, Wrows, mrows, uk)
+    assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"],
+                      "small-table g per-bag magnitudes")
