@@ -330,7 +330,8 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
 
     fwd_ms = avg["fwd_pool"]
     pre_ms = avg["linearize"] + avg["sort"] + avg["rle_route"]
-    bwd_ms = avg["bwd_short"] + avg["long_schedule"] + avg["bwd_long"] + avg["bwd_apply"]
+    bwd_ms = (avg["bwd_short"] + avg.get("bwd_hot", 0.0) + avg["long_schedule"] + avg["bwd_long"]
+              + avg["bwd_apply"])
     eff = effective_bytes(cfg, N, st["U"], st["n_chunks"], st["long_lookups"], weighted, st["n_long"])
     comp = compulsory_bytes(cfg, st, weighted)
     res = {

@@ -31,12 +31,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 TBE_OK, TBE_ERR_ARG, TBE_ERR_UNSUPPORTED, TBE_ERR_WORKSPACE, TBE_ERR_INDEX_RANGE, TBE_ERR_HIP = range(6)
 TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
 TBE_FLAG_VALIDATE, TBE_FLAG_FORCE_GENERIC, TBE_FLAG_CHECK, TBE_FLAG_FUSED_LONG = 0x1, 0x2, 0x4, 0x8
+TBE_FLAG_NO_HOT_ROWS = 0x10
 TBE_ERROR_INDEX = 0x1
 TBE_PATH_GENERIC, TBE_PATH_SMALL_TABLE = 0, 1
 (TBE_OP_FORWARD, TBE_OP_FORWARD_PREPROCESS, TBE_OP_PREPROCESS, TBE_OP_BACKWARD,
  TBE_OP_BACKWARD_SELF) = range(5)
 STAGES = ["fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "bwd_long", "bwd_apply",
-          "small_fwd", "small_bwd", "small_apply", "validate", "long_schedule", "small_count"]
+          "small_fwd", "small_bwd", "small_apply", "validate", "long_schedule", "small_count",
+          "bwd_hot"]
 TBE_NUM_STAGES = len(STAGES)
 TBE_NOALLOC_SCRATCH_BYTES = 64 << 20   # built-in scratch of tbe_backward_adagrad_noalloc
 META_FIELDS = ["counts", "run_keys", "run_offsets", "sorted_pos", "sorted_bag", "sorted_psw",

@@ -26,8 +26,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC]
 
-SOURCES = ["api.cpp", "util.hip", "forward.hip", "sort.hip", "rle_route.hip", "backward.hip", "probe.hip",
-           "small_table.hip"]
+SOURCES = ["api.cpp", "util.hip", "forward.hip", "hot_rows.hip", "sort.hip", "rle_route.hip",
+           "backward.hip", "hot_backward.hip", "probe.hip", "small_table.hip"]
 
 
 def _compile(src: str) -> str:

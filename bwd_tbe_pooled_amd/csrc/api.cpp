@@ -50,7 +50,8 @@ static tbe_status check_desc(const tbe_desc* d, int64_t N, int64_t* sum, int64_t
   if (d->T < 1 || d->D < 1 || d->B < 0 || N < 0) return TBE_ERR_ARG;
   if (d->wdtype != TBE_F32 && d->wdtype != TBE_F16 && d->wdtype != TBE_BF16) return TBE_ERR_UNSUPPORTED;
   if (d->flags &
-      ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC | TBE_FLAG_CHECK | TBE_FLAG_FUSED_LONG))
+      ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC | TBE_FLAG_CHECK | TBE_FLAG_FUSED_LONG |
+        TBE_FLAG_NO_HOT_ROWS))
     return TBE_ERR_ARG;
   if ((d->flags & TBE_FLAG_CHECK) && !d->error_flags) return TBE_ERR_ARG;
   if (d->short_max < 0 || d->chunk < 0) return TBE_ERR_ARG;
@@ -80,6 +81,9 @@ static void derive_sizes(Problem* p) {
   p->cap_chunks = p->cap_long ? p->N / p->C + p->cap_long : 0;
   p->small_splits = small_splits_for(p->T, p->B);
   p->ld = (int64_t)p->T * p->D;
+  choose_hot(p);
+  p->hot_bwd = hot_backward_eligible(*p);  // reads no_hot: set before this
+  p->hot_nseg = p->hot_bwd ? hot_backward_segments(*p) : 0;
 }
 
 tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) {
@@ -103,9 +107,10 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   p->S = d->short_max ? d->short_max : kDefaultShortMax;
   p->C = d->chunk ? d->chunk : kDefaultChunk;
   p->path = small_eligible(d, N, weighted, mx) ? TBE_PATH_SMALL_TABLE : TBE_PATH_GENERIC;
+  p->fused_long = (d->flags & TBE_FLAG_FUSED_LONG) != 0;
+  p->no_hot = (d->flags & (TBE_FLAG_NO_HOT_ROWS | TBE_FLAG_FUSED_LONG)) != 0;
   derive_sizes(p);
   p->err = (d->flags & TBE_FLAG_CHECK) ? d->error_flags : nullptr;
-  p->fused_long = (d->flags & TBE_FLAG_FUSED_LONG) != 0;
   return TBE_OK;
 }
 
@@ -164,6 +169,8 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
     L.route_tiles = take(sizeof(int32_t) * (size_t)(3 * rt + 4));
   }
   if (!generic && op == TBE_OP_FORWARD) L.hist = take((size_t)p.nbags * kSmallE);
+  if (generic && op == TBE_OP_FORWARD_PREPROCESS && p.hot_k > 0)
+    L.hot_rows = take(sizeof(int32_t) * (size_t)p.T * (size_t)p.hot_k);
   L.has_meta = op == TBE_OP_BACKWARD_SELF;
   if (L.has_meta) {
     int64_t caps[TBE_META_NUM_ARRAYS];
@@ -178,6 +185,13 @@ WsLayout ws_layout(const Problem& p, tbe_op op) {
       const size_t acc = p.wdtype == TBE_F32 ? 8 : 4;
       L.partials = take(acc * (size_t)p.cap_chunks * (size_t)p.D);
       L.sched = take(sizeof(int32_t) * long_schedule_ints(p));
+      if (p.hot_bwd) {
+        L.hb_rows = take(sizeof(int32_t) * (size_t)p.T * 256);
+        L.hb_run_slot = take(sizeof(int32_t) * (size_t)p.cap_long);
+        L.hb_min = take(sizeof(int32_t) * (size_t)p.T);
+        L.hb_flag = take(sizeof(int32_t) * (size_t)p.T);
+        L.hb_parts = take(sizeof(float) * (size_t)p.T * (size_t)p.hot_nseg * 256 * (size_t)p.D);
+      }
     } else {
       const size_t parts = (size_t)p.T * (size_t)p.small_splits * kSmallE;
       L.partials = take(sizeof(float) * parts * (size_t)p.D);
@@ -357,6 +371,17 @@ tbe_status forward_impl(const tbe_desc* desc, const Problem& p, const void* W,
     timer_end(desc->timer, TBE_STAGE_SMALL_FWD, s);
     return TBE_OK;
   }
+  if (meta && p.hot_k > 0) {
+    // the transpose first: its longest runs are the rows the pool then reads
+    // from LDS (same values, same order: the same output bits)
+    if ((st = run_preprocess(desc, p, indices, offsets, psw, *meta, ws, L, s)) != TBE_OK) return st;
+    int32_t* hot = at<int32_t>(ws, L.hot_rows);
+    timer_begin(desc->timer, TBE_STAGE_FWD_POOL, s);
+    TBE_TRY_HIP(launch_hot_plan(p, *meta, tinfo, p.hot_k, hot, nullptr, nullptr, nullptr, s));
+    TBE_TRY_HIP(launch_forward_pool_hot(p, W, indices, offsets, psw, tinfo, hot, out, s));
+    timer_end(desc->timer, TBE_STAGE_FWD_POOL, s);
+    return TBE_OK;
+  }
   timer_begin(desc->timer, TBE_STAGE_FWD_POOL, s);
   TBE_TRY_HIP(launch_forward_pool(p, W, indices, offsets, psw, tinfo, out, s));
   timer_end(desc->timer, TBE_STAGE_FWD_POOL, s);
@@ -404,8 +429,27 @@ tbe_status backward_impl(const tbe_desc* desc, const Problem& p, void* W, float*
   timer_begin(desc->timer, TBE_STAGE_BWD_SHORT, s);
   TBE_TRY_HIP(launch_bwd_short(p, W, momentum, grad_out, m, tinfo, lr, eps, s));
   timer_end(desc->timer, TBE_STAGE_BWD_SHORT, s);
+  HotBwd hot{};
+  if (p.hot_bwd) {
+    // the hot rows' plan, then their contraction; tables it flags go back to
+    // the chunk path below
+    int32_t* hb_rows = at<int32_t>(ws, L.hb_rows);
+    int32_t* hb_flag = at<int32_t>(ws, L.hb_flag);
+    float* hb_parts = at<float>(ws, L.hb_parts);
+    hot.run_slot = at<int32_t>(ws, L.hb_run_slot);
+    hot.hot_min = at<int32_t>(ws, L.hb_min);
+    hot.hot_flag = hb_flag;
+    hot.parts = hb_parts;
+    hot.nseg = p.hot_nseg;
+    timer_begin(desc->timer, TBE_STAGE_BWD_HOT, s);
+    TBE_TRY_HIP(launch_hot_plan(p, m, tinfo, 256, hb_rows, at<int32_t>(ws, L.hb_run_slot),
+                                at<int32_t>(ws, L.hb_min), hb_flag, s));
+    TBE_TRY_HIP(launch_bwd_hot(p, grad_out, indices, offsets, psw, hb_rows, tinfo, hb_parts,
+                               hb_flag, s));
+    timer_end(desc->timer, TBE_STAGE_BWD_HOT, s);
+  }
   timer_begin(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
-  TBE_TRY_HIP(launch_long_schedule(p, m, at<int32_t>(ws, L.sched), s));
+  TBE_TRY_HIP(launch_long_schedule(p, m, at<int32_t>(ws, L.sched), hot, s));
   timer_end(desc->timer, TBE_STAGE_LONG_SCHEDULE, s);
   timer_begin(desc->timer, TBE_STAGE_BWD_LONG, s);
   if (p.fused_long) {
@@ -417,7 +461,7 @@ tbe_status backward_impl(const tbe_desc* desc, const Problem& p, void* W, float*
   TBE_TRY_HIP(launch_bwd_long(p, grad_out, m, parts, at<int32_t>(ws, L.sched), s));
   timer_end(desc->timer, TBE_STAGE_BWD_LONG, s);
   timer_begin(desc->timer, TBE_STAGE_BWD_APPLY, s);
-  TBE_TRY_HIP(launch_bwd_apply(p, W, momentum, m, parts, lr, eps, s));
+  TBE_TRY_HIP(launch_bwd_apply(p, W, momentum, m, parts, hot, lr, eps, s));
   timer_end(desc->timer, TBE_STAGE_BWD_APPLY, s);
   return TBE_OK;
 }
@@ -461,8 +505,12 @@ Problem bound_problem(const tbe_desc* d, int64_t N, int weighted, int64_t sum, i
   p.S = d->short_max ? d->short_max : kDefaultShortMax;
   p.C = d->chunk ? d->chunk : kDefaultChunk;
   p.path = path;
+  p.fused_long = (d->flags & TBE_FLAG_FUSED_LONG) != 0;
+  p.no_hot = (d->flags & (TBE_FLAG_NO_HOT_ROWS | TBE_FLAG_FUSED_LONG)) != 0;
   derive_sizes(&p);
   p.sort_bits = 7;  // a group with fewer rows can take fewer, wider digits
+  // a group of T_g tables takes T_g * ceil(256 / T_g) <= T + 255 segments in all
+  if (p.hot_bwd) p.hot_nseg = (int32_t)((p.T + 255 + p.T - 1) / p.T);
   if (path == TBE_PATH_SMALL_TABLE) {  // split partials: T_g * splits(T_g) at most
     int64_t parts = 0;
     for (int32_t tg = 1; tg <= d->T; ++tg)

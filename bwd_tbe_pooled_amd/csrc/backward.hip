@@ -35,6 +35,8 @@
 //   keeps. Each chunk still writes its own partial, so the result does
 //   not depend on the schedule.
 #include <algorithm>
+#include <type_traits>
+
 #include "adagrad.h"
 #include "block_scan.h"
 #include "device.h"
@@ -310,15 +312,16 @@ __global__ __launch_bounds__(kThreads) void bwd_long_kernel(
   }
 }
 
-// Sum of the partials of chunks [c0, c1) of one long run, then its Adagrad
-// step. Slot s sums chunks c0+s, c0+s+NS, ... in ascending order and the
-// slots are combined by a fixed butterfly, so the order is the same every
-// call; the apply kernel and the fused long kernel both reduce through this
-// function with the same row shape, so they give the same bits.
+// Sum of the n partials part[0], part[stride], ... of one long run (its
+// chunks' partials, or its segment partials from the hot rows' contraction),
+// then its Adagrad step. Slot s sums partials s, s+NS, ... in ascending order
+// and the slots are combined by a fixed butterfly, so the order is the same
+// every call; the apply kernel and the fused long kernel both reduce through
+// this function with the same row shape, so they give the same bits.
 template <typename WT, typename ACC, int V, int PMAX>
 __device__ __forceinline__ void reduce_apply_run(WT* __restrict__ W, float* __restrict__ mom,
-                                                 const ACC* __restrict__ partials, int32_t c0,
-                                                 int32_t c1, int32_t key, int32_t D, int G,
+                                                 const ACC* __restrict__ part, int64_t stride,
+                                                 int32_t n, int32_t key, int32_t D, int G,
                                                  int log2G, int P, ACC lr, ACC eps) {
   const int lane = lane_id();
   const int slot = lane >> log2G;
@@ -328,12 +331,12 @@ __device__ __forceinline__ void reduce_apply_run(WT* __restrict__ W, float* __re
   constexpr int UNROLL = 4;  // chunks in flight per slot: a run's chain of loads is the latency
   ACC acc[PMAX][V];
   zero_acc<ACC, V, PMAX>(acc);
-  for (int32_t cb = c0 + slot; cb < c1; cb += NS * UNROLL) {
+  for (int32_t cb = slot; cb < n; cb += NS * UNROLL) {
     RAW buf[UNROLL][PMAX];
 #pragma unroll
     for (int uu = 0; uu < UNROLL; ++uu) {
       const int32_t c = cb + uu * NS;
-      const ACC* src = partials + (int64_t)(c < c1 ? c : c0) * D;
+      const ACC* src = part + (int64_t)(c < n ? c : 0) * stride;
 #pragma unroll
       for (int p = 0; p < PMAX; ++p) {
         const int e = (p * G + col) * V;
@@ -343,7 +346,7 @@ __device__ __forceinline__ void reduce_apply_run(WT* __restrict__ W, float* __re
     }
 #pragma unroll
     for (int uu = 0; uu < UNROLL; ++uu) {
-      if (cb + uu * NS >= c1) break;
+      if (cb + uu * NS >= n) break;
 #pragma unroll
       for (int p = 0; p < PMAX; ++p) {
         const ACC* x = reinterpret_cast<const ACC*>(&buf[uu][p]);
@@ -360,21 +363,34 @@ __device__ __forceinline__ void reduce_apply_run(WT* __restrict__ W, float* __re
     adagrad_row<WT, ACC, V, PMAX>(W + (int64_t)key * D, mom + key, acc, col, G, P, D, lr, eps);
 }
 
+// A hot run (run_slot[l] = t*256 + slot, its table not flagged back to the
+// chunk path) sums its nseg segment partials hot_parts[t][seg][slot][:], the
+// other long runs their chunks' partials.
 template <typename WT, int V, int PMAX>
 __global__ __launch_bounds__(kThreads) void bwd_apply_kernel(
     WT* __restrict__ W, float* __restrict__ mom, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ long_runs, const int32_t* __restrict__ long_chunk_begin,
     const int32_t* __restrict__ run_keys, const typename acc_of<WT>::type* __restrict__ partials,
-    int32_t D, int32_t G, int32_t log2G, int32_t P, typename acc_of<WT>::type lr,
-    typename acc_of<WT>::type eps) {
+    const int32_t* __restrict__ run_slot, const int32_t* __restrict__ hot_flag,
+    const typename acc_of<WT>::type* __restrict__ hot_parts, int32_t nseg, int32_t D, int32_t G,
+    int32_t log2G, int32_t P, typename acc_of<WT>::type lr, typename acc_of<WT>::type eps) {
   using ACC = typename acc_of<WT>::type;
   const int64_t n_long = counts[2];
   const int64_t gwave = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
   const int64_t nwaves = (int64_t)gridDim.x * kWaves;
   for (int64_t l = gwave; l < n_long; l += nwaves) {
-    reduce_apply_run<WT, ACC, V, PMAX>(W, mom, partials, long_chunk_begin[l],
-                                       long_chunk_begin[l + 1], run_keys[long_runs[l]], D, G,
-                                       log2G, P, lr, eps);
+    const int32_t q = run_slot ? run_slot[l] : -1;
+    const int32_t key = run_keys[long_runs[l]];
+    if (q >= 0 && hot_flag[q / 256] == 0) {
+      const int32_t t = q / 256, sl = q % 256;
+      reduce_apply_run<WT, ACC, V, PMAX>(W, mom, hot_parts + ((int64_t)t * nseg * 256 + sl) * D,
+                                         (int64_t)256 * D, nseg, key, D, G, log2G, P, lr, eps);
+    } else {
+      const int32_t c0 = long_chunk_begin[l];
+      reduce_apply_run<WT, ACC, V, PMAX>(W, mom, partials + (int64_t)c0 * D, D,
+                                         long_chunk_begin[l + 1] - c0, key, D, G, log2G, P, lr,
+                                         eps);
+    }
   }
 }
 
@@ -436,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void bwd_long_fused_kernel(
     prev = __shfl(prev, 0);
     if (prev != nch - 1) continue;  // another chunk of the run is still to come
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    reduce_apply_run<WT, ACC, V, PMAX>(W, mom, partials, c_first, c_first + nch, run_keys[u], D,
+    reduce_apply_run<WT, ACC, V, PMAX>(W, mom, partials + (int64_t)c_first * D, D, nch, run_keys[u], D,
                                        G, log2G, P, lr, eps);
   }
 }
@@ -462,10 +478,14 @@ __global__ void sched_zero_kernel(int32_t* __restrict__ p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// With the backward of the hot rows (hot_min non-null), the chunks of a hot
+// run (length >= hot_min of its table) are left out of the lists, unless the
+// table's hot_flag sent its hot runs back to the chunk path.
 __global__ __launch_bounds__(256) void sched_count_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ chunk_start,
     const int32_t* __restrict__ sorted_bag, const int32_t* __restrict__ chunk_run,
     const int32_t* __restrict__ run_offsets, int32_t C, int32_t B, int32_t T,
+    const int32_t* __restrict__ hot_min, const int32_t* __restrict__ hot_flag,
     int32_t* __restrict__ hist, int32_t* __restrict__ bucket_of, int32_t* __restrict__ arrivals) {
   const int64_t n = counts[3];
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
@@ -473,11 +493,16 @@ __global__ __launch_bounds__(256) void sched_count_kernel(
     arrivals[c] = 0;  // arrival counters of the fused long kernel
     // the chunk's place in batch order: the middle of its bag span
     const int32_t k0 = chunk_start[c];
-    const int32_t ke = run_offsets[chunk_run[c] + 1];
+    const int32_t u = chunk_run[c];
+    const int32_t ke = run_offsets[u + 1];
     const int32_t klast = (k0 + C < ke ? k0 + C : ke) - 1;
     const int32_t bag0 = sorted_bag[k0], bag1 = sorted_bag[klast];
     const int32_t bag = bag0 + (bag1 - bag0) / 2;
     const int32_t t = bag / B, b = bag - t * B;
+    if (hot_min && ke - run_offsets[u] >= hot_min[t] && hot_flag[t] == 0) {
+      bucket_of[c] = -1;  // summed by the hot rows' contraction
+      continue;
+    }
     int bk;
     if (T % kXcds == 0) {
       // T/8 whole tables per XCD, walked kSchedTables at a time in bag order
@@ -521,7 +546,9 @@ __global__ __launch_bounds__(256) void sched_scatter_kernel(const int32_t* __res
   const int64_t n = counts[3];
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n;
        c += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t pos = atomicAdd(&cursor[bucket_of[c]], 1);
+    const int32_t bk = bucket_of[c];
+    if (bk < 0) continue;
+    const int32_t pos = atomicAdd(&cursor[bk], 1);
     order[pos] = (int32_t)c;
   }
 }
@@ -639,13 +666,16 @@ hipError_t long_fused_typed(const Problem& p, const RowShape& rs, void* W, float
 
 template <typename WT, int V, int PMAX>
 hipError_t apply_typed(const Problem& p, const RowShape& rs, void* W, float* m,
-                       const tbe_meta& meta, const void* partials, double lr, double eps,
-                       hipStream_t s) {
+                       const tbe_meta& meta, const void* partials, const HotBwd& hot, double lr,
+                       double eps, hipStream_t s) {
   using ACC = typename acc_of<WT>::type;
   const dim3 grid((unsigned)persistent_blocks(p.cap_long));
+  // hot partials are f32: the backward of the hot rows runs for f16/bf16 weights only
+  const ACC* hot_parts = std::is_same<ACC, float>::value ? (const ACC*)hot.parts : nullptr;
   hipLaunchKernelGGL((bwd_apply_kernel<WT, V, PMAX>), grid, dim3(kThreads), 0, s, (WT*)W, m,
                      meta.counts, meta.long_runs, meta.long_chunk_begin, meta.run_keys,
-                     (const ACC*)partials, p.D, rs.G, rs.log2G, rs.P, (ACC)lr, (ACC)eps);
+                     (const ACC*)partials, hot_parts ? hot.run_slot : nullptr, hot.hot_flag,
+                     hot_parts, hot.nseg, p.D, rs.G, rs.log2G, rs.P, (ACC)lr, (ACC)eps);
   return hipGetLastError();
 }
 
@@ -716,9 +746,10 @@ hipError_t long_fused_for(const Problem& p, void* W, float* m, const float* grad
 // long kernel (which reduces in the same wave that accumulated) matches it.
 template <typename WT>
 hipError_t apply_for(const Problem& p, void* W, float* m, const tbe_meta& meta,
-                     const void* partials, double lr, double eps, hipStream_t s) {
+                     const void* partials, const HotBwd& hot, double lr, double eps,
+                     hipStream_t s) {
   const RowShape rs = grad_row_shape(p.D);
-#define CALL(VV, PP) apply_typed<WT, VV, PP>(p, rs, W, m, meta, partials, lr, eps, s)
+#define CALL(VV, PP) apply_typed<WT, VV, PP>(p, rs, W, m, meta, partials, hot, lr, eps, s)
   TBE_DISPATCH_V(rs, CALL);
 #undef CALL
 }
@@ -739,15 +770,15 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
 }
 
 hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t* sched,
-                                hipStream_t s) {
+                                const HotBwd& hot, hipStream_t s) {
   if (p.cap_chunks == 0) return hipSuccess;
   const SchedLayout L = sched_layout(sched, p.cap_chunks);
   // bucket counts, list starts and queue counters are contiguous: clear them together
   hipLaunchKernelGGL(sched_zero_kernel, dim3(32), dim3(256), 0, s, L.hist,
                      (int)(L.arrivals - L.hist));
   hipLaunchKernelGGL(sched_count_kernel, dim3(1024), dim3(256), 0, s, meta.counts, meta.chunk_start,
-                     meta.sorted_bag, meta.chunk_run, meta.run_offsets, p.C, p.B, p.T, L.hist,
-                     L.bucket_of, L.arrivals);
+                     meta.sorted_bag, meta.chunk_run, meta.run_offsets, p.C, p.B, p.T, hot.hot_min,
+                     hot.hot_flag, L.hist, L.bucket_of, L.arrivals);
   hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(1024), 0, s, L.hist, L.list_begin);
   hipLaunchKernelGGL(sched_scatter_kernel, dim3(1024), dim3(256), 0, s, meta.counts, L.bucket_of,
                      L.hist, L.order);
@@ -780,12 +811,13 @@ size_t long_schedule_ints(const Problem& p) {
 }
 
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
-                            const void* partials, double lr, double eps, hipStream_t s) {
+                            const void* partials, const HotBwd& hot, double lr, double eps,
+                            hipStream_t s) {
   if (p.cap_long == 0) return hipSuccess;
   switch (p.wdtype) {
-    case TBE_F32: return apply_for<float>(p, W, m, meta, partials, lr, eps, s);
-    case TBE_F16: return apply_for<f16_t>(p, W, m, meta, partials, lr, eps, s);
-    case TBE_BF16: return apply_for<bf16_t>(p, W, m, meta, partials, lr, eps, s);
+    case TBE_F32: return apply_for<float>(p, W, m, meta, partials, hot, lr, eps, s);
+    case TBE_F16: return apply_for<f16_t>(p, W, m, meta, partials, hot, lr, eps, s);
+    case TBE_BF16: return apply_for<bf16_t>(p, W, m, meta, partials, hot, lr, eps, s);
   }
   return hipErrorInvalidValue;
 }

@@ -100,6 +100,34 @@ __device__ __forceinline__ typename raw_vec<T, V>::type load_vec(const T* p) {
   return *reinterpret_cast<const R*>(p);
 }
 
+// Buffer resource over `bytes` bytes from `base` (raw, stride 0). A load at
+// an offset at or past `bytes` returns zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Raw buffer load of 2 to 32 bytes at byte offset `off` of the resource.
+template <typename R>
+__device__ __forceinline__ R buffer_load_raw(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(R) == 32) {
+    struct P { uint4 a, b; };
+    static_assert(sizeof(P) == 32, "32-byte piece");
+    P p;
+    p.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    p.b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0));
+    return __builtin_bit_cast(R, p);
+  } else if constexpr (sizeof(R) == 16) {
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  } else if constexpr (sizeof(R) == 8) {
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  } else if constexpr (sizeof(R) == 4) {
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  } else {
+    static_assert(sizeof(R) == 2, "buffer_load_raw: 2, 4, 8, 16 or 32 bytes");
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+  }
+}
+
 // Unpack V elements from a raw vector into accumulator values.
 template <typename T, int V, typename ACC>
 __device__ __forceinline__ void unpack(const typename raw_vec<T, V>::type& r, ACC (&out)[V]) {

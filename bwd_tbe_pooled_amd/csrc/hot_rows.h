@@ -1,0 +1,58 @@
+// A table's hot rows: the rows of its longest runs, known once the transpose
+// has run (page 1, the segment-length distribution: at the Zipf-skewed batch
+// the 256 longest runs of a table hold about three quarters of its lookups).
+// The forward after the transpose reads them from LDS, and the backward sums
+// their gradients on the matrix cores. Both find a lookup's hot slot through
+// an LDS hash of the table's hot rows, built here.
+#pragma once
+
+#include "device.h"
+
+namespace tbe {
+
+constexpr int kHotMaxK = 256;         // hot rows per table at most (slots fit a byte)
+constexpr int kHotBuckets = 256;      // hash buckets of 4 rows
+constexpr int kHotHash = 4 * kHotBuckets;
+
+// Bucket of a row: the top 8 bits of a multiplicative hash. A bucket holds 4
+// rows (one 16-byte LDS read); a full bucket spills into the next one, so a
+// lookup stops at the first bucket that holds it or has an empty entry.
+__device__ __forceinline__ uint32_t hot_bucket(int32_t row) {
+  return ((uint32_t)row * 0x9E3779B1u) >> 24;
+}
+
+// Fill the hash (s_key[kHotHash], 16-byte aligned, and s_slotof) from
+// rows[0..K), entries < 0 being empty slots. Called by every thread of the
+// workgroup between two barriers: s_key must be all -1 before (the caller
+// clears it and synchronises), and is complete after the caller's next
+// barrier.
+__device__ __forceinline__ void hot_hash_insert(int32_t* s_key, uint8_t* s_slotof,
+                                                const int32_t* __restrict__ rows, int K) {
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    const int32_t r = rows[k];
+    if (r < 0) continue;
+    uint32_t h = hot_bucket(r) * 4;
+    for (;;) {  // at most 256 rows in 1024 entries: a free entry exists
+      if (atomicCAS(&s_key[h], -1, r) == -1) {
+        s_slotof[h] = (uint8_t)k;
+        break;
+      }
+      h = (h + 1) & (kHotHash - 1);
+    }
+  }
+}
+
+// Slot of `row` among the hot rows, or -1.
+__device__ __forceinline__ int hot_hash_find(const int32_t* s_key, const uint8_t* s_slotof,
+                                             int32_t row) {
+  uint32_t b = hot_bucket(row);
+  for (;;) {
+    const int4 q = reinterpret_cast<const int4*>(s_key)[b];
+    const int j = q.x == row ? 0 : q.y == row ? 1 : q.z == row ? 2 : q.w == row ? 3 : -1;
+    if (j >= 0) return s_slotof[b * 4 + j];
+    if (q.w < 0) return -1;  // entries fill in order: an empty one ends the search
+    b = (b + 1) & (kHotBuckets - 1);
+  }
+}
+
+}  // namespace tbe

@@ -1,0 +1,99 @@
+// The hot-row plan: per table, the rows of up to K of its longest runs.
+#include "hot_rows.h"
+#include "internal.h"
+
+namespace tbe {
+
+namespace {
+
+// One workgroup per table: the row index (in its table) of up to K of the
+// table's longest runs, in hot_rows[t*K ..], the rest -1. Long runs of table
+// t are a contiguous range of the long-run list (keys ascend, tables are key
+// ranges); those with at least v lookups are taken, v the least length >= S
+// that leaves at most K of them. Optionally also, for every long run l of the
+// table, run_slot[l] = t*K + its slot, or -1 when it is not hot; and
+// hot_min[t] = v, or INT32_MAX when the table has no hot run: a long run is
+// hot exactly when its length is at least hot_min of its table; and
+// hot_flag[t] = 0 (the backward of the hot rows sets it to send them back to
+// the chunk path).
+__global__ __launch_bounds__(256) void hot_plan_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ long_runs,
+    const int32_t* __restrict__ run_offsets, const int32_t* __restrict__ run_keys,
+    const int32_t* __restrict__ tinfo, int32_t T, int32_t K, int32_t S,
+    int32_t* __restrict__ hot_rows, int32_t* __restrict__ run_slot,
+    int32_t* __restrict__ hot_min, int32_t* __restrict__ hot_flag) {
+  __shared__ int32_t s_range[2];
+  __shared__ int32_t s_n;
+  __shared__ int32_t red[256 / kWave];
+  const int32_t t = blockIdx.x;
+  const int64_t n_long = counts[2];
+  const int32_t first = tinfo[t];
+  for (int i = threadIdx.x; i < K; i += blockDim.x) hot_rows[(int64_t)t * K + i] = -1;
+  if (threadIdx.x < 2) {
+    const int32_t key = threadIdx.x == 0 ? first : first + tinfo[T + t];
+    int64_t lo = 0, hi = n_long;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (run_keys[long_runs[mid]] < key) lo = mid + 1;
+      else hi = mid;
+    }
+    s_range[threadIdx.x] = (int32_t)lo;
+  }
+  if (threadIdx.x == 0) {
+    s_n = 0;
+    if (hot_flag) hot_flag[t] = 0;
+  }
+  __syncthreads();
+  const int32_t l0 = s_range[0], l1 = s_range[1];
+  auto len = [&](int32_t l) {
+    const int32_t u = long_runs[l];
+    return run_offsets[u + 1] - run_offsets[u];
+  };
+  auto count_ge = [&](int32_t v) {
+    int32_t c = 0;
+    for (int32_t l = l0 + threadIdx.x; l < l1; l += blockDim.x) c += len(l) >= v;
+    for (int m = 1; m < kWave; m <<= 1) c += __shfl_xor(c, m);
+    __syncthreads();
+    if (lane_id() == 0) red[threadIdx.x / kWave] = c;
+    __syncthreads();
+    int32_t tot = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) tot += red[w];
+    return tot;
+  };
+  int32_t v = S;
+  if (count_ge(v) > K) {
+    int32_t lo = v + 1, hi = 0x7fffffff;
+    while (lo < hi) {
+      const int32_t mid = lo + (hi - lo) / 2;
+      if (count_ge(mid) <= K) hi = mid;
+      else lo = mid + 1;
+    }
+    v = lo;
+  }
+  __syncthreads();  // hot_rows cleared before any slot is written
+  for (int32_t l = l0 + threadIdx.x; l < l1; l += blockDim.x) {
+    int32_t q = -1;
+    if (len(l) >= v) {
+      q = atomicAdd(&s_n, 1);  // slot order does not change any value computed
+      hot_rows[(int64_t)t * K + q] = run_keys[long_runs[l]] - first;
+    }
+    if (run_slot) run_slot[l] = q < 0 ? -1 : t * K + q;
+  }
+  if (hot_min) {
+    __syncthreads();  // every slot taken (ties at v-1 may leave none)
+    if (threadIdx.x == 0) hot_min[t] = s_n > 0 ? v : 0x7fffffff;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hot_plan(const Problem& p, const tbe_meta& meta, const int32_t* tinfo, int32_t K,
+                           int32_t* hot_rows, int32_t* run_slot, int32_t* hot_min,
+                           int32_t* hot_flag, hipStream_t s) {
+  hipLaunchKernelGGL(hot_plan_kernel, dim3((unsigned)p.T), dim3(256), 0, s, meta.counts,
+                     meta.long_runs, meta.run_offsets, meta.run_keys, tinfo, p.T, K, p.S, hot_rows,
+                     run_slot, hot_min, hot_flag);
+  return hipGetLastError();
+}
+
+}  // namespace tbe

@@ -49,6 +49,15 @@ struct Problem {
   int32_t* err;
   // TBE_FLAG_FUSED_LONG: long runs reduced and applied by the long kernel
   bool fused_long;
+  // TBE_FLAG_NO_HOT_ROWS (implied by TBE_FLAG_FUSED_LONG): no hot-row paths
+  bool no_hot;
+  // Forward after the transpose: hot rows per table kept in LDS (0 = the
+  // plain gather) and bags per workgroup of that kernel.
+  int32_t hot_k, hot_bags;
+  // Backward of the hot rows on the matrix cores (generic path, f16/bf16
+  // weights, D a multiple of 32 up to 128): segments of the batch per table.
+  bool hot_bwd;
+  int32_t hot_nseg;
   // Row stride (floats) of the pooled output and of the upstream gradient:
   // T*D, or the whole problem's T*D when this problem is one group of tables
   // of a larger call.
@@ -81,6 +90,11 @@ struct WsLayout {
   size_t part_wide;    // small-table per-split flag: gradients outside the f16 split's range
   size_t hist;         // small-table counts of a forward given no metadata
   size_t sched;        // long-chunk schedule (order, buckets, list bounds)
+  size_t hot_rows;     // forward after the transpose: hot rows per table, int32[T * hot_k]
+  // backward of the hot rows: hot rows int32[T * 256], slot of each long run
+  // int32[cap_long], shortest hot run and fallback flag per table int32[T] each,
+  // segment partials float[T * nseg * 256 * D]
+  size_t hb_rows, hb_run_slot, hb_min, hb_flag, hb_parts;
   bool has_pre, has_meta, has_partials;
 };
 
@@ -104,6 +118,28 @@ hipError_t launch_validate(const Problem& p, const int32_t* indices, const int32
 hipError_t launch_forward_pool(const Problem& p, const void* W, const int32_t* indices,
                                const int32_t* offsets, const float* psw, const int32_t* tinfo,
                                float* out, hipStream_t s);
+void choose_hot(Problem* p);
+hipError_t launch_hot_plan(const Problem& p, const tbe_meta& meta, const int32_t* tinfo, int32_t K,
+                           int32_t* hot_rows, int32_t* run_slot, int32_t* hot_min,
+                           int32_t* hot_flag, hipStream_t s);
+bool hot_backward_eligible(const Problem& p);
+int32_t hot_backward_segments(const Problem& p);
+hipError_t launch_bwd_hot(const Problem& p, const float* grad, const int32_t* indices,
+                          const int32_t* offsets, const float* psw, const int32_t* hot_rows,
+                          const int32_t* tinfo, float* hot_parts, int32_t* hot_flag,
+                          hipStream_t s);
+// The hot rows' plan, flags and partials as the chunk schedule and the apply
+// read them (all null when the backward takes no hot rows).
+struct HotBwd {
+  const int32_t* run_slot;   // per long run: t*256 + slot, or -1
+  const int32_t* hot_min;    // per table: the shortest hot run's length
+  const int32_t* hot_flag;   // per table: 1 = its hot runs take the chunk path
+  const float* parts;        // [T][nseg][256][D]
+  int32_t nseg;
+};
+hipError_t launch_forward_pool_hot(const Problem& p, const void* W, const int32_t* indices,
+                                   const int32_t* offsets, const float* psw, const int32_t* tinfo,
+                                   const int32_t* hot_rows, float* out, hipStream_t s);
 
 struct SortBuffers {
   int32_t* A[4];       // key, pos, bag, psw after even passes
@@ -126,7 +162,7 @@ hipError_t launch_bwd_short(const Problem& p, void* W, float* m, const float* gr
                             const tbe_meta& meta, const int32_t* tinfo, double lr, double eps,
                             hipStream_t s);
 hipError_t launch_long_schedule(const Problem& p, const tbe_meta& meta, int32_t* sched,
-                                hipStream_t s);
+                                const HotBwd& hot, hipStream_t s);
 hipError_t launch_bwd_long(const Problem& p, const float* grad, const tbe_meta& meta,
                            void* partials, int32_t* sched, hipStream_t s);
 hipError_t launch_bwd_long_fused(const Problem& p, void* W, float* m, const float* grad,
@@ -134,7 +170,8 @@ hipError_t launch_bwd_long_fused(const Problem& p, void* W, float* m, const floa
                                  double eps, hipStream_t s);
 size_t long_schedule_ints(const Problem& p);  // workspace ints of the chunk schedule
 hipError_t launch_bwd_apply(const Problem& p, void* W, float* m, const tbe_meta& meta,
-                            const void* partials, double lr, double eps, hipStream_t s);
+                            const void* partials, const HotBwd& hot, double lr, double eps,
+                            hipStream_t s);
 
 // int64 index arrays: table start offsets (T+1) and int32 copies of one
 // group of tables.

@@ -8,11 +8,11 @@
 // both on the matrix cores (v_mfma_f32_32x32x16_f16: f16 inputs, f32
 // accumulation). Counts are exact in f16 up to 2048. The backward scales each
 // gradient column by a power of two 2^s that brings its magnitudes near
-// [2^8, 2^9), splits the scaled value x into
+// [2^4, 2^5), splits the scaled value x into
 // hi = f16(x) and lo = f16((x - hi) * 2^11), contracts H with both (the lo
 // product with H * 2^-11, exact in f16) and unscales the sums by 2^-s at the
 // end. That compensates the f16 rounding to about 2^-22 relative for every
-// gradient down to 2^-23 of the column's first largest, whatever its magnitude.
+// gradient down to 2^-18 of the column's first largest, whatever its magnitude.
 // The scale of a column is set by its first tile with a nonzero gradient; a
 // workgroup that meets a tile far outside it, or a non-finite gradient, flags
 // its (table, split), and the f32 kernel then recomputes that partial. The
@@ -518,11 +518,11 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     // B operands: this tile's gradients of column d times 2^sc, split into
     // hi = f16(x) and lo = f16((x - hi) * 2^11). sc is a power-of-two scale
     // per column (lanes i and i + 32 agree on it), set by the first tile with
-    // a nonzero gradient so that its largest magnitude lands in [2^8, 2^9):
+    // a nonzero gradient so that its largest magnitude lands in [2^4, 2^5):
     // gradients far below 1 would otherwise fall into f16's subnormals, and
     // above 65504 overflow. The sums are in units of 2^-sc, unscaled once at
     // the end (exact). A later tile whose largest scaled magnitude leaves
-    // [2^-6, 2^15) (64 times the first tile's largest, or 2^14 times less)
+    // [2^-14, 2^15) (1024 times the first tile's largest, or 2^18 times less)
     // marks the split for the f32 kernel, like a non-finite one.
     load_grad(b0);
     {
@@ -537,9 +537,9 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
       if (gmax > 0.f) {
         const int e = __builtin_amdgcn_frexp_expf(gmax);  // gmax in [2^(e-1), 2^e)
         if (!has_sc) {
-          sc = 9 - e;
+          sc = 5 - e;
           has_sc = true;
-        } else if (e + sc > 15 || e + sc < -5) {
+        } else if (e + sc > 15 || e + sc < -13) {
           big = true;
         }
       }

@@ -93,9 +93,20 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
                                         a device-scope release and counts
                                         itself in; the last chunk of a run
                                         reduces the run's partials in chunk
-                                        order and applies Adagrad. Same bits
-                                        as the default two launches (chunk
-                                        partials, then apply). */
+                                        order and applies Adagrad. Implies
+                                        TBE_FLAG_NO_HOT_ROWS; same bits as
+                                        the two launches (chunk partials,
+                                        then apply) under that flag. */
+#define TBE_FLAG_NO_HOT_ROWS   0x10u /* no hot-row paths: the forward after the
+                                        transpose gathers every row through
+                                        the plain gather, and the backward
+                                        sends every long run through the
+                                        chunk path (by default the rows of
+                                        each table's longest runs are read
+                                        from LDS in that forward and summed
+                                        on the matrix cores in the backward,
+                                        f16/bf16 weights, D a multiple of 32
+                                        up to 128) */
 
 /* Bits OR-ed into *tbe_desc.error_flags under TBE_FLAG_CHECK. */
 #define TBE_ERROR_INDEX 0x1u   /* some index was outside its table */
@@ -121,7 +132,8 @@ typedef enum {
     TBE_STAGE_VALIDATE = 10,    /* TBE_FLAG_VALIDATE check                    */
     TBE_STAGE_LONG_SCHEDULE = 11, /* per-XCD order of the long-run chunks     */
     TBE_STAGE_SMALL_COUNT = 12, /* small-table per-bag row counts             */
-    TBE_NUM_STAGES = 13
+    TBE_STAGE_BWD_HOT = 13,     /* hot rows: plan + matrix-core contraction   */
+    TBE_NUM_STAGES = 14
 } tbe_stage;
 
 typedef struct tbe_timer tbe_timer;   /* opaque; see tbe_timer_create */
@@ -155,9 +167,8 @@ typedef struct {
  * backward; the small-table path keeps per-bag row counts instead.
  *
  * Generic path, with U runs (unique keys) over N lookups:
- *   counts[0] = U, counts[1] = n_short, counts[2] = n_long, counts[3] = n_chunks,
- *   counts[4] = 1 if a small-table count exceeded 255 (else 0),
- *   counts[5] = 1 if a small-table count exceeded 2048 (else 0);
+ *   counts[0] = U, counts[1] = n_short, counts[2] = n_long, counts[3] = n_chunks
+ *   (counts[4..7] are not written on this path);
  *   run_keys[u]       linearized key of run u, strictly increasing;
  *   run_offsets[u]    first sorted slot of run u; run_offsets[U] = N;
  *   sorted_pos[k]     lookup position at sorted slot k (stable order); optional:

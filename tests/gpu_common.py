@@ -64,11 +64,12 @@ def make_desc(cfg, S=0, C=0, flags=0, timer=None, error_flags=None):
 
 
 def run_library(cfg, batch, W, m, *, meta_in_forward: bool, backward_meta: bool = True,
-                S=0, C=0, flags=0, dev=None, with_pos: bool = True, error_flags=None):
+                S=0, C=0, flags=0, dev=None, with_pos: bool = True, error_flags=None,
+                timer=None):
     """Forward (+ preprocessing when meta_in_forward) and backward through the
     C ABI. W and m are updated in place. Returns out and the metadata."""
     tbe = lib()
-    desc = make_desc(cfg, S, C, flags, error_flags=error_flags)
+    desc = make_desc(cfg, S, C, flags, timer=timer, error_flags=error_flags)
     dev = dev or device_batch(batch)
     N = batch.indices.size
     weighted = batch.psw is not None

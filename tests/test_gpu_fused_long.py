@@ -3,9 +3,9 @@ its partial with a device-scope release and counts itself in on its run; the
 last chunk to arrive reduces the run's partials in chunk order and applies
 Adagrad (page 1, backward section, the fused path of figure 3).
 
-Ordering and race checks: the fused path must give the same bits as the
-default two launches (chunk partials, then a separate apply), which reduce in
-the same order. A reader that saw a partial before it was complete would
+Ordering and race checks: the fused path (which takes no hot-row path) must
+give the same bits as the two launches (chunk partials, then a separate
+apply) under TBE_FLAG_NO_HOT_ROWS, which reduce in the same order. A reader that saw a partial before it was complete would
 break that:
 - the backward workspace is filled with 0xFF bytes first, so a partial read
   before its chunk wrote it is a NaN;
@@ -68,7 +68,7 @@ def _compare(name, B, S, C):
     g2 = torch.randn(dev["grad"].shape, generator=gen, device="cuda", dtype=torch.float32)
     grads = [dev["grad"], g2]
     tbe = lib()
-    W0, m0, c0 = _steps(cfg, batch, dev, grads, 0, S, C)
+    W0, m0, c0 = _steps(cfg, batch, dev, grads, tbe.TBE_FLAG_NO_HOT_ROWS, S, C)
     W1, m1, c1 = _steps(cfg, batch, dev, grads, tbe.TBE_FLAG_FUSED_LONG, S, C)
     np.testing.assert_array_equal(c0, c1)
     n_long, n_chunks = int(c1[2]), int(c1[3])
