@@ -286,6 +286,10 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
         flags = {"none": 0, "fused": tbe.TBE_FLAG_CHECK, "validate": tbe.TBE_FLAG_VALIDATE}[args.check]
         if args.long == "fused":
             flags |= tbe.TBE_FLAG_FUSED_LONG
+        elif args.long == "hot":
+            flags |= tbe.TBE_FLAG_HOT_BACKWARD
+        if args.hot_rows == "off":
+            flags |= tbe.TBE_FLAG_NO_HOT_ROWS
     desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, flags=flags, error_flags=err)
     assert tbe.tbe_select_path(desc, N, weighted) == tbe.TBE_PATH_GENERIC
     meta = tbe.Meta(desc, N, weighted, with_pos=False)   # the backward needs no positions
@@ -544,9 +548,15 @@ def main():
     ap.add_argument("--preprocess", choices=["forward", "backward"], default="forward",
                     help="where the transpose (sort, RLE, routing) runs: in the forward "
                          "(default; the pages' hoisting) or inside the backward (their baseline)")
-    ap.add_argument("--long", choices=["two_launch", "fused"], default="two_launch",
-                    help="long runs: chunk partials then a separate apply (default), or one "
-                         "launch whose last chunk per run reduces and applies (TBE_FLAG_FUSED_LONG)")
+    ap.add_argument("--hot-rows", choices=["on", "off"], default="on",
+                    help="the forward after the transpose reads each table's hottest rows from "
+                         "LDS (on, default) or gathers every row (off: TBE_FLAG_NO_HOT_ROWS)")
+    ap.add_argument("--long", choices=["two_launch", "fused", "hot"], default="two_launch",
+                    help="long runs: chunk partials then a separate apply (default), one "
+                         "launch whose last chunk per run reduces and applies (fused: "
+                         "TBE_FLAG_FUSED_LONG), or the hottest rows' gradients as one "
+                         "matrix-core contraction and the rest as chunks (hot: "
+                         "TBE_FLAG_HOT_BACKWARD)")
     ap.add_argument("--rows", choices=["zipf", "uniform"], default="zipf",
                     help="row distribution of the large workload: Zipf-Mandelbrot (default) or "
                          "uniform (a diagnostic without reuse)")
@@ -577,7 +587,8 @@ def main():
     dev = torch.device("cuda")
     scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     diagnostic = (args.check != "none" or args.preprocess != "forward" or args.long != "two_launch"
-                  or args.rows != "zipf" or args.index != "int32" or args.tables != 32)
+                  or args.rows != "zipf" or args.index != "int32" or args.tables != 32
+                  or args.hot_rows != "on")
 
     if args.workload == "small":
         cfg = SMALL_TABLE
@@ -688,7 +699,9 @@ def main():
         "config": {"workload": cfg.name + (f" ({args.rows} rows)" if args.rows != "zipf" else "")
                    + ("" if args.preprocess == "forward" else ", preprocessing in the backward")
                    + ("" if args.check == "none" else f", index check {args.check}")
-                   + ("" if args.long == "two_launch" else ", long runs in one launch")
+                   + {"two_launch": "", "fused": ", long runs in one launch",
+                      "hot": ", hot rows' backward on the matrix cores"}[args.long]
+                   + ("" if args.hot_rows == "on" else ", no hot rows in the forward")
                    + ("" if args.index == "int32" else ", int64 indices")
                    + ("" if args.tables == 32 else f", {args.tables} tables"),
                    **head["shape"], "parallelism": "single GPU"},

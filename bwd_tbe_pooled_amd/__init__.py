@@ -31,7 +31,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 TBE_OK, TBE_ERR_ARG, TBE_ERR_UNSUPPORTED, TBE_ERR_WORKSPACE, TBE_ERR_INDEX_RANGE, TBE_ERR_HIP = range(6)
 TBE_F32, TBE_F16, TBE_BF16 = 0, 1, 2
 TBE_FLAG_VALIDATE, TBE_FLAG_FORCE_GENERIC, TBE_FLAG_CHECK, TBE_FLAG_FUSED_LONG = 0x1, 0x2, 0x4, 0x8
-TBE_FLAG_NO_HOT_ROWS = 0x10
+TBE_FLAG_NO_HOT_ROWS, TBE_FLAG_HOT_BACKWARD = 0x10, 0x20
 TBE_ERROR_INDEX = 0x1
 TBE_PATH_GENERIC, TBE_PATH_SMALL_TABLE = 0, 1
 (TBE_OP_FORWARD, TBE_OP_FORWARD_PREPROCESS, TBE_OP_PREPROCESS, TBE_OP_BACKWARD,

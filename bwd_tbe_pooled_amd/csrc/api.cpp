@@ -51,7 +51,7 @@ static tbe_status check_desc(const tbe_desc* d, int64_t N, int64_t* sum, int64_t
   if (d->wdtype != TBE_F32 && d->wdtype != TBE_F16 && d->wdtype != TBE_BF16) return TBE_ERR_UNSUPPORTED;
   if (d->flags &
       ~(TBE_FLAG_VALIDATE | TBE_FLAG_FORCE_GENERIC | TBE_FLAG_CHECK | TBE_FLAG_FUSED_LONG |
-        TBE_FLAG_NO_HOT_ROWS))
+        TBE_FLAG_NO_HOT_ROWS | TBE_FLAG_HOT_BACKWARD))
     return TBE_ERR_ARG;
   if ((d->flags & TBE_FLAG_CHECK) && !d->error_flags) return TBE_ERR_ARG;
   if (d->short_max < 0 || d->chunk < 0) return TBE_ERR_ARG;
@@ -82,7 +82,7 @@ static void derive_sizes(Problem* p) {
   p->small_splits = small_splits_for(p->T, p->B);
   p->ld = (int64_t)p->T * p->D;
   choose_hot(p);
-  p->hot_bwd = hot_backward_eligible(*p);  // reads no_hot: set before this
+  p->hot_bwd = hot_backward_eligible(*p);  // reads no_hot, hot_bwd_asked: set before this
   p->hot_nseg = p->hot_bwd ? hot_backward_segments(*p) : 0;
 }
 
@@ -109,6 +109,7 @@ tbe_status make_problem(const tbe_desc* d, int64_t N, int weighted, Problem* p) 
   p->path = small_eligible(d, N, weighted, mx) ? TBE_PATH_SMALL_TABLE : TBE_PATH_GENERIC;
   p->fused_long = (d->flags & TBE_FLAG_FUSED_LONG) != 0;
   p->no_hot = (d->flags & (TBE_FLAG_NO_HOT_ROWS | TBE_FLAG_FUSED_LONG)) != 0;
+  p->hot_bwd_asked = (d->flags & TBE_FLAG_HOT_BACKWARD) != 0;
   derive_sizes(p);
   p->err = (d->flags & TBE_FLAG_CHECK) ? d->error_flags : nullptr;
   return TBE_OK;
@@ -507,6 +508,7 @@ Problem bound_problem(const tbe_desc* d, int64_t N, int weighted, int64_t sum, i
   p.path = path;
   p.fused_long = (d->flags & TBE_FLAG_FUSED_LONG) != 0;
   p.no_hot = (d->flags & (TBE_FLAG_NO_HOT_ROWS | TBE_FLAG_FUSED_LONG)) != 0;
+  p.hot_bwd_asked = (d->flags & TBE_FLAG_HOT_BACKWARD) != 0;
   derive_sizes(&p);
   p.sort_bits = 7;  // a group with fewer rows can take fewer, wider digits
   // a group of T_g tables takes T_g * ceil(256 / T_g) <= T + 255 segments in all

@@ -312,13 +312,11 @@ __global__ __launch_bounds__(kHbThreads) void bwd_hot_kernel(
 
 }  // namespace
 
-// Off by default for now: at T=32, B=131072, D=128 bf16 on one MI355X the
-// contraction takes 2.16 ms (and the remaining chunks 0.85 ms) against 2.05 ms
-// for the chunk path alone. kHotBackwardOn turns it on.
-constexpr bool kHotBackwardOn = false;
-
+// Opt-in (TBE_FLAG_HOT_BACKWARD): at T=32, B=131072, D=128 bf16 on one
+// MI355X the contraction takes 2.16 ms and the remaining long runs' chunks
+// 0.85 ms, against 2.05 ms for the chunk path alone.
 bool hot_backward_eligible(const Problem& p) {
-  return kHotBackwardOn && p.path == TBE_PATH_GENERIC && !p.no_hot && p.wdtype != TBE_F32 &&
+  return p.hot_bwd_asked && !p.no_hot && p.path == TBE_PATH_GENERIC && p.wdtype != TBE_F32 &&
          p.D % 32 == 0 && p.D <= 128 && p.B >= 1 && p.cap_long > 0;
 }
 

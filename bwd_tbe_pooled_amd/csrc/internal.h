@@ -51,11 +51,14 @@ struct Problem {
   bool fused_long;
   // TBE_FLAG_NO_HOT_ROWS (implied by TBE_FLAG_FUSED_LONG): no hot-row paths
   bool no_hot;
+  // TBE_FLAG_HOT_BACKWARD: the hot rows' backward on the matrix cores, asked for
+  bool hot_bwd_asked;
   // Forward after the transpose: hot rows per table kept in LDS (0 = the
   // plain gather) and bags per workgroup of that kernel.
   int32_t hot_k, hot_bags;
-  // Backward of the hot rows on the matrix cores (generic path, f16/bf16
-  // weights, D a multiple of 32 up to 128): segments of the batch per table.
+  // Backward of the hot rows on the matrix cores (TBE_FLAG_HOT_BACKWARD,
+  // generic path, f16/bf16 weights, D a multiple of 32 up to 128): segments of
+  // the batch per table.
   bool hot_bwd;
   int32_t hot_nseg;
   // Row stride (floats) of the pooled output and of the upstream gradient:

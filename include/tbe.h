@@ -99,14 +99,21 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
                                         then apply) under that flag. */
 #define TBE_FLAG_NO_HOT_ROWS   0x10u /* no hot-row paths: the forward after the
                                         transpose gathers every row through
-                                        the plain gather, and the backward
-                                        sends every long run through the
-                                        chunk path (by default the rows of
-                                        each table's longest runs are read
-                                        from LDS in that forward and summed
-                                        on the matrix cores in the backward,
-                                        f16/bf16 weights, D a multiple of 32
-                                        up to 128) */
+                                        the plain gather (by default it reads
+                                        the rows of each table's longest runs
+                                        from LDS), and TBE_FLAG_HOT_BACKWARD
+                                        is ignored */
+#define TBE_FLAG_HOT_BACKWARD  0x20u /* the backward sums the gradients of
+                                        each table's up to 256 longest runs
+                                        as one matrix-core contraction that
+                                        reads every gradient row once (page
+                                        1, the compensated f16 hi/lo
+                                        contraction; f16/bf16 weights, D a
+                                        multiple of 32 up to 128), the other
+                                        long runs on the chunk path.
+                                        Opt-in: slower than the chunk path
+                                        alone at the Zipf-skewed batch on
+                                        gfx950 */
 
 /* Bits OR-ed into *tbe_desc.error_flags under TBE_FLAG_CHECK. */
 #define TBE_ERROR_INDEX 0x1u   /* some index was outside its table */

@@ -75,8 +75,9 @@ def test_bad_descriptions_are_rejected():
     assert tbe.tbe_select_path(_desc(), 10, False) == tbe.TBE_PATH_GENERIC
     assert tbe.tbe_select_path(_desc(flags=tbe.TBE_FLAG_FUSED_LONG), 10, False) == 0
     assert tbe.tbe_select_path(_desc(flags=tbe.TBE_FLAG_NO_HOT_ROWS), 10, False) == 0
+    assert tbe.tbe_select_path(_desc(flags=tbe.TBE_FLAG_HOT_BACKWARD), 10, False) == 0
     for kw in [dict(T=0, rows=[]), dict(D=0), dict(B=-1), dict(rows=[100, 0]),
-               dict(flags=0x20), dict(flags=0x80), dict(short_max=-1), dict(chunk=-3),
+               dict(flags=0x40), dict(flags=0x80), dict(short_max=-1), dict(chunk=-3),
                dict(flags=tbe.TBE_FLAG_CHECK)]:   # the fused check needs an error word
         with pytest.raises(tbe.TbeError) as e:
             tbe.tbe_select_path(_desc(**kw), 10, False)

@@ -1,5 +1,5 @@
 """Backward of the hot rows (the rows of each table's longest runs) on the
-matrix cores, through the C ABI against the oracle. Each gradient row is read
+matrix cores (TBE_FLAG_HOT_BACKWARD), through the C ABI against the oracle. Each gradient row is read
 once per table and contracted with the hot rows' per-bag weight sums; the
 other long runs keep the chunk path and the apply sums a hot row's segment
 partials. Every updated row must match the oracle (weights within tolerance
@@ -20,8 +20,7 @@ from tests.gpu_common import (assert_rows_match, assert_untouched_unchanged, fre
                               host_rows, oracle_all, run_library)
 from workloads import LARGE, Batch, Config, make_batch
 
-pytestmark = [pytest.mark.gpu,
-              pytest.mark.skip(reason="the hot rows' backward is switched off in this build")]
+pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -41,7 +40,8 @@ def _check(cfg, batch, S=0, C=0, label=""):
     uk = np.unique(keys)
     Wrows, mrows = host_rows(W0, m0, uk)
     timer = tbe.Timer(4)
-    r = run_library(cfg, batch, W, m, meta_in_forward=True, S=S, C=C, timer=timer)
+    r = run_library(cfg, batch, W, m, meta_in_forward=True, S=S, C=C, timer=timer,
+                    flags=tbe.TBE_FLAG_HOT_BACKWARD)
     pre, _, bw = oracle_all(cfg, batch, Wrows, mrows, uk, S or 256, C or 256)
     assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], label or cfg.name)
     assert_untouched_unchanged(W0, W, m0, m, uk)
