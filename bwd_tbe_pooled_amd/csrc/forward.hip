@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
 // A bag's sum is taken hot rows first, then cold rows, each in lookup order:
 // another order than fwd_pool_kernel's, so the two agree to rounding.
 constexpr int kHotBytes = 65536;      // LDS for hot rows
+constexpr int kHotRowMax = 1024;      // longest row on this path: 64 lanes of 16 bytes
 constexpr int kHotThreads = 512;
 constexpr int kHotWaves = kHotThreads / kWave;
 constexpr int kHotStage = 2 * kWave;  // staged lookups per wave and window
@@ -253,7 +254,8 @@ void fwd_pool_hot_kernel(
   using RAW = typename raw_vec<WT, V>::type;
   constexpr int CU = kColdUnroll<(int)sizeof(RAW)>;
   constexpr int HU = kHotUnroll<(int)sizeof(RAW)>;
-  __shared__ __align__(16) unsigned char s_rows[kHotBytes];
+  // hot rows in slots 0..K-1, then slot K, a row of zeros that padded lanes read
+  __shared__ __align__(16) unsigned char s_rows[kHotBytes + kHotRowMax];
   __shared__ __align__(16) int32_t s_key[kHotHash];
   __shared__ uint8_t s_slotof[kHotHash];
   __shared__ int32_t s_cidx[kHotWaves][kHotStage];   // cold lookups' rows, in lookup order
@@ -280,6 +282,14 @@ void fwd_pool_hot_kernel(
   const int e = col * V;
   const bool col_ok = e < D;
   const uint64_t lt = mask_below(lane);
+  // Cold rows come through a buffer resource over the table (at most 2 GiB and
+  // 2^24 rows, so a row's offset is a 24-bit product): a lane with nothing to
+  // load gives an offset past the end, and the load returns zeros.
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(Wt, Et * (uint32_t)row_bytes);
+  constexpr uint32_t kNoRow = 0x80000000u;
+  const uint32_t eb = (uint32_t)(e * (int)sizeof(WT));
+  const int eb_lds = col_ok ? e * (int)sizeof(WT) : 0;  // lanes past the row read column 0
+  const int zero_slot = K;
 
   // hash of the table's hot rows, then the rows themselves
   for (int i = threadIdx.x; i < kHotHash; i += kHotThreads) s_key[i] = -1;
@@ -294,6 +304,8 @@ void fwd_pool_hot_kernel(
         reinterpret_cast<uint4*>(s_rows)[q] =
             reinterpret_cast<const uint4*>(Wt + (int64_t)r * D)[o];
     }
+    for (int q = threadIdx.x; q < row_bytes / 16; q += kHotThreads)
+      reinterpret_cast<uint4*>(s_rows)[n16 + q] = uint4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
@@ -405,14 +417,13 @@ void fwd_pool_hot_kernel(
       const int kk = ok ? k : 0;
       idx[u] = s_cidx[wave][kk];
       if constexpr (WEIGHTED) cs[u] = ok ? s_w[wave][kk] : 0.f;
-      else cs[u] = ok ? 1.f : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < CU; ++u) asm volatile("" ::"v"(idx[u]));
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
-      if (c + u < c1 && col_ok) cb[u] = load_vec<WT, V>(Wt + (int64_t)idx[u] * D + e);
-      else cb[u] = RAW{};
+      const uint32_t off = __umul24((uint32_t)idx[u], (uint32_t)row_bytes) + eb;
+      cb[u] = buffer_load_raw<RAW>(wres, c + u < c1 && col_ok ? off : kNoRow);
     }
   };
   auto add_rows = [&](ACC (&acc)[V], const RAW* rb, const float* rs, auto n) {
@@ -422,7 +433,10 @@ void fwd_pool_hot_kernel(
       ACC x[V];
       unpack<WT, V, ACC>(rb[u], x);
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] += sv * x[v];
+      for (int v = 0; v < V; ++v) {
+        if constexpr (WEIGHTED) acc[v] += sv * x[v];
+        else acc[v] += x[v];  // padded lanes hold zeros
+      }
     }
   };
   // One window of the slot's bag [ob, oe): `pre` (the next group's loads),
@@ -438,11 +452,11 @@ void fwd_pool_hot_kernel(
     const int h0 = lo - c0, h1 = hi - c1;
     pre();  // before the cold rows: waiting for those then covers these too
     RAW cb[CU];
-    float cs[CU];
+    float cs[CU] = {};
     cold_batch(c0, c1, cb, cs);
     for (int k = h0; k < h1; k += HU) {
       RAW hb[HU];
-      float hsc[HU];
+      float hsc[HU] = {};
       int hslot[HU];
 #pragma unroll
       for (int u = 0; u < HU; ++u) {
@@ -451,16 +465,13 @@ void fwd_pool_hot_kernel(
         const int q = ok ? kk : 0;
         hslot[u] = s_hslot[wave][q];
         if constexpr (WEIGHTED) hsc[u] = ok ? s_w[wave][kHotStage - 1 - q] : 0.f;
-        else hsc[u] = ok ? 1.f : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < HU; ++u) asm volatile("" ::"v"(hslot[u]));
 #pragma unroll
       for (int u = 0; u < HU; ++u) {
-        if (k + u < h1 && col_ok)
-          hb[u] = *reinterpret_cast<const RAW*>(s_rows + (size_t)hslot[u] * row_bytes +
-                                                (size_t)e * sizeof(WT));
-        else hb[u] = RAW{};
+        const int sl = k + u < h1 ? hslot[u] : zero_slot;
+        hb[u] = *reinterpret_cast<const RAW*>(s_rows + sl * row_bytes + eb_lds);
       }
       add_rows(acc, hb, hsc, std::integral_constant<int, HU>{});
     }
@@ -533,6 +544,10 @@ hipError_t launch_hot_typed(const Problem& p, const RowShape& rs, const void* W,
                             const int32_t* indices, const int32_t* offsets, const float* psw,
                             const int32_t* tinfo, const int32_t* hot_rows, float* out,
                             hipStream_t s) {
+  const int64_t row = (int64_t)p.D * sizeof(WT);
+  // the hot rows and the zero row after them fit the kernel's LDS
+  if (row > kHotRowMax || (int64_t)p.hot_k * row > kHotBytes || p.hot_k > kHotMaxK)
+    return hipErrorInvalidValue;
   const int64_t per_table = (p.B + p.hot_bags - 1) / p.hot_bags;
   const int64_t nblocks = per_table * p.T;
   if (nblocks == 0) return hipSuccess;
@@ -630,6 +645,9 @@ void choose_hot(Problem* p) {
   const int64_t row = p->D * wbytes;
   if (p->no_hot || p->path != TBE_PATH_GENERIC || row % 16 != 0 || row_shape(p->D, hot_max_v(wbytes)).P != 1)
     return;
+  // cold rows are read at 32-bit offsets below 2^31, rows numbered in 24 bits
+  if (p->max_rows >= (int64_t(1) << 24) || p->max_rows * row >= (int64_t(1) << 31)) return;
+  if (row > kHotRowMax) return;
   const int64_t k = std::min<int64_t>(256, kHotBytes / row);
   if (k < 16 || p->B < 1) return;
   int32_t bags = 2048;  // halve until the grid holds about four workgroups per CU
