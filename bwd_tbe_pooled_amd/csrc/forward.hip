@@ -228,15 +228,19 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_pool_kernel(
 // - loads the next group's indices and offsets while this one is summed.
 // A bag's sum is taken hot rows first, then cold rows, each in lookup order:
 // another order than fwd_pool_kernel's, so the two agree to rounding.
-constexpr int kHotBytes = 65536;      // LDS for hot rows
-constexpr int kHotRowMax = 1024;      // longest row on this path: 64 lanes of 16 bytes
+constexpr int kHotBytes = 65536;      // LDS for the hot rows and one row of zeros
 constexpr int kHotThreads = 512;
 constexpr int kHotWaves = kHotThreads / kWave;
 constexpr int kHotStage = 2 * kWave;  // staged lookups per wave and window
-// rows in flight per row slot: cold 8 and hot 4 of 16-byte pieces, half as
-// many of 32-byte pieces (f32 rows of 128 or more)
+// rows in flight per row slot: cold 8 of 16-byte pieces, 4 of 32-byte pieces
+// (f32 rows of 128 or more); hot 2 of 16 or 32 bytes, 4 of smaller ones
 template <int RAW_BYTES> constexpr int kColdUnroll = RAW_BYTES > 16 ? 4 : 8;
-template <int RAW_BYTES> constexpr int kHotUnroll = RAW_BYTES > 16 ? 2 : 4;
+template <int RAW_BYTES> constexpr int kHotUnroll = RAW_BYTES >= 16 ? 2 : 4;
+// bf16 hot rows are held in LDS widened to f32 (a bf16 is the upper half of an
+// f32), so the hot lookups cost one multiply-add per element and no unpack;
+// half as many rows fit. f16 rows convert inside the multiply-add anyway.
+template <typename WT> constexpr bool kHotWiden = std::is_same<WT, bf16_t>::value;
+template <typename WT> constexpr int kHotLdsElem = kHotWiden<WT> ? 4 : (int)sizeof(WT);
 
 __device__ __forceinline__ uint64_t mask_below(int n) {  // bits [0, n)
   return n <= 0 ? 0ull : n >= 64 ? ~0ull : ((1ull << n) - 1ull);
@@ -252,16 +256,20 @@ void fwd_pool_hot_kernel(
     int32_t K, int32_t hot_bags, int64_t nblocks, int64_t ld, int32_t* __restrict__ err) {
   using ACC = typename acc_of<WT>::type;
   using RAW = typename raw_vec<WT, V>::type;
+  constexpr bool WIDEN = kHotWiden<WT>;
+  using HRAW = typename vec_bytes<V * kHotLdsElem<WT>>::type;  // a lane's piece of an LDS row
   constexpr int CU = kColdUnroll<(int)sizeof(RAW)>;
-  constexpr int HU = kHotUnroll<(int)sizeof(RAW)>;
+  constexpr int HU = kHotUnroll<(int)sizeof(HRAW)>;
   // hot rows in slots 0..K-1, then slot K, a row of zeros that padded lanes read
-  __shared__ __align__(16) unsigned char s_rows[kHotBytes + kHotRowMax];
+  __shared__ __align__(16) unsigned char s_rows[kHotBytes];
   __shared__ __align__(16) int32_t s_key[kHotHash];
   __shared__ uint8_t s_slotof[kHotHash];
   __shared__ int32_t s_cidx[kHotWaves][kHotStage];   // cold lookups' rows, in lookup order
   __shared__ uint8_t s_hslot[kHotWaves][kHotStage];  // hot lookups' LDS slots, in lookup order
   // weights: cold lookups from the front, hot lookups from the back
   __shared__ float s_w[kHotWaves][WEIGHTED ? kHotStage : 1];
+  // cold lookups before window position i, for i in [0, window length]
+  __shared__ uint8_t s_cpre[kHotWaves][kHotStage + 4];
 
   const int64_t lb = xcd_logical_block(nblocks);
   if (lb < 0) return;
@@ -288,24 +296,33 @@ void fwd_pool_hot_kernel(
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(Wt, Et * (uint32_t)row_bytes);
   constexpr uint32_t kNoRow = 0x80000000u;
   const uint32_t eb = (uint32_t)(e * (int)sizeof(WT));
-  const int eb_lds = col_ok ? e * (int)sizeof(WT) : 0;  // lanes past the row read column 0
-  const int zero_slot = K;
+  const uint32_t lrow = (uint32_t)(D * kHotLdsElem<WT>);  // LDS bytes per hot row
+  const uint32_t eb_lds = col_ok ? (uint32_t)(e * kHotLdsElem<WT>) : 0u;  // lanes past the row read column 0
+  const uint32_t zero_slot = (uint32_t)K;
 
   // hash of the table's hot rows, then the rows themselves
   for (int i = threadIdx.x; i < kHotHash; i += kHotThreads) s_key[i] = -1;
   __syncthreads();
   hot_hash_insert(s_key, s_slotof, hot_rows + (int64_t)t * K, K);
   {
-    const int n16 = K * row_bytes / 16;
+    const int n16 = K * row_bytes / 16;  // 16-byte pieces of the hot rows in memory
     for (int q = threadIdx.x; q < n16; q += kHotThreads) {
       const int k = q / (row_bytes / 16), o = q % (row_bytes / 16);
       const int32_t r = hot_rows[(int64_t)t * K + k];
-      if (r >= 0)
-        reinterpret_cast<uint4*>(s_rows)[q] =
-            reinterpret_cast<const uint4*>(Wt + (int64_t)r * D)[o];
+      if (r >= 0) {
+        const uint4 x = reinterpret_cast<const uint4*>(Wt + (int64_t)r * D)[o];
+        if constexpr (WIDEN) {  // eight bf16 become eight f32: piece q lands at 32q
+          reinterpret_cast<uint4*>(s_rows)[2 * q] =
+              uint4{x.x << 16, x.x & 0xffff0000u, x.y << 16, x.y & 0xffff0000u};
+          reinterpret_cast<uint4*>(s_rows)[2 * q + 1] =
+              uint4{x.z << 16, x.z & 0xffff0000u, x.w << 16, x.w & 0xffff0000u};
+        } else {
+          reinterpret_cast<uint4*>(s_rows)[q] = x;
+        }
+      }
     }
-    for (int q = threadIdx.x; q < row_bytes / 16; q += kHotThreads)
-      reinterpret_cast<uint4*>(s_rows)[n16 + q] = uint4{0u, 0u, 0u, 0u};
+    for (int q = threadIdx.x; q < (int)lrow / 16; q += kHotThreads)
+      reinterpret_cast<uint4*>(s_rows + (size_t)K * lrow)[q] = uint4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
@@ -334,10 +351,10 @@ void fwd_pool_hot_kernel(
       else rw[r] = 1.f;
     }
   };
-  // Split a window held in registers into the cold and hot lists; cm = the
-  // cold lookups' bits, lookup w0+i at bit i of cm[i / 64].
-  auto stage = [&](const int32_t (&ri)[2], const float (&rw)[2], int32_t wn, uint64_t (&cm)[2]) {
-    uint64_t hm[2];
+  // Split a window held in registers into the cold and hot lists, and count
+  // the cold lookups before each position (s_cpre).
+  auto stage = [&](const int32_t (&ri)[2], const float (&rw)[2], int32_t wn) {
+    uint64_t cm[2], hm[2];  // cold and hot lookups' bits: position i at bit i % 64 of [i / 64]
     int32_t hs[2], id[2];
     // Wait for the window's loads here, outside any branch: a wait inside a
     // branch leaves the registers pending after it, and the next window's
@@ -388,12 +405,14 @@ void fwd_pool_hot_kernel(
       hm[r] = __ballot(valid[r] && hs[r] >= 0);
     }
     wave_lds_sync();  // the previous window's lists have been read
+    if (lane == 0) s_cpre[wave][wn] = (uint8_t)(__popcll(cm[0]) + __popcll(cm[1]));
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int i = lane + r * kWave;
       if (i < wn) {
+        const int cpos = (r ? __popcll(cm[0]) : 0) + __popcll(cm[r] & lt);  // cold before i
+        s_cpre[wave][i] = (uint8_t)cpos;
         if (hs[r] < 0) {
-          const int cpos = (r ? __popcll(cm[0]) : 0) + __popcll(cm[r] & lt);
           s_cidx[wave][cpos] = id[r];
           if constexpr (WEIGHTED) s_w[wave][cpos] = rw[r];
         } else {
@@ -416,22 +435,38 @@ void fwd_pool_hot_kernel(
       const bool ok = k < c1;
       const int kk = ok ? k : 0;
       idx[u] = s_cidx[wave][kk];
-      if constexpr (WEIGHTED) cs[u] = ok ? s_w[wave][kk] : 0.f;
+      if constexpr (WEIGHTED) cs[u] = s_w[wave][kk];
     }
+    // idx and the weights are read unconditionally (the padded lanes' select
+    // comes after), so the loads are not split into exec-masked ones
 #pragma unroll
-    for (int u = 0; u < CU; ++u) asm volatile("" ::"v"(idx[u]));
+    for (int u = 0; u < CU; ++u) {
+      asm volatile("" ::"v"(idx[u]));
+      if constexpr (WEIGHTED) asm volatile("" : "+v"(cs[u]));
+    }
+    if constexpr (WEIGHTED) {
+#pragma unroll
+      for (int u = 0; u < CU; ++u) cs[u] = c + u < c1 ? cs[u] : 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
       const uint32_t off = __umul24((uint32_t)idx[u], (uint32_t)row_bytes) + eb;
       cb[u] = buffer_load_raw<RAW>(wres, c + u < c1 && col_ok ? off : kNoRow);
     }
   };
-  auto add_rows = [&](ACC (&acc)[V], const RAW* rb, const float* rs, auto n) {
+  auto add_rows = [&](ACC (&acc)[V], const auto* rb, const float* rs, auto n) {
+    using R = std::remove_cv_t<std::remove_pointer_t<decltype(rb)>>;
 #pragma unroll
     for (int u = 0; u < decltype(n)::value; ++u) {
       const ACC sv = (ACC)rs[u];
       ACC x[V];
-      unpack<WT, V, ACC>(rb[u], x);
+      if constexpr (std::is_same<R, RAW>::value) {
+        unpack<WT, V, ACC>(rb[u], x);
+      } else {  // an LDS row widened to f32
+        const float* f = reinterpret_cast<const float*>(&rb[u]);
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[v] = (ACC)f[v];
+      }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         if constexpr (WEIGHTED) acc[v] += sv * x[v];
@@ -442,20 +477,18 @@ void fwd_pool_hot_kernel(
   // One window of the slot's bag [ob, oe): `pre` (the next group's loads),
   // the first cold batch, the hot rows while it is in flight, then the cold
   // batch and any further ones.
-  auto window = [&](int32_t w0, int32_t wn, const uint64_t (&cm)[2], int32_t ob, int32_t oe,
-                    ACC (&acc)[V], auto&& pre) {
+  auto window = [&](int32_t w0, int32_t wn, int32_t ob, int32_t oe, ACC (&acc)[V], auto&& pre) {
     int32_t lo = ob - w0, hi = oe - w0;
     lo = lo < 0 ? 0 : (lo > wn ? wn : lo);
     hi = hi < lo ? lo : (hi > wn ? wn : hi);
-    const int c0 = __popcll(cm[0] & mask_below(lo)) + __popcll(cm[1] & mask_below(lo - kWave));
-    const int c1 = __popcll(cm[0] & mask_below(hi)) + __popcll(cm[1] & mask_below(hi - kWave));
+    const int c0 = s_cpre[wave][lo], c1 = s_cpre[wave][hi];
     const int h0 = lo - c0, h1 = hi - c1;
     pre();  // before the cold rows: waiting for those then covers these too
     RAW cb[CU];
     float cs[CU] = {};
     cold_batch(c0, c1, cb, cs);
     for (int k = h0; k < h1; k += HU) {
-      RAW hb[HU];
+      HRAW hb[HU];
       float hsc[HU] = {};
       int hslot[HU];
 #pragma unroll
@@ -470,8 +503,14 @@ void fwd_pool_hot_kernel(
       for (int u = 0; u < HU; ++u) asm volatile("" ::"v"(hslot[u]));
 #pragma unroll
       for (int u = 0; u < HU; ++u) {
-        const int sl = k + u < h1 ? hslot[u] : zero_slot;
-        hb[u] = *reinterpret_cast<const RAW*>(s_rows + sl * row_bytes + eb_lds);
+        const uint32_t sl = k + u < h1 ? hslot[u] : zero_slot;
+        const unsigned char* q = s_rows + (__umul24(sl, lrow) + eb_lds);
+        if constexpr (sizeof(HRAW) == 32) {  // two 16-byte LDS reads, not eight of 4
+          hb[u].a = reinterpret_cast<const uint4*>(q)[0];
+          hb[u].b = reinterpret_cast<const uint4*>(q)[1];
+        } else {
+          hb[u] = *reinterpret_cast<const HRAW*>(q);
+        }
       }
       add_rows(acc, hb, hsc, std::integral_constant<int, HU>{});
     }
@@ -505,10 +544,9 @@ void fwd_pool_hot_kernel(
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = (ACC)0;
     const int32_t wn0 = J1 - J0 < kHotStage ? J1 - J0 : kHotStage;
-    uint64_t cm[2];
-    stage(ri, rw, wn0, cm);
+    stage(ri, rw, wn0);
     int32_t n2_b, n2_e;
-    window(J0, wn0, cm, cur_b, cur_e, acc, [&]() {
+    window(J0, wn0, cur_b, cur_e, acc, [&]() {
       load_window(nJ0, nJ1 - nJ0 < kHotStage ? nJ1 - nJ0 : kHotStage, ri, rw);
       load_offsets(g + 2 * stride, n2_b, n2_e);
     });
@@ -517,8 +555,8 @@ void fwd_pool_hot_kernel(
       int32_t xi[2];
       float xw[2];
       load_window(w0, wn, xi, xw);
-      stage(xi, xw, wn, cm);
-      window(w0, wn, cm, cur_b, cur_e, acc, []() {});
+      stage(xi, xw, wn);
+      window(w0, wn, cur_b, cur_e, acc, []() {});
     }
     const int32_t gn = bb1 - g < NS ? bb1 - g : NS;
     if (slot < gn && col_ok) {
@@ -544,9 +582,9 @@ hipError_t launch_hot_typed(const Problem& p, const RowShape& rs, const void* W,
                             const int32_t* indices, const int32_t* offsets, const float* psw,
                             const int32_t* tinfo, const int32_t* hot_rows, float* out,
                             hipStream_t s) {
-  const int64_t row = (int64_t)p.D * sizeof(WT);
+  const int64_t lrow = (int64_t)p.D * kHotLdsElem<WT>;
   // the hot rows and the zero row after them fit the kernel's LDS
-  if (row > kHotRowMax || (int64_t)p.hot_k * row > kHotBytes || p.hot_k > kHotMaxK)
+  if ((int64_t)(p.hot_k + 1) * lrow > kHotBytes || p.hot_k > kHotMaxK || p.hot_k < 1)
     return hipErrorInvalidValue;
   const int64_t per_table = (p.B + p.hot_bags - 1) / p.hot_bags;
   const int64_t nblocks = per_table * p.T;
@@ -636,8 +674,9 @@ hipError_t launch_hot_for_type(const Problem& p, const void* W, const int32_t* i
 }  // namespace
 
 // Hot rows per table for the forward after the transpose: as many as fit in
-// kHotBytes of LDS, at most 256 (the hash stays at most half full); 0 when the
-// row is not one pass of 16-byte multiples or the grid would be too small.
+// kHotBytes of LDS (bf16 rows widened to f32) with a row of zeros after them,
+// at most 256 (the hash stays at most a quarter full); 0 when the row is not
+// one pass of 16-byte multiples or the grid would be too small.
 void choose_hot(Problem* p) {
   p->hot_k = 0;
   p->hot_bags = 0;
@@ -647,8 +686,8 @@ void choose_hot(Problem* p) {
     return;
   // cold rows are read at 32-bit offsets below 2^31, rows numbered in 24 bits
   if (p->max_rows >= (int64_t(1) << 24) || p->max_rows * row >= (int64_t(1) << 31)) return;
-  if (row > kHotRowMax) return;
-  const int64_t k = std::min<int64_t>(256, kHotBytes / row);
+  const int64_t lrow = p->D * (p->wdtype == TBE_BF16 ? kHotLdsElem<bf16_t> : wbytes);
+  const int64_t k = std::min<int64_t>(256, kHotBytes / lrow - 1);  // and the zero row
   if (k < 16 || p->B < 1) return;
   int32_t bags = 2048;  // halve until the grid holds about four workgroups per CU
   while (bags > 256 && (int64_t)p->T * ((p->B + bags - 1) / bags) < 1024) bags /= 2;

@@ -4,7 +4,7 @@ before its cold ones. Its output is compared with the oracle on the whole
 batch (as is the plain gather's, given no metadata, on the same inputs), and
 the metadata it writes must equal that of tbe_preprocess. Checked on weighted
 bf16, unweighted f16 and f32 rows of 16, with more and with fewer long runs
-than the 256 hot rows a table holds, with bags longer than one staged window
+than the hot rows a table holds (255 rows of 256 bytes), with bags longer than one staged window
 of 128 lookups, and with the fused bounds check on planted bad indices (read
 as row 0, as the oracle is told)."""
 import dataclasses
@@ -71,7 +71,7 @@ def _forward_pair(cfg, batch, flags=0, S=0, dev=None, oracle_indices=None):
 
 
 @pytest.mark.parametrize("name,cfg,B", [
-    ("bf16_weighted", LARGE, 2048),        # 13-15 long runs per table: fewer than 256
+    ("bf16_weighted", LARGE, 2048),        # 13-15 long runs per table: fewer than 255
     ("f16", MEDIUM, 16384),
     ("f32_d16", dataclasses.replace(DEMO3, B=32768), 32768),
 ])
@@ -84,7 +84,8 @@ def test_forward_after_transpose_equals_plain_gather(name, cfg, B):
 
 def test_forward_after_transpose_many_hot_rows():
     """More than 256 long runs per table (uniform rows over 600 per table,
-    about 136 lookups each, with S = 16): the plan keeps the 256 longest."""
+    about 136 lookups each, with S = 16): the plan keeps the 255 longest
+    (one LDS row of the 64 KB holds zeros)."""
     from workloads import Config
     cfg = Config("hot_many", T=64, B=4096, D=128, rows=(600,) * 64, dtype="bf16",
                  bag=("fixed", 20), index=("uniform",), weighted=True,
