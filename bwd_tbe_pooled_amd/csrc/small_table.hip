@@ -445,7 +445,8 @@ __global__ __launch_bounds__(kThreads) void small_recount_forward_kernel(
 // the rows as plain arithmetic carries it) or lies outside its column's
 // scaled range, so that the f32 kernel launched next recomputes that partial;
 // 0 otherwise.
-__global__ __launch_bounds__(kThreads) void small_backward_kernel(
+// Three waves per SIMD (168 registers; the few spills are on the recount path).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void small_backward_kernel(
     const float* __restrict__ grad, const uint8_t* __restrict__ hist,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, float* __restrict__ partials,
@@ -484,37 +485,67 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
   int sc = 0;                  // this column's scale: the sums are in units of 2^-sc
   bool has_sc = false;         // set by the first tile with a nonzero gradient
 
-  // gradient of bag b0 + ks*16 + kb*8 + j at column d, in gn[ks*8 + j]
-  float gn[kBagTile / 2];
-  auto load_grad = [&](int32_t b0) {
+  // gradient of bag b0 + ks*16 + kb*8 + j at column d, in g[ks*8 + j]; the
+  // next tile's are loaded while this one is split and contracted. Every
+  // load is in bounds (a ragged tile rereads its last bag, a lane past D
+  // reads column D-1), and the returned mask, applied where the values are
+  // used, zeroes those: no select waits for the loads right after issue.
+  float gn[kBagTile / 2], gnext[kBagTile / 2];
+  auto load_grad = [&](int32_t b0, float (&g)[kBagTile / 2]) -> uint32_t {
     const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
+    if (nb <= 0) return 0u;
     if (nb == kBagTile) {
 #pragma unroll
       for (int ks = 0; ks < kBagTile / 16; ++ks)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float* row = gt + (int64_t)(b0 + ks * 16 + j) * gstride;  // uniform
-          const float g = row[lane_off];
-          gn[ks * 8 + j] = has_col ? g : 0.f;
+          g[ks * 8 + j] = row[lane_off];
         }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < kBagTile / 16; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float* row = gt + (int64_t)(b0 + ks * 16 + j) * gstride;
-          const int bl = ks * 16 + kb * 8 + j;
-          gn[ks * 8 + j] = (has_col && bl < nb) ? row[lane_off] : 0.f;
-        }
+      return has_col ? 0xffffffffu : 0u;
     }
+    uint32_t m = 0u;
+    const int32_t dc = d < D ? d : D - 1;
+#pragma unroll
+    for (int ks = 0; ks < kBagTile / 16; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int bl = ks * 16 + kb * 8 + j;
+        const int bc = bl < nb ? bl : nb - 1;
+        g[ks * 8 + j] = gt[(int64_t)(b0 + bc) * gstride + dc];
+        m |= (has_col && bl < nb ? 1u : 0u) << (ks * 8 + j);
+      }
+    return m;
   };
 
   typedef _Float16 half2v __attribute__((ext_vector_type(2)));
   const half2v ones = {(_Float16)1.f, (_Float16)1.f};
 
+  // Saved counts of bag hb, rows h16..h16+15, one tile ahead like the
+  // gradients and loaded before them (loads complete in order): a ragged
+  // tile rereads its last bag, zeroed where used.
+  const int hb = threadIdx.x >> 2, h16 = (threadIdx.x & 3) * 16;
+  auto load_hist = [&](int32_t b0) -> uint4 {
+    const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
+    if (recount || nb <= 0) return uint4{0, 0, 0, 0};
+    const int bc = hb < nb ? hb : nb - 1;
+    return *reinterpret_cast<const uint4*>(hist + ((int64_t)t * B + b0 + bc) * kSmallE + h16);
+  };
+  uint4 hnext = load_hist(sb0);
+  uint32_t mnext = load_grad(sb0, gnext);
   for (int32_t b0 = sb0; b0 < sb1; b0 += kBagTile) {
     const int nb = sb1 - b0 < kBagTile ? sb1 - b0 : kBagTile;
     const int64_t bag0 = (int64_t)t * B + b0;
+    const uint4 hv = hb < nb ? hnext : uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int q = 0; q < kBagTile / 2; ++q) gn[q] = (mnext >> q) & 1u ? gnext[q] : 0.f;
+    // this tile's values are taken before the next tile's loads are issued,
+    // so that the wait for them does not also wait for those
+#pragma unroll
+    for (int q = 0; q < kBagTile / 2; ++q) asm volatile("" ::"v"(gn[q]));
+    asm volatile("" ::"v"(hv.x), "v"(hv.y), "v"(hv.z), "v"(hv.w) : "memory");
+    hnext = load_hist(b0 + kBagTile);
+    mnext = load_grad(b0 + kBagTile, gnext);
     // B operands: this tile's gradients of column d times 2^sc, split into
     // hi = f16(x) and lo = f16((x - hi) * 2^11). sc is a power-of-two scale
     // per column (lanes i and i + 32 agree on it), set by the first tile with
@@ -524,7 +555,6 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     // the end (exact). A later tile whose largest scaled magnitude leaves
     // [2^-14, 2^15) (1024 times the first tile's largest, or 2^18 times less)
     // marks the split for the f32 kernel, like a non-finite one.
-    load_grad(b0);
     {
       float gmax = 0.f;
 #pragma unroll
@@ -559,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
     else __syncthreads();  // earlier readers of HT are done
     {
       // Counts of bag bl, rows e16..e16+15, into HT[e][bl] as f16 (exact).
-      const int bl = threadIdx.x >> 2, e16 = (threadIdx.x & 3) * 16;
+      const int bl = hb, e16 = h16;
       uint32_t c[16];
       if (recount) {
         const uint4* hp = reinterpret_cast<const uint4*>(&H[bl][e16]);
@@ -569,9 +599,7 @@ __global__ __launch_bounds__(kThreads) void small_backward_kernel(
           c[4 * q] = v.x; c[4 * q + 1] = v.y; c[4 * q + 2] = v.z; c[4 * q + 3] = v.w;
         }
       } else {
-        uint4 v = uint4{0, 0, 0, 0};
-        if (bl < nb) v = *reinterpret_cast<const uint4*>(hist + (bag0 + bl) * kSmallE + e16);
-        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t wds[4] = {hv.x, hv.y, hv.z, hv.w};
 #pragma unroll
         for (int q = 0; q < 16; ++q) c[q] = (wds[q >> 2] >> (8 * (q & 3))) & 0xffu;
       }
@@ -719,8 +747,9 @@ __global__ void zero_counts_kernel(int32_t* counts) {
 }  // namespace
 
 int small_splits_for(int32_t T, int32_t B) {
-  // About 1024 workgroups over the whole problem, at least 256 bags each.
-  int64_t per_table = 1024 / (T > 0 ? T : 1);
+  // About three workgroups per CU over the whole problem (the backward holds
+  // three per CU: one round, no tail), at least 256 bags each.
+  int64_t per_table = 3 * (int64_t)device_cu_count() / (T > 0 ? T : 1);
   if (per_table < 1) per_table = 1;
   int64_t max_splits = (B + 255) / 256;
   if (max_splits < 1) max_splits = 1;
