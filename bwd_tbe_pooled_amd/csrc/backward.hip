@@ -57,12 +57,6 @@ __device__ __forceinline__ void zero_acc(ACC (&acc)[PMAX][V]) {
     for (int v = 0; v < V; ++v) acc[p][v] = (ACC)0;
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // All row slots of a wave accumulate sorted slots [k0, k1) of one run of table
 // t: slot s takes k0+s, k0+s+NS, ...; bag ids and weights of 64 slots at a
 // time are loaded coalesced and handed to the slots with shuffles. On return

@@ -128,6 +128,14 @@ __device__ __forceinline__ R buffer_load_raw(__amdgpu_buffer_rsrc_t r, uint32_t 
   }
 }
 
+// A wave's LDS writes are visible to all its lanes after this (the wave's
+// lanes exchange data through LDS without a workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Unpack V elements from a raw vector into accumulator values.
 template <typename T, int V, typename ACC>
 __device__ __forceinline__ void unpack(const typename raw_vec<T, V>::type& r, ACC (&out)[V]) {

@@ -28,12 +28,6 @@ constexpr int kFwdThreads = 256;
 constexpr int kFwdWaves = kFwdThreads / kWave;
 constexpr int kStage = 256;  // staged lookups per wave and window
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // CHECK: the bounds check fused into the gather (an index outside its table
 // is read as row 0 and sets TBE_ERROR_INDEX in *err).
 //

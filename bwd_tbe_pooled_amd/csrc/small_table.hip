@@ -148,10 +148,11 @@ __device__ __forceinline__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_o
 // Saturating uint8 counts of kCountTiles consecutive 64-bag tiles of one
 // table, written to hist, and the flags: counts[4] when a count exceeds 255,
 // counts[5] when one exceeds 2048. Grid (ceil(B / (64 * kCountTiles)), T).
-// The tiles are pipelined: wave w owns bags 16w .. 16w+15 of each tile, and
-// the first 64 lookups of its bags in tile k+1 are loaded (one coalesced
-// load per bag) before it counts tile k with LDS atomics; the thread that
-// packs a count row into hist also clears it for the next tile.
+// The tiles are pipelined: wave w owns bags 16w .. 16w+15 of each tile (its
+// own rows of H), and the first 64 lookups of its bags in tile k+1 are loaded
+// (one coalesced load per bag) before it counts tile k with LDS atomics; it
+// then packs its rows into hist and clears them for the next tile. The waves
+// share no rows, so after the first barrier they run without any.
 template <bool CHECK>
 __global__ __launch_bounds__(kThreads) void small_count_kernel(
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
@@ -221,10 +222,11 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
           if (c + q * kWave + lane < len) atomicAdd(&H[bl][count_row<CHECK>(x[q], Et, bad)], 1u);
       }
     }
-    __syncthreads();
+    wave_lds_sync();  // this wave's atomics have landed
     const int64_t bag0 = wbag0 + tb0;
-    for (int q = threadIdx.x; q < nb * (kSmallE / 4); q += kThreads) {
-      const int bl = q >> 4, e4 = (q & 15) * 4;
+    for (int q = lane; q < NBW * (kSmallE / 4); q += kWave) {
+      const int bl = wave * NBW + (q >> 4), e4 = (q & 15) * 4;
+      if (bl >= nb) break;
       uint4* hp = reinterpret_cast<uint4*>(&H[bl][e4]);
       const uint4 c = *hp;
       *hp = uint4{0, 0, 0, 0};
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void small_count_kernel(
                               (c.z > 255u ? 255u : c.z) << 16 | (c.w > 255u ? 255u : c.w) << 24;
       *reinterpret_cast<uint32_t*>(hist + (bag0 + bl) * kSmallE + e4) = packed;
     }
-    __syncthreads();
+    wave_lds_sync();  // cleared before this wave's next atomics
   }
   if constexpr (CHECK) {
     if (__ballot(bad) != 0 && lane == 0) atomicOr(err, (int32_t)TBE_ERROR_INDEX);
