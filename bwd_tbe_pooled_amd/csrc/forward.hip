@@ -240,6 +240,12 @@ __device__ __forceinline__ uint64_t mask_below(int n) {  // bits [0, n)
   return n <= 0 ? 0ull : n >= 64 ? ~0ull : ((1ull << n) - 1ull);
 }
 
+// Bits of m below this lane's (v_mbcnt: two instructions).
+__device__ __forceinline__ int count_below_lane(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 template <typename WT, int V, bool WEIGHTED, bool CHECK>
 __global__ __launch_bounds__(kHotThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void fwd_pool_hot_kernel(
@@ -283,7 +289,6 @@ void fwd_pool_hot_kernel(
   const int row_bytes = D * (int)sizeof(WT);
   const int e = col * V;
   const bool col_ok = e < D;
-  const uint64_t lt = mask_below(lane);
   // Cold rows come through a buffer resource over the table (at most 2 GiB and
   // 2^24 rows, so a row's offset is a 24-bit product): a lane with nothing to
   // load gives an offset past the end, and the load returns zeros.
@@ -376,7 +381,15 @@ void fwd_pool_hot_kernel(
         if (j >= 0) { f = (int32_t)(b * 4 + j); go = false; }
         else if (q.w < 0) go = false;  // entries fill in order: an empty one ends the search
       };
-      while (go0 || go1) {
+      {  // the first probe of both, outside the loop: most searches end there
+        const int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
+        const int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
+        look(q0, id[0], b0, go0, f0);
+        look(q1, id[1], b1, go1, f1);
+        b0 = (b0 + 1) & (kHotBuckets - 1);
+        b1 = (b1 + 1) & (kHotBuckets - 1);
+      }
+      while (go0 || go1) {  // a full bucket: the search goes on in the next
         const int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
         const int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
         if (go0) {
@@ -404,13 +417,13 @@ void fwd_pool_hot_kernel(
     for (int r = 0; r < 2; ++r) {
       const int i = lane + r * kWave;
       if (i < wn) {
-        const int cpos = (r ? __popcll(cm[0]) : 0) + __popcll(cm[r] & lt);  // cold before i
+        const int cpos = (r ? __popcll(cm[0]) : 0) + count_below_lane(cm[r]);  // cold before i
         s_cpre[wave][i] = (uint8_t)cpos;
         if (hs[r] < 0) {
           s_cidx[wave][cpos] = id[r];
           if constexpr (WEIGHTED) s_w[wave][cpos] = rw[r];
         } else {
-          const int hpos = (r ? __popcll(hm[0]) : 0) + __popcll(hm[r] & lt);
+          const int hpos = (r ? __popcll(hm[0]) : 0) + count_below_lane(hm[r]);
           s_hslot[wave][hpos] = (uint8_t)hs[r];
           if constexpr (WEIGHTED) s_w[wave][kHotStage - 1 - hpos] = rw[r];
         }
