@@ -226,9 +226,11 @@ constexpr int kHotBytes = 65536;      // LDS for the hot rows and one row of zer
 constexpr int kHotThreads = 512;
 constexpr int kHotWaves = kHotThreads / kWave;
 constexpr int kHotStage = 2 * kWave;  // staged lookups per wave and window
-// rows in flight per row slot: cold 8 of 16-byte pieces, 4 of 32-byte pieces
-// (f32 rows of 128 or more); hot 2 of 16 or 32 bytes, 4 of smaller ones
-template <int RAW_BYTES> constexpr int kColdUnroll = RAW_BYTES > 16 ? 4 : 8;
+// rows in flight per row slot: cold 5 of 16-byte pieces (a batch is issued
+// whole, and a bag averages about six cold rows at the Zipf-skewed batch:
+// 3, 4, 6, 7 and 8 measured slower), 4 of 32-byte pieces (f32 rows of 128 or
+// more); hot 2 of 16 or 32 bytes, 4 of smaller ones
+template <int RAW_BYTES> constexpr int kColdUnroll = RAW_BYTES > 16 ? 4 : 5;
 template <int RAW_BYTES> constexpr int kHotUnroll = RAW_BYTES >= 16 ? 2 : 4;
 // bf16 hot rows are held in LDS widened to f32 (a bf16 is the upper half of an
 // f32), so the hot lookups cost one multiply-add per element and no unpack;
