@@ -15,7 +15,10 @@ namespace {
 // hot_min[t] = v, or INT32_MAX when the table has no hot run: a long run is
 // hot exactly when its length is at least hot_min of its table; and
 // hot_flag[t] = 0 (the backward of the hot rows sets it to send them back to
-// the chunk path).
+// the chunk path). The table's run lengths are read once into LDS (when there
+// are at most kPlanCache long runs; otherwise each count rereads them), and v
+// is found by bisection between S and the longest run.
+constexpr int kPlanCache = 4096;
 __global__ __launch_bounds__(256) void hot_plan_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ long_runs,
     const int32_t* __restrict__ run_offsets, const int32_t* __restrict__ run_keys,
@@ -25,6 +28,7 @@ __global__ __launch_bounds__(256) void hot_plan_kernel(
   __shared__ int32_t s_range[2];
   __shared__ int32_t s_n;
   __shared__ int32_t red[256 / kWave];
+  __shared__ int32_t s_len[kPlanCache];
   const int32_t t = blockIdx.x;
   const int64_t n_long = counts[2];
   const int32_t first = tinfo[t];
@@ -45,24 +49,43 @@ __global__ __launch_bounds__(256) void hot_plan_kernel(
   }
   __syncthreads();
   const int32_t l0 = s_range[0], l1 = s_range[1];
-  auto len = [&](int32_t l) {
+  const bool cached = l1 - l0 <= kPlanCache;
+  auto len_global = [&](int32_t l) {
     const int32_t u = long_runs[l];
     return run_offsets[u + 1] - run_offsets[u];
   };
-  auto count_ge = [&](int32_t v) {
-    int32_t c = 0;
-    for (int32_t l = l0 + threadIdx.x; l < l1; l += blockDim.x) c += len(l) >= v;
-    for (int m = 1; m < kWave; m <<= 1) c += __shfl_xor(c, m);
+  auto len = [&](int32_t l) { return cached ? s_len[l - l0] : len_global(l); };
+  // block-wide sum (op 0) or maximum (op 1) of one value per thread
+  auto block_reduce = [&](int32_t c, int op) {
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int32_t o = __shfl_xor(c, m);
+      c = op ? (o > c ? o : c) : c + o;
+    }
     __syncthreads();
     if (lane_id() == 0) red[threadIdx.x / kWave] = c;
     __syncthreads();
-    int32_t tot = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) tot += red[w];
+    int32_t tot = op ? red[0] : 0;
+    for (int w = op ? 1 : 0; w < (int)(blockDim.x / kWave); ++w)
+      tot = op ? (red[w] > tot ? red[w] : tot) : tot + red[w];
     return tot;
+  };
+  int32_t mx = 0;
+  for (int32_t l = l0 + threadIdx.x; l < l1; l += blockDim.x) {
+    const int32_t n = len_global(l);
+    if (cached) s_len[l - l0] = n;
+    mx = n > mx ? n : mx;
+  }
+  mx = block_reduce(mx, 1);  // its barriers also publish s_len
+  auto count_ge = [&](int32_t v) {
+    int32_t c = 0;
+    for (int32_t l = l0 + threadIdx.x; l < l1; l += blockDim.x) c += len(l) >= v;
+    return block_reduce(c, 0);
   };
   int32_t v = S;
   if (count_ge(v) > K) {
-    int32_t lo = v + 1, hi = 0x7fffffff;
+    // more than K runs reach S, so mx >= S and v is in (S, mx + 1]: above the
+    // longest no run is counted (more than K runs tied at mx leave v = mx + 1)
+    int32_t lo = v + 1, hi = mx < 0x7fffffff ? mx + 1 : mx;
     while (lo < hi) {
       const int32_t mid = lo + (hi - lo) / 2;
       if (count_ge(mid) <= K) hi = mid;
@@ -75,7 +98,8 @@ __global__ __launch_bounds__(256) void hot_plan_kernel(
     int32_t q = -1;
     if (len(l) >= v) {
       q = atomicAdd(&s_n, 1);  // slot order does not change any value computed
-      hot_rows[(int64_t)t * K + q] = run_keys[long_runs[l]] - first;
+      if (q < K) hot_rows[(int64_t)t * K + q] = run_keys[long_runs[l]] - first;
+      else q = -1;  // cannot happen: at most K runs reach v
     }
     if (run_slot) run_slot[l] = q < 0 ? -1 : t * K + q;
   }

@@ -95,6 +95,19 @@ def test_forward_after_transpose_many_hot_rows():
     assert n_long >= 600 * 64 * 0.9
 
 
+def test_forward_after_transpose_many_long_runs_per_table():
+    """About 6000 long runs per table (uniform rows over 6000 per table, about
+    27 lookups each, with S = 16): more runs than the plan holds in LDS, so it
+    reads their lengths from the run list at every count."""
+    from workloads import Config
+    cfg = Config("hot_many_runs", T=8, B=8192, D=128, rows=(6000,) * 8, dtype="bf16",
+                 bag=("fixed", 20), index=("uniform",), weighted=True,
+                 preprocess_in_forward=True, seed=73)
+    batch = make_batch(cfg)
+    n_long, _, _ = _forward_pair(cfg, batch, S=16)
+    assert n_long > 8 * 4096
+
+
 def test_forward_after_transpose_with_fused_bounds_check():
     import bwd_tbe_pooled_amd as tbe
     batch = make_batch(LARGE, B=2048)
