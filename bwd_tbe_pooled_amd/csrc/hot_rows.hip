@@ -33,15 +33,33 @@ __global__ __launch_bounds__(256) void hot_plan_kernel(
   const int64_t n_long = counts[2];
   const int32_t first = tinfo[t];
   for (int i = threadIdx.x; i < K; i += blockDim.x) hot_rows[(int64_t)t * K + i] = -1;
-  if (threadIdx.x < 2) {
-    const int32_t key = threadIdx.x == 0 ? first : first + tinfo[T + t];
-    int64_t lo = 0, hi = n_long;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) / 2;
-      if (run_keys[long_runs[mid]] < key) lo = mid + 1;
-      else hi = mid;
+  {
+    // The table's range of the long-run list: the first run at or above each
+    // of its two bounding keys, by a 128-way search (threads 0-127 for the
+    // first key, 128-255 for the second). Each round probes 128 evenly spaced
+    // runs of [lo, hi); those below the key are a prefix of c probes, and the
+    // answer lies after the last of them and at or before the next.
+    const int half = threadIdx.x >> 7, j = threadIdx.x & 127;
+    const int32_t key = half == 0 ? first : first + tinfo[T + t];
+    int32_t lo = 0, hi = (int32_t)n_long;
+    while (__syncthreads_or(lo < hi)) {
+      const int32_t step = (hi - lo + 127) / 128;
+      const int32_t q = lo + j * step;
+      const bool below = lo < hi && q < hi && run_keys[long_runs[q]] < key;
+      const int32_t c0 = __syncthreads_count(half == 0 && below);
+      const int32_t c1 = __syncthreads_count(half == 1 && below);
+      const int32_t c = half ? c1 : c0;
+      if (lo < hi) {
+        if (c == 0) {
+          hi = lo;
+        } else {
+          const int32_t nhi = lo + c * step < hi ? lo + c * step : hi;
+          lo = lo + (c - 1) * step + 1;
+          hi = nhi;
+        }
+      }
     }
-    s_range[threadIdx.x] = (int32_t)lo;
+    if (j == 0) s_range[half] = lo;
   }
   if (threadIdx.x == 0) {
     s_n = 0;
