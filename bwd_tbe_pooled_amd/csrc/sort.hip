@@ -114,66 +114,56 @@ __device__ __forceinline__ TileInfo tile_info(int64_t g, const int4* __restrict_
   return ti;
 }
 
-// Per-tile digit counts (digits of at most 7 bits). Each thread counts its
-// elements into its own column of byte counters, cnt[d mod 32][thread] byte
-// (d / 32), so no two lanes ever update the same word; then eight threads per
-// row add the row's 256 columns with 16-bit lanes (sums fit: at most 4096 per
-// tile) and combine with shuffles. Rows are padded by one word and the
-// summing threads start at staggered columns, so LDS banks rarely collide.
+// Per-tile digit counts (digits of at most 7 bits), one 128-bin LDS histogram
+// per wave. A wave's 64 lanes hold 64 consecutive keys; after the lower
+// digits' passes equal digits sit together, so only the first lane of each
+// run of equal digits adds the run's length (one atomic per run, not per key).
 __global__ __launch_bounds__(kThreads) void sort_upsweep_kernel(
     const int32_t* __restrict__ keys, const int4* __restrict__ tile_desc, int shift, int bits,
     int64_t tiles_max, int32_t* __restrict__ digit_counts, const int32_t* __restrict__ clamp_rows) {
-  __shared__ uint32_t cnt[32][kThreads + 1];
+  constexpr int kUpWaves = kThreads / kWave;
+  __shared__ uint32_t hist[kUpWaves][128];
   const int64_t g = xcd_logical_block(tiles_max);
   if (g < 0) return;
   const TileInfo ti = tile_info(g, tile_desc);
   if (!ti.valid) return;
   const int tid = threadIdx.x;
-  const int radix = 1 << bits;
-  const uint32_t mask = (uint32_t)radix - 1;
-#pragma unroll
-  for (int r = 0; r < 32; ++r) cnt[r][tid] = 0;
+  const int wave = tid / kWave;
+  const int lane = lane_id();
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int i = tid; i < kUpWaves * 128; i += kThreads) (&hist[0][0])[i] = 0u;
   int32_t key[kItems];
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
     const int32_t j = ti.a + q * kThreads + tid;
     key[q] = j < ti.e ? keys[j] : 0;
   }
-  if (clamp_rows) {  // bounds check of the first pass: a bad row sorts as row 0
-    const uint32_t Et = (uint32_t)clamp_rows[ti.t];
-#pragma unroll
-    for (int q = 0; q < kItems; ++q) key[q] = (uint32_t)key[q] < Et ? key[q] : 0;
-  }
+  const uint32_t Et = clamp_rows ? (uint32_t)clamp_rows[ti.t] : 0u;
+  __syncthreads();
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
-    if (ti.a + q * kThreads + tid < ti.e) {
-      const uint32_t d = ((uint32_t)key[q] >> shift) & mask;
-      // own column: no other thread touches the word; the atomic is one LDS
-      // instruction instead of a read, an add and a write
-      __hip_atomic_fetch_add(&cnt[d & 31][tid], 1u << (8 * (d >> 5)), __ATOMIC_RELAXED,
+    const bool ok = ti.a + q * kThreads + tid < ti.e;
+    // TBE_FLAG_CHECK (first pass): a row outside the table sorts as row 0
+    const uint32_t k = (clamp_rows && (uint32_t)key[q] >= Et) ? 0u : (uint32_t)key[q];
+    const int d = ok ? (int)((k >> shift) & mask) : -1;
+    const int dp = __shfl_up(d, 1);
+    const bool head = ok && (lane == 0 || dp != d);
+    const uint64_t heads = __ballot(head);
+    const uint64_t valid = __ballot(ok);
+    if (head) {
+      // the run ends at the next head or at the last valid lane
+      const uint64_t after = lane == 63 ? 0ull : (heads | ~valid) & (~0ull << (lane + 1));
+      const int end = after ? __builtin_ctzll(after) : 64;
+      __hip_atomic_fetch_add(&hist[wave][d], (uint32_t)(end - lane), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
   __syncthreads();
-  const int row = tid >> 3, part = tid & 7;
-  uint32_t lo = 0, hi = 0;  // 16-bit lanes: digits row, row+64 | row+32, row+96
-#pragma unroll 8
-  for (int c = 0; c < 32; ++c) {
-    const uint32_t w = cnt[row][part * 32 + ((c + part * 4) & 31)];
-    lo += w & 0x00FF00FFu;
-    hi += (w >> 8) & 0x00FF00FFu;
-  }
+  if (tid < 128) {
+    uint32_t c = 0u;
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    lo += __shfl_xor(lo, m);
-    hi += __shfl_xor(hi, m);
-  }
-  if (part == 0) {
-    const int32_t c0 = lo & 0xFFFF, c64 = lo >> 16, c32 = hi & 0xFFFF, c96 = hi >> 16;
-    if (row < radix) digit_counts[(int64_t)row * tiles_max + g] = c0;
-    if (row + 32 < radix) digit_counts[(int64_t)(row + 32) * tiles_max + g] = c32;
-    if (row + 64 < radix) digit_counts[(int64_t)(row + 64) * tiles_max + g] = c64;
-    if (row + 96 < radix) digit_counts[(int64_t)(row + 96) * tiles_max + g] = c96;
+    for (int v = 0; v < kUpWaves; ++v) c += hist[v][tid];
+    if (tid <= (int)mask) digit_counts[(int64_t)tid * tiles_max + g] = (int32_t)c;
   }
 }
 
