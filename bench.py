@@ -332,7 +332,7 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
     if headline and not wide and args.check != "validate":
         g_ms = graph_ms(torch, step, steps)
 
-    fwd_ms = avg["fwd_pool"]
+    fwd_ms = avg["fwd_pool"] + avg.get("hot_plan", 0.0)   # the gather, and its hot-row plan
     pre_ms = avg["linearize"] + avg["sort"] + avg["rle_route"]
     bwd_ms = (avg["bwd_short"] + avg.get("bwd_hot", 0.0) + avg["long_schedule"] + avg["bwd_long"]
               + avg["bwd_apply"])
@@ -446,11 +446,14 @@ def measure_small(torch, tbe, cfg, batch, args, scratch, *, headline=False):
     return res
 
 
-def all_hot_forward_ms(torch, tbe, cfg, batch, steps=5):
+def all_hot_forward_ms(torch, tbe, cfg, batch, steps=5, transpose=True):
     """The forward gather on the headline batch's bags with every lookup
     redirected to one of its table's first 64 rows (512 KiB of weights in
-    all): the same kernel and gather count, every row an L2 hit. Its time is
-    the gather's own L2-hit ceiling on this batch shape."""
+    all): the same gather count, every row an L2 hit. With `transpose` it is
+    the headline's forward (the transpose, then the gather that reads each
+    table's hot rows from LDS; those 64 rows are then all hot), and its gather
+    stage is that kernel's time with no row read from memory; without, the
+    plain gather, whose time is then its own L2-hit ceiling."""
     from workloads import init_weights
     dev = torch.device("cuda")
     idx = torch.from_numpy(batch.indices).to(dev) & 63
@@ -459,16 +462,22 @@ def all_hot_forward_ms(torch, tbe, cfg, batch, steps=5):
     W = init_weights(cfg, dev)
     out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device=dev)
     desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype)
-    ws = tbe.workspace(desc, idx.numel(), psw is not None, tbe.TBE_OP_FORWARD)
-    tbe.tbe_forward(desc, W, idx, off, psw, out, None, ws)
+    N, weighted = idx.numel(), psw is not None
+    meta = tbe.Meta(desc, N, weighted, with_pos=False) if transpose else None
+    ws = tbe.workspace(desc, N, weighted,
+                       tbe.TBE_OP_FORWARD_PREPROCESS if transpose else tbe.TBE_OP_FORWARD)
+    tbe.tbe_forward(desc, W, idx, off, psw, out, meta, ws)
     timer = tbe.Timer(capacity=steps + 1)
     desc.set_timer(timer)
     for _ in range(steps):
-        tbe.tbe_forward(desc, W, idx, off, psw, out, None, ws)
+        tbe.tbe_forward(desc, W, idx, off, psw, out, meta, ws)
     torch.cuda.synchronize()
     desc.set_timer(None)
-    ms, n = timer.read()["fwd_pool"]
-    del idx, off, psw, W, out, ws
+    t = timer.read()
+    ms, n = t["fwd_pool"]
+    if transpose and t["hot_plan"][1] == 0:
+        log("all-hot probe: the forward after the transpose did not take the hot rows")
+    del idx, off, psw, W, out, ws, meta
     torch.cuda.empty_cache()
     return round(ms / n, 4)
 
@@ -618,7 +627,9 @@ def main():
         probes["l2_gather_GBps_512B_rows"] = l2_gather_ceiling(torch, tbe, dev, 128)
         probes["stream_copy_GBps"] = stream_copy_gbps(torch, dev)
         if args.workload == "large" and not diagnostic:
-            probes["fwd_pool_all_l2_hits_ms"] = all_hot_forward_ms(torch, tbe, cfg, batch)
+            probes["fwd_pool_all_hot_ms"] = all_hot_forward_ms(torch, tbe, cfg, batch)
+            probes["fwd_plain_all_l2_hits_ms"] = all_hot_forward_ms(torch, tbe, cfg, batch,
+                                                                    transpose=False)
 
     # dominant single kernel, on the compulsory-byte model
     ks = head["kernels"]
@@ -642,10 +653,11 @@ def main():
         if ceil:
             roofline["l2_gather_ceiling_GBps"] = ceil
             roofline["frac_of_l2_gather_ceiling"] = round(dk["gathered_GBps"] / ceil, 4)
-    if "fwd_pool_all_l2_hits_ms" in probes and "fwd_pool" in ks:
-        ks["fwd_pool"]["all_l2_hits_ms"] = probes["fwd_pool_all_l2_hits_ms"]
-        ks["fwd_pool"]["frac_of_all_l2_hits_speed"] = round(
-            probes["fwd_pool_all_l2_hits_ms"] / ks["fwd_pool"]["ms"], 4)
+    if "fwd_pool_all_hot_ms" in probes and "fwd_pool" in ks:
+        # the same gather with every row hot: its own time with no row from memory
+        ks["fwd_pool"]["all_hot_ms"] = probes["fwd_pool_all_hot_ms"]
+        ks["fwd_pool"]["frac_of_all_hot_speed"] = round(
+            probes["fwd_pool_all_hot_ms"] / ks["fwd_pool"]["ms"], 4)
     for k, v in ks.items():
         if "gathered_GBps" in v:
             row_bytes = 4 * cfg.D if k != "fwd_pool" else cfg.D * (2 if cfg.dtype != "f32" else 4)

@@ -377,8 +377,10 @@ tbe_status forward_impl(const tbe_desc* desc, const Problem& p, const void* W,
     // from LDS (same values, same order: the same output bits)
     if ((st = run_preprocess(desc, p, indices, offsets, psw, *meta, ws, L, s)) != TBE_OK) return st;
     int32_t* hot = at<int32_t>(ws, L.hot_rows);
-    timer_begin(desc->timer, TBE_STAGE_FWD_POOL, s);
+    timer_begin(desc->timer, TBE_STAGE_HOT_PLAN, s);
     TBE_TRY_HIP(launch_hot_plan(p, *meta, tinfo, p.hot_k, hot, nullptr, nullptr, nullptr, s));
+    timer_end(desc->timer, TBE_STAGE_HOT_PLAN, s);
+    timer_begin(desc->timer, TBE_STAGE_FWD_POOL, s);
     TBE_TRY_HIP(launch_forward_pool_hot(p, W, indices, offsets, psw, tinfo, hot, out, s));
     timer_end(desc->timer, TBE_STAGE_FWD_POOL, s);
     return TBE_OK;

@@ -124,7 +124,9 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
 
 /* Stages a timer can attribute device time to. */
 typedef enum {
-    TBE_STAGE_FWD_POOL = 0,     /* generic forward gather-and-pool            */
+    TBE_STAGE_FWD_POOL = 0,     /* generic forward gather-and-pool (after the
+                                   transpose: the gather that reads the hot
+                                   rows from LDS)                            */
     TBE_STAGE_LINEARIZE = 1,    /* sort setup: table segments and tiles       */
     TBE_STAGE_SORT = 2,         /* radix passes                               */
     TBE_STAGE_RLE_ROUTE = 3,    /* run-length encoding and routing            */
@@ -140,7 +142,9 @@ typedef enum {
     TBE_STAGE_LONG_SCHEDULE = 11, /* per-XCD order of the long-run chunks     */
     TBE_STAGE_SMALL_COUNT = 12, /* small-table per-bag row counts             */
     TBE_STAGE_BWD_HOT = 13,     /* hot rows: plan + matrix-core contraction   */
-    TBE_NUM_STAGES = 14
+    TBE_STAGE_HOT_PLAN = 14,    /* the forward's hot-row plan (after the
+                                   transpose, when the hot rows are on)       */
+    TBE_NUM_STAGES = 15
 } tbe_stage;
 
 typedef struct tbe_timer tbe_timer;   /* opaque; see tbe_timer_create */

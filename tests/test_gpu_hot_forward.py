@@ -43,14 +43,19 @@ def _forward_pair(cfg, batch, flags=0, S=0, dev=None, oracle_indices=None):
     out_hot = torch.full((cfg.B, cfg.T * cfg.D), float("nan"), device="cuda")
     out_plain = torch.full((cfg.B, cfg.T * cfg.D), float("nan"), device="cuda")
     meta = tbe.Meta(d1, N, weighted)
+    timer = tbe.Timer(4)
+    d1.set_timer(timer)
     tbe.tbe_forward(d1, W, dev["indices"], dev["offsets"], dev["psw"], out_hot, meta,
                     tbe.workspace(d1, N, weighted, tbe.TBE_OP_FORWARD_PREPROCESS))
+    d1.set_timer(None)
     tbe.tbe_forward(d2, W, dev["indices"], dev["offsets"], dev["psw"], out_plain, None,
                     tbe.workspace(d2, N, weighted, tbe.TBE_OP_FORWARD))
     meta2 = tbe.Meta(d2, N, weighted)
     tbe.tbe_preprocess(d2, dev["indices"], dev["offsets"], dev["psw"], meta2,
                        tbe.workspace(d2, N, weighted, tbe.TBE_OP_PREPROCESS))
     torch.cuda.synchronize()
+    # the case is only a test of the forward after the transpose if it took the hot rows
+    assert timer.read()["hot_plan"][1] == 1, "the forward after the transpose did not run"
     idx = batch.indices if oracle_indices is None else oracle_indices
     keys, _ = oracle.linearize(cfg.T, cfg.B, cfg.rows, idx, batch.offsets)
     need = np.unique(keys)
@@ -125,11 +130,12 @@ def test_forward_after_transpose_with_fused_bounds_check():
 
 
 def test_forward_after_transpose_long_bags():
-    """Bags of 150-400 lookups: a group of bags spans several staged windows,
-    and a bag's cold rows need several batches."""
+    """Bags of 150-300 lookups: a group of bags spans several staged windows,
+    and a bag's cold rows need several batches (8 tables of 8192 bags: enough
+    workgroups for the forward after the transpose)."""
     from workloads import Config
-    cfg = Config("hot_long_bags", T=4, B=4096, D=64, rows=(3000,) * 4, dtype="bf16",
-                 bag=("uniform", 150, 400), index=("zipf", 1.05), weighted=True,
+    cfg = Config("hot_long_bags", T=8, B=8192, D=64, rows=(3000,) * 8, dtype="bf16",
+                 bag=("uniform", 150, 300), index=("zipf", 1.05), weighted=True,
                  preprocess_in_forward=True, seed=73)
     batch = make_batch(cfg)
     n_long, _, _ = _forward_pair(cfg, batch)
