@@ -238,10 +238,6 @@ template <int RAW_BYTES> constexpr int kHotUnroll = RAW_BYTES >= 16 ? 2 : 4;
 template <typename WT> constexpr bool kHotWiden = std::is_same<WT, bf16_t>::value;
 template <typename WT> constexpr int kHotLdsElem = kHotWiden<WT> ? 4 : (int)sizeof(WT);
 
-__device__ __forceinline__ uint64_t mask_below(int n) {  // bits [0, n)
-  return n <= 0 ? 0ull : n >= 64 ? ~0ull : ((1ull << n) - 1ull);
-}
-
 // Bits of m below this lane's (v_mbcnt: two instructions).
 __device__ __forceinline__ int count_below_lane(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
