@@ -2,8 +2,10 @@
 table from LDS and the rest from global memory, and sums a bag's hot rows
 before its cold ones. Its output is compared with the oracle on the whole
 batch (as is the plain gather's, given no metadata, on the same inputs), and
-the metadata it writes must equal that of tbe_preprocess. Checked on weighted
-bf16, unweighted f16 and f32 rows of 16, with more and with fewer long runs
+the metadata it writes must equal that of tbe_preprocess, and the stage timer
+must show that the hot rows were taken. Checked on weighted and unweighted
+bf16 (rows held widened to f32 in LDS), bf16 rows of 96 (four idle lanes per
+row slot), empty bags, unweighted f16 and f32 rows of 16, with more and with fewer long runs
 than the hot rows a table holds (255 rows of 256 bytes), with bags longer than one staged window
 of 128 lookups, and with the fused bounds check on planted bad indices (read
 as row 0, as the oracle is told)."""
@@ -75,8 +77,22 @@ def _forward_pair(cfg, batch, flags=0, S=0, dev=None, oracle_indices=None):
     return int(h1["counts"][2]), int(err1.item()), int(err2.item())
 
 
+def _cfg(name, **kw):
+    from workloads import Config
+    base = dict(T=8, B=8192, D=128, rows=(3000,) * 8, dtype="bf16", bag=("poisson", 20.0),
+                index=("zipf", 1.05), weighted=True, preprocess_in_forward=True, seed=79)
+    base.update(kw)
+    return Config(name, **base)
+
+
 @pytest.mark.parametrize("name,cfg,B", [
-    ("bf16_weighted", LARGE, 2048),        # 13-15 long runs per table: fewer than 255
+    ("bf16_weighted", LARGE, 2048),        # 13-15 long runs per table: fewer than 127
+    ("bf16_unweighted", dataclasses.replace(LARGE, weighted=False), 2048),
+    # 12 of a slot's 16 lanes hold the row; 169 widened rows per table
+    ("bf16_d96", _cfg("hot_d96", D=96), 8192),
+    # about 5% of the bags are empty
+    ("bf16_empty_bags", _cfg("hot_empty", rows=(2000,) * 8, bag=("poisson", 3.0),
+                             index=("zipf", 1.1)), 8192),
     ("f16", MEDIUM, 16384),
     ("f32_d16", dataclasses.replace(DEMO3, B=32768), 32768),
 ])
