@@ -6,7 +6,8 @@ the metadata it writes must equal that of tbe_preprocess, and the stage timer
 must show that the hot rows were taken. Checked on weighted and unweighted
 bf16 (rows held widened to f32 in LDS), bf16 rows of 96 (four idle lanes per
 row slot), empty bags, unweighted f16 and f32 rows of 16, with more and with fewer long runs
-than the hot rows a table holds (255 rows of 256 bytes), with bags longer than one staged window
+than the hot rows a table holds (127 widened bf16 rows of 512 bytes at D = 128),
+with bags longer than one staged window
 of 128 lookups, and with the fused bounds check on planted bad indices (read
 as row 0, as the oracle is told)."""
 import dataclasses
