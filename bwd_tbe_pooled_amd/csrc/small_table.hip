@@ -154,7 +154,8 @@ __device__ __forceinline__ void count_tile(uint32_t (*H)[kHStride], int32_t* s_o
 // then packs its rows into hist and clears them for the next tile. The waves
 // share no rows, so after the first barrier they run without any.
 template <bool CHECK>
-__global__ __launch_bounds__(kThreads) void small_count_kernel(
+// Seven waves per SIMD (72 registers): more bags' loads in flight per CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(7))) void small_count_kernel(
     const int32_t* __restrict__ indices, const int32_t* __restrict__ offsets,
     uint8_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t B,
     const int32_t* __restrict__ trows, int32_t* __restrict__ err) {
