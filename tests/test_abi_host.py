@@ -36,6 +36,32 @@ def test_exports_every_declared_function():
     assert sorted(tbe.exported_symbols()) == declared
 
 
+def _header_constants():
+    """#define and enum constants of include/tbe.h: name -> integer value."""
+    src = open(os.path.join(ROOT, "include", "tbe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    vals = {}
+    for name, v in re.findall(r"#define\s+(TBE_[A-Z0-9_]+)\s+\(?(0x[0-9a-fA-F]+|\d+)u?\)?", src):
+        vals[name] = int(v, 0)
+    for name, v in re.findall(r"\b(TBE_[A-Z0-9_]+)\s*=\s*(0x[0-9a-fA-F]+|\d+)", src):
+        vals[name] = int(v, 0)
+    return vals
+
+
+def test_binding_stages_and_flags_match_the_header():
+    """The binding's stage names follow the header's TBE_STAGE_* order, and its
+    flag and path constants have the header's values."""
+    h = _header_constants()
+    stages = sorted((v, k) for k, v in h.items() if k.startswith("TBE_STAGE_"))
+    assert [v for v, _ in stages] == list(range(len(stages)))
+    assert h["TBE_NUM_STAGES"] == len(stages) == tbe.TBE_NUM_STAGES == len(tbe.STAGES)
+    assert [k[len("TBE_STAGE_"):].lower() for _, k in stages] == tbe.STAGES
+    for name in ("TBE_FLAG_CHECK", "TBE_FLAG_VALIDATE", "TBE_FLAG_FUSED_LONG",
+                 "TBE_FLAG_NO_HOT_ROWS", "TBE_FLAG_HOT_BACKWARD", "TBE_PATH_GENERIC",
+                 "TBE_PATH_SMALL_TABLE"):
+        assert getattr(tbe, name) == h[name], name
+
+
 def test_status_strings():
     for s in range(6):
         assert tbe.tbe_status_str(s) and tbe.tbe_status_str(s) != "unknown status"
