@@ -499,13 +499,21 @@ void fwd_pool_hot_kernel(
 #pragma unroll
       for (int u = 0; u < HU; ++u) {
         const int kk = k + u;
-        const bool ok = kk < h1;
-        const int q = ok ? kk : 0;
+        const int q = kk < h1 ? kk : 0;
         hslot[u] = s_hslot[wave][q];
-        if constexpr (WEIGHTED) hsc[u] = ok ? s_w[wave][kHotStage - 1 - q] : 0.f;
+        if constexpr (WEIGHTED) hsc[u] = s_w[wave][kHotStage - 1 - q];
       }
+      // read unconditionally (the padded lanes' select comes after), so the
+      // reads are not split into exec-masked ones
 #pragma unroll
-      for (int u = 0; u < HU; ++u) asm volatile("" ::"v"(hslot[u]));
+      for (int u = 0; u < HU; ++u) {
+        asm volatile("" ::"v"(hslot[u]));
+        if constexpr (WEIGHTED) asm volatile("" : "+v"(hsc[u]));
+      }
+      if constexpr (WEIGHTED) {
+#pragma unroll
+        for (int u = 0; u < HU; ++u) hsc[u] = k + u < h1 ? hsc[u] : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < HU; ++u) {
         const uint32_t sl = k + u < h1 ? hslot[u] : zero_slot;
