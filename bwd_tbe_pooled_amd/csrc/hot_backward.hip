@@ -9,21 +9,25 @@
 // gradient row is read once instead: with H[s][b] the summed per-sample
 // weight of hot slot s in bag b (the count when unweighted),
 //     G[s, :] = sum_b H[s][b] * grad[b, t-block]         ([256 x B] x [B x D])
-// is one dense contraction per table, tiled over 32-bag tiles and split over
-// the batch into segments (one workgroup each). The chunk path keeps the
-// other long runs; the apply then reduces each hot row's segment partials in
-// segment order (deterministic) and applies its Adagrad step.
+// is one dense contraction per table, tiled over 16-bag tiles and split over
+// the batch into segments (one workgroup of four waves each, two per CU). The
+// chunk path keeps the other long runs; the apply then reduces each hot row's
+// segment partials in segment order (deterministic) and applies its Adagrad
+// step.
 //
 // Per tile (its gradients, indices and weights loaded during the previous
 // tile's contraction):
-//  A. H is cleared and each gradient column's largest magnitude found;
-//  B. 16 threads per bag add each hot lookup's weight into H[slot][bag]
-//     (the slot through the LDS hash) with f64 atomics: H holds sums of a
-//     bag's few f32 weights, which are exact in f64, so the bits do not
-//     depend on the order of the adds; each gradient column is scaled by its
-//     power-of-two scale and split into f16 hi and lo (the B operands);
-//  C. wave w multiplies hot slots 32w..32w+31 by the tile on
-//     v_mfma_f32_32x32x16_f16, accumulating in f32.
+//  A. build: the cells of H the last tile set are cleared by the threads that
+//     set them; 16 threads per bag add each hot lookup's weight into
+//     H[slot][bag] (the slot through the LDS hash, two lookups probing
+//     together) with f32 LDS atomics: all adds to one cell come from its
+//     bag's 16 threads, which sit in one wave, in a fixed order of
+//     instructions and lanes, so the sums are the same from run to run; two
+//     threads per gradient column scale it by its power-of-two scale and
+//     split it into f16 hi and lo (the B operands); then the next tile's
+//     loads are issued;
+//  B. wave w multiplies hot slots 64w..64w+63 (two 32-row blocks) by the tile
+//     on v_mfma_f32_32x32x16_f16, accumulating in f32.
 //
 // Precision: each gradient column is scaled by a power of two set by its
 // first tile with a nonzero value (largest magnitude then in [2^4, 2^5)); x =
@@ -32,9 +36,11 @@
 // H_res = f16(H' - H_hi) with H' = H times its slot's power-of-two scale, set
 // by the slot's first nonzero tile so that its largest sum lands in [1, 2)).
 // That is about 2^-22 relative per term for every gradient down to 2^-18 of
-// its column's scale. A gradient that is not finite or whose scaled value
-// reaches 2^15 (1024 times the column's first largest), a weight sum 2^14
-// times its slot's first, or a count above 2048 flags the table
+// its column's scale. A tile whose largest gradient or weight sum reaches
+// 2^12 once scaled moves its column's or slot's scale back to the ranges
+// above (the accumulated values are multiplied by the exact power of two
+// between the two scales before the tile's products), so f16 never overflows. A gradient or
+// weight sum that is not finite, or a count above 2048, flags the table
 // (hot_flag[t]); the schedule then sends that table's hot runs through the
 // chunk path, which the apply reads for them instead.
 //
@@ -55,28 +61,31 @@ __device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kHbThreads = 512;             // 8 waves: wave w owns hot slots 32w..32w+31
+constexpr int kHbThreads = 256;             // 4 waves: wave w owns hot slots 64w..64w+63
 constexpr int kHbWaves = kHbThreads / kWave;
-static_assert(kHbWaves * 32 == kHotMaxK, "one 32-slot block per wave");
-constexpr int kHbBags = 32;                 // bags per tile: two 16-bag k-steps
+static_assert(kHbWaves * 64 == kHotMaxK, "two 32-slot blocks per wave");
+constexpr int kHbBags = 16;                 // bags per tile: one k-step of the 32x32x16 product
 static_assert(kHbBags * 16 == kHbThreads, "16 threads per bag");
-constexpr int kHbHStride = kHbBags + 2;     // doubles per H row: 16-byte aligned, banks rotate
+static_assert(kHbThreads == 2 * 128, "two threads per gradient column of 128");
+constexpr int kHbHStride = kHbBags + 4;     // floats per H row: 16-byte aligned, banks rotate
 constexpr int kHbAhead = 2;                 // lookups per thread loaded a tile ahead
 
 template <bool WEIGHTED, int NT>
-__global__ __launch_bounds__(kHbThreads) void bwd_hot_kernel(
+__global__ __launch_bounds__(kHbThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_hot_kernel(
     const float* __restrict__ grad, const int32_t* __restrict__ indices,
     const int32_t* __restrict__ offsets, const float* __restrict__ psw,
     const int32_t* __restrict__ hot_rows, const int32_t* __restrict__ tinfo,
     float* __restrict__ hot_parts, int32_t* __restrict__ hot_flag, int32_t T, int32_t B,
-    int64_t ld, int32_t seg_bags) {
+    int64_t ld, int32_t seg_bags, int64_t N) {
   constexpr int D = NT * 32;
   __shared__ __align__(16) int32_t s_key[kHotHash];
   __shared__ uint8_t s_slotof[kHotHash];
-  __shared__ __align__(16) double s_H[kHotMaxK][kHbHStride];      // weight sums, exact
-  __shared__ __align__(16) _Float16 s_gb[2][2][NT][kWave][8];     // [hi, lo][k-step][nt][lane][j]
-  __shared__ uint32_t s_cmax[D];  // per column: bits of the tile's largest finite |g|
+  __shared__ __align__(16) float s_H[kHotMaxK][kHbHStride];   // weight sums
+  __shared__ __align__(16) _Float16 s_gb[2][NT][kWave][8];    // [hi, lo][nt][lane][j]
   __shared__ int32_t s_gsc[D];    // per column: scale exponent, for the unscaling
+  __shared__ int32_t s_gdelta[D]; // per column: exponent change in this tile (rescaled columns)
+  __shared__ int32_t s_resc[2];   // per tile parity: some column was rescaled
   __shared__ int32_t s_nhot;
 
   const int32_t t = blockIdx.y;
@@ -91,35 +100,49 @@ __global__ __launch_bounds__(kHbThreads) void bwd_hot_kernel(
   const uint32_t Et = (uint32_t)tinfo[T + t];
 
   for (int q = threadIdx.x; q < kHotHash; q += kHbThreads) s_key[q] = -1;
-  for (int d = threadIdx.x; d < D; d += kHbThreads) s_cmax[d] = 0u;
-  if (threadIdx.x == 0) s_nhot = 0;
+  for (int q = threadIdx.x; q < kHotMaxK * kHbHStride / 4; q += kHbThreads)
+    reinterpret_cast<float4*>(&s_H[0][0])[q] = float4{0.f, 0.f, 0.f, 0.f};
+  if (threadIdx.x == 0) {
+    s_nhot = 0;
+    s_resc[0] = s_resc[1] = 0;
+  }
+  for (int d = threadIdx.x; d < D; d += kHbThreads) s_gdelta[d] = 0;
   __syncthreads();
   hot_hash_insert(s_key, s_slotof, hr, kHotMaxK);
   if (threadIdx.x < kHotMaxK && hr[threadIdx.x] >= 0) atomicMax(&s_nhot, (int)threadIdx.x + 1);
   __syncthreads();
   const int n_hot = s_nhot;  // slots 0..n_hot-1 are taken
   if (n_hot == 0) return;    // the whole workgroup: the table has no hot row
-  const bool mine = wave * 32 < n_hot;  // this wave owns a taken slot
+  const bool mine = wave * 64 < n_hot;  // this wave owns a taken slot
 
   // Lookups: 16 threads per bag of the tile, thread k of bag lb taking its
-  // lookups k, k+16, ... Gradients: thread (g, c) holds column c of the 8
-  // bags 8g..8g+7 (the j = 0..7 of one MFMA B operand lane).
+  // lookups k, k+16, ... Gradients: threads 2c and 2c+1 hold column c of bags
+  // 0..7 and 8..15 (lane kb*32 + c%32 of block c/32 of the B operand).
   const int lb = threadIdx.x >> 4, lk = threadIdx.x & 15;
-  const bool gthr = (int)threadIdx.x < 4 * D;
-  const int gc = threadIdx.x % D, gg = threadIdx.x / D;
-  const float* __restrict__ gcol = grad + (int64_t)t * D + gc;
-  int gsc = 0;        // scale of column gc (the same in the 4 threads of a column)
+  const int gc = threadIdx.x >> 1, gh = threadIdx.x & 1;
+  const bool gthr = gc < D;
+  int gsc = 0;        // scale of column gc (the same in both threads of a column)
   bool gset = false;
-  int hsc = 0;        // scale of hot slot 32*wave + i (weighted)
-  bool hset = false;
+  int hsc[2] = {0, 0};  // scales of hot slots 64*wave + 32*mb + i (weighted)
+  bool hset[2] = {false, false};
   bool bad = false;
 
-  float16v acc[NT];
+  float16v acc[2][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nt][r] = 0.f;
 
+  // Loads through buffer resources at 32-bit byte offsets (the launcher
+  // checks the bounds): a lookup past its bag or a gradient row past the
+  // tile reads as zero from an offset past the resource's end.
+  constexpr uint32_t kNoRow = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t ridx = make_rsrc(indices, (uint32_t)N * 4u);
+  const __amdgpu_buffer_rsrc_t rpsw = make_rsrc(WEIGHTED ? (const void*)psw : (const void*)indices, (uint32_t)N * 4u);
+  const uint32_t ldb = (uint32_t)ld * 4u;                              // bytes per gradient row
+  const uint32_t goff = (uint32_t)(gh * 8) * ldb + (uint32_t)gc * 4u;  // row 8*gh, column gc
   const int32_t* __restrict__ ofs = offsets + (int64_t)t * B;
   auto tile_nb = [&](int32_t b0) { return b_end - b0 < kHbBags ? b_end - b0 : kHbBags; };
   // Global loads run ahead: the next-but-one tile's offsets, and the next
@@ -140,156 +163,230 @@ __global__ __launch_bounds__(kHbThreads) void bwd_hot_kernel(
     }
   };
   auto load_data = [&](int32_t b0, const Off& o, Data& x) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x.g[j] = 0.f;
-#pragma unroll
-    for (int r = 0; r < kHbAhead; ++r) {
-      x.idx[r] = 0;
-      x.w[r] = 0.f;
-    }
-    if (b0 >= b_end) return;
-    const int nb = tile_nb(b0);
-    if (gthr) {
+    // gthr is the same in a whole wave (a wave's threads hold 32 columns)
+    if (b0 < b_end && gthr) {
+      const __amdgpu_buffer_rsrc_t rg =
+          make_rsrc(grad + (int64_t)b0 * ld + (int64_t)t * D, (uint32_t)tile_nb(b0) * ldb);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (gg * 8 + j < nb) x.g[j] = gcol[(int64_t)(b0 + gg * 8 + j) * ld];
+        x.g[j] = __builtin_bit_cast(float,
+                                    __builtin_amdgcn_raw_buffer_load_b32(rg, goff + j * ldb, 0, 0));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x.g[j] = 0.f;
     }
 #pragma unroll
     for (int r = 0; r < kHbAhead; ++r) {
       const int32_t q = o.q0 + lk + r * 16;
-      if (q < o.q1) {
-        x.idx[r] = indices[q];
-        if constexpr (WEIGHTED) x.w[r] = psw[q];
-      }
+      const uint32_t off = q < o.q1 ? (uint32_t)q * 4u : kNoRow;
+      x.idx[r] = __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(ridx, off, 0, 0));
+      if constexpr (WEIGHTED)
+        x.w[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rpsw, off, 0, 0));
+      else
+        x.w[r] = 1.f;
     }
   };
-  auto add_lookup = [&](int32_t idx, float w) {
-    const int slot = hot_hash_find(s_key, s_slotof, (uint32_t)idx < Et ? idx : 0);
-    // f64 sums of a bag's few f32 weights are exact, so the order in which
-    // the atomics land does not change the bits
-    if (slot >= 0) atomicAdd(&s_H[slot][lb], (double)w);
+  auto slot_of = [&](int32_t idx) {
+    return hot_hash_find(s_key, s_slotof, (uint32_t)idx < Et ? idx : 0);
   };
+
+  // H cells this thread added to in the last tile, cleared before the next
+  // tile's adds (by this same thread, or, after a bag longer than the
+  // lookups staged ahead, by its bag's 16 threads over the whole column)
+  int zslot[kHbAhead] = {-1, -1};
+  bool zcol = false;
+  bool gdirty = false;  // this thread wrote s_gdelta[gc] in the last tile
+  int par = 0;          // tile parity: which s_resc flag this tile sets
 
   Off o_cur, o_nxt;
   Data dat;
   load_off(b_begin, o_cur);
   load_data(b_begin, o_cur, dat);
   load_off(b_begin + kHbBags, o_nxt);
-  for (int32_t b0 = b_begin; b0 < b_end; b0 += kHbBags) {
-    // --- A: H cleared; the gradients' per-column maximum -----------------
-    for (int q = threadIdx.x; q < kHotMaxK * kHbHStride / 2; q += kHbThreads)
-      reinterpret_cast<double2*>(&s_H[0][0])[q] = double2{0.0, 0.0};
-    if (gthr) {
-      float m = 0.f;
+  for (int32_t b0 = b_begin; b0 < b_end; b0 += kHbBags, par ^= 1) {
+    // --- build: the last tile's H cells cleared, H[slot][bag] += weight of
+    //     each hot lookup, the gradients scaled and split into the B operands
+    if (zcol) {
+      for (int s = lk; s < kHotMaxK; s += 16) s_H[s][lb] = 0.f;
+    } else {
+#pragma unroll
+      for (int r = 0; r < kHbAhead; ++r)
+        if (zslot[r] >= 0) s_H[zslot[r]][lb] = 0.f;
+    }
+    if (threadIdx.x == 0) s_resc[par ^ 1] = 0;  // read in the last tile's contraction
+    if (gdirty) s_gdelta[gc] = 0;
+    gdirty = false;
+    // both staged lookups probe the hash together
+    static_assert(kHbAhead == 2, "two staged lookups per thread");
+    {
+      const bool v0 = o_cur.q0 + lk < o_cur.q1, v1 = o_cur.q0 + lk + 16 < o_cur.q1;
+      hot_hash_find2(s_key, s_slotof, (uint32_t)dat.idx[0] < Et ? dat.idx[0] : 0, v0,
+                     (uint32_t)dat.idx[1] < Et ? dat.idx[1] : 0, v1, zslot[0], zslot[1]);
+    }
+    {
+      // the largest |g| as the largest bit pattern (finite values only)
+      uint32_t mbits = 0u;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float a = __builtin_fabsf(dat.g[j]);
-        if (a <= 3.402823466e38f) m = a > m ? a : m;
-        else bad = true;  // Inf or NaN
+        const uint32_t a = __float_as_uint(dat.g[j]) & 0x7fffffffu;
+        mbits = a > mbits ? a : mbits;
       }
-      if (m > 0.f) atomicMax(&s_cmax[gc], __float_as_uint(m));
-    }
-    __syncthreads();
-
-    // --- B: H[slot][bag] += weight of each hot lookup; the gradients scaled
-    //        and split into the B operands ----------------------------------
-#pragma unroll
-    for (int r = 0; r < kHbAhead; ++r)
-      if (o_cur.q0 + lk + r * 16 < o_cur.q1) add_lookup(dat.idx[r], WEIGHTED ? dat.w[r] : 1.f);
-    for (int32_t q = o_cur.q0 + lk + kHbAhead * 16; q < o_cur.q1; q += 16)  // long bags
-      add_lookup(indices[q], WEIGHTED ? psw[q] : 1.f);
-    if (gthr) {
-      const uint32_t mb = s_cmax[gc];
-      if (mb != 0u) {
-        const int e = __builtin_amdgcn_frexp_expf(__uint_as_float(mb));  // max in [2^(e-1), 2^e)
+      mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 1));  // the column's other eight bags
+      bad |= mbits >= 0x7f800000u;                             // Inf or NaN
+      if (mbits != 0u && mbits < 0x7f800000u) {
+        const int e = __builtin_amdgcn_frexp_expf(__uint_as_float(mbits));  // max in [2^(e-1), 2^e)
         if (!gset) {
-          gsc = 5 - e;
+          gsc = 5 - e;  // the column's first nonzero tile: largest in [2^4, 2^5)
           gset = true;
-        } else if (e + gsc > 15) {
-          bad = true;  // 1024 times the column's first largest: beyond f16 after scaling
+        } else if (e + gsc > 12) {
+          // a value 2^12 above the scale: the column is rescaled (its
+          // accumulators too, before this tile's products)
+          if (gh == 0) {
+            s_gdelta[gc] = (5 - e) - gsc;
+            s_resc[par] = 1;
+            gdirty = true;
+          }
+          gsc = 5 - e;
         }
       }
-      half8 h, l;
+      if (gthr) {
+        half8 h, l;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = __builtin_ldexpf(dat.g[j], gsc);
-        h[j] = (_Float16)x;
-        l[j] = (_Float16)((x - (float)h[j]) * 2048.f);
+        for (int j = 0; j < 8; ++j) {
+          const float x = __builtin_ldexpf(dat.g[j], gsc);
+          h[j] = (_Float16)x;
+          l[j] = (_Float16)((x - (float)h[j]) * 2048.f);
+        }
+        // B[kb*8 + j][i] of block nt: bag 8*gh + j, column gc = nt*32 + i
+        const int bl = gh * 32 + (gc & 31);
+        *reinterpret_cast<half8*>(&s_gb[0][gc >> 5][bl][0]) = h;
+        *reinterpret_cast<half8*>(&s_gb[1][gc >> 5][bl][0]) = l;
       }
-      // B[kb*8 + j][i] of k-step gg/2: bag 8*gg + j, column gc = nt*32 + i
-      const int bl = (gg & 1) * 32 + (gc & 31);
-      *reinterpret_cast<half8*>(&s_gb[0][gg >> 1][gc >> 5][bl][0]) = h;
-      *reinterpret_cast<half8*>(&s_gb[1][gg >> 1][gc >> 5][bl][0]) = l;
     }
-    __syncthreads();
-
-    // the next tile's loads, in flight during the contraction
+    // A cell's adds all come from the 16 threads of its bag, which are in one
+    // wave, in a fixed order of instructions and lanes, so the f32 sums do not
+    // change from run to run.
+#pragma unroll
+    for (int r = 0; r < kHbAhead; ++r) {
+      if (zslot[r] >= 0) {
+        if constexpr (WEIGHTED) bad |= !(__builtin_fabsf(dat.w[r]) <= 3.402823466e38f);
+        atomicAdd(&s_H[zslot[r]][lb], dat.w[r]);
+      }
+    }
+    zcol = o_cur.q1 - o_cur.q0 > kHbAhead * 16;
+    for (int32_t q = o_cur.q0 + lk + kHbAhead * 16; q < o_cur.q1; q += 16) {  // long bags
+      const int sl = slot_of(indices[q]);
+      if (sl >= 0) {
+        const float w = WEIGHTED ? psw[q] : 1.f;
+        bad |= !(__builtin_fabsf(w) <= 3.402823466e38f);
+        atomicAdd(&s_H[sl][lb], w);
+      }
+    }
+    // the next tile's loads, issued as soon as this tile's registers are
+    // consumed: in flight during the barrier and the contraction
     o_cur = o_nxt;
     load_data(b0 + kHbBags, o_cur, dat);
     load_off(b0 + 2 * kHbBags, o_nxt);
+    __syncthreads();
 
-    // --- C: the contraction -------------------------------------------------
+    // --- the contraction ----------------------------------------------------
     if (mine) {
-      const double* hrow = &s_H[wave * 32 + i][0];
       float hx[2][8];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int mb = 0; mb < 2; ++mb) {
+        const float* hrow = &s_H[wave * 64 + mb * 32 + i][kb * 8];
+        const float4 v0 = *reinterpret_cast<const float4*>(hrow);
+        const float4 v1 = *reinterpret_cast<const float4*>(hrow + 4);
+        hx[mb][0] = v0.x; hx[mb][1] = v0.y; hx[mb][2] = v0.z; hx[mb][3] = v0.w;
+        hx[mb][4] = v1.x; hx[mb][5] = v1.y; hx[mb][6] = v1.z; hx[mb][7] = v1.w;
+      }
+      // columns rescaled in this tile's build (workgroup-uniform flag)
+      if (s_resc[par]) {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const double2 v = *reinterpret_cast<const double2*>(hrow + ks * 16 + kb * 8 + j);
-          hx[ks][j] = (float)v.x;
-          hx[ks][j + 1] = (float)v.y;
-        }
-      if constexpr (WEIGHTED) {
-        float hm = 0.f;
+        for (int nt = 0; nt < NT; ++nt) {
+          const int dg = s_gdelta[nt * 32 + i];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) hm = fmaxf(hm, __builtin_fabsf(hx[ks][j]));
-        hm = fmaxf(hm, __shfl_xor(hm, 32));
-        if (hm > 0.f) {
-          const int e = __builtin_amdgcn_frexp_expf(hm);
-          if (!(hm <= 3.402823466e38f)) bad = true;
-          else if (!hset) {
-            hsc = 1 - e;  // the slot's first nonzero tile: largest sum in [1, 2)
-            hset = true;
-          } else if (e + hsc > 15) {
-            bad = true;
-          }
+            for (int r = 0; r < 16; ++r) acc[mb][nt][r] = __builtin_ldexpf(acc[mb][nt][r], dg);
         }
       }
+      half8 a_hi[2], a_hs[2], a_res[2];
+      int dsc[2] = {0, 0};  // exponent change of this lane's slot in block mb
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        half8 a_hi, a_hs, a_res;
+      for (int mb = 0; mb < 2; ++mb) {
+        if constexpr (WEIGHTED) {
+          float hm = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) hm = fmaxf(hm, __builtin_fabsf(hx[mb][j]));
+          hm = fmaxf(hm, __shfl_xor(hm, 32));
+          if (hm > 0.f) {
+            const int e = __builtin_amdgcn_frexp_expf(hm);
+            if (!(hm <= 3.402823466e38f)) bad = true;
+            else if (!hset[mb]) {
+              hsc[mb] = 1 - e;  // the slot's first nonzero tile: largest sum in [1, 2)
+              hset[mb] = true;
+            } else if (e + hsc[mb] > 12) {  // 2^12 above the scale: the slot is rescaled
+              dsc[mb] = (1 - e) - hsc[mb];
+              hsc[mb] = 1 - e;
+            }
+          }
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if constexpr (WEIGHTED) {
-            const float x = __builtin_ldexpf(hx[ks][j], hsc);
+            const float x = __builtin_ldexpf(hx[mb][j], hsc[mb]);
             const _Float16 h = (_Float16)x;
-            a_hi[j] = h;
-            a_res[j] = (_Float16)(x - (float)h);
+            a_hi[mb][j] = h;
+            a_res[mb][j] = (_Float16)(x - (float)h);
           } else {
-            bad |= hx[ks][j] > 2048.f;  // counts are exact in f16 up to 2048
-            a_hi[j] = (_Float16)hx[ks][j];
+            bad |= hx[mb][j] > 2048.f;  // counts are exact in f16 up to 2048
+            a_hi[mb][j] = (_Float16)hx[mb][j];
           }
-          a_hs[j] = a_hi[j] * (_Float16)(1.f / 2048.f);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const half8 b_hi = *reinterpret_cast<const half8*>(&s_gb[0][ks][nt][lane][0]);
-          const half8 b_lo = *reinterpret_cast<const half8*>(&s_gb[1][ks][nt][lane][0]);
-          acc[nt] = mfma32(a_hi, b_hi, acc[nt]);
-          acc[nt] = mfma32(a_hs, b_lo, acc[nt]);
-          if constexpr (WEIGHTED) acc[nt] = mfma32(a_res, b_hi, acc[nt]);
+          a_hs[mb][j] = a_hi[mb][j] * (_Float16)(1.f / 2048.f);
         }
       }
+      if constexpr (WEIGHTED) {
+        // a rescaled slot's accumulator rows follow its new scale (lane `row`
+        // holds the change of slot row; a wave-uniform test, rarely taken)
+        if (__ballot(dsc[0] != 0 || dsc[1] != 0) != 0) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int d = __shfl(dsc[mb], 8 * (r / 4) + 4 * kb + (r % 4));
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) acc[mb][nt][r] = __builtin_ldexpf(acc[mb][nt][r], d);
+            }
+        }
+      }
+      half8 b_hi[NT], b_lo[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        b_hi[nt] = *reinterpret_cast<const half8*>(&s_gb[0][nt][lane][0]);
+        b_lo[nt] = *reinterpret_cast<const half8*>(&s_gb[1][nt][lane][0]);
+      }
+      // products in rounds over the eight independent accumulators
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mb][nt] = mfma32(a_hi[mb], b_hi[nt], acc[mb][nt]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mb][nt] = mfma32(a_hs[mb], b_lo[nt], acc[mb][nt]);
+      if constexpr (WEIGHTED) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[mb][nt] = mfma32(a_res[mb], b_hi[nt], acc[mb][nt]);
+      }
     }
-    for (int d = threadIdx.x; d < D; d += kHbThreads) s_cmax[d] = 0u;  // read in B, done
-    __syncthreads();
+    __syncthreads();  // H and the B operands read: the next tile may overwrite them
   }
 
   // Column scales to LDS, then the unscaled partials of this segment.
-  if (gthr && gg == 0) s_gsc[gc] = gsc;
+  if (gthr && gh == 0) s_gsc[gc] = gsc;
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
   if (any_bad) {
     if (threadIdx.x == 0) atomicOr(&hot_flag[t], 1);
@@ -297,35 +394,39 @@ __global__ __launch_bounds__(kHbThreads) void bwd_hot_kernel(
   }
   if (!mine) return;
   float* __restrict__ out =
-      hot_parts + ((int64_t)t * gridDim.x + seg) * kHotMaxK * D + (int64_t)wave * 32 * D;
+      hot_parts + ((int64_t)t * gridDim.x + seg) * kHotMaxK * D + (int64_t)wave * 64 * D;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r / 4) + 4 * kb + (r % 4);   // slot within this wave's block
-    const int rs = WEIGHTED ? __shfl(hsc, row) : 0;   // that slot's scale (lane row holds it)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int d = nt * 32 + i;
-      out[(int64_t)row * D + d] = __builtin_ldexpf(acc[nt][r], -(rs + s_gsc[d]));
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r / 4) + 4 * kb + (r % 4);      // slot within this 32-slot block
+      const int rs = WEIGHTED ? __shfl(hsc[mb], row) : 0;  // that slot's scale (lane row holds it)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int d = nt * 32 + i;
+        out[(int64_t)(mb * 32 + row) * D + d] = __builtin_ldexpf(acc[mb][nt][r], -(rs + s_gsc[d]));
+      }
     }
-  }
 }
 
 }  // namespace
 
 // Opt-in (TBE_FLAG_HOT_BACKWARD): at T=32, B=131072, D=128 bf16 on one
-// MI355X the contraction takes 2.16 ms and the remaining long runs' chunks
-// 0.85 ms, against 2.05 ms for the chunk path alone.
+// MI355X the plan and the contraction take 1.58 ms and the remaining long
+// runs' chunks 0.44 ms, against 2.06 ms for the chunk path alone.
 bool hot_backward_eligible(const Problem& p) {
+  // 32-bit byte offsets: the lookups below 2^29, a 16-row gradient tile below 2^31 bytes
   return p.hot_bwd_asked && !p.no_hot && p.path == TBE_PATH_GENERIC && p.wdtype != TBE_F32 &&
-         p.D % 32 == 0 && p.D <= 128 && p.B >= 1 && p.cap_long > 0;
+         p.D % 32 == 0 && p.D <= 128 && p.B >= 1 && p.cap_long > 0 && p.N < (int64_t(1) << 29) &&
+         p.ld < (int64_t(1) << 25);
 }
 
 int32_t hot_backward_segments(const Problem& p) {
-  // about one workgroup per CU over all tables, and at least 16 tiles (512
+  // about two workgroups per CU over all tables, and at least 32 tiles (512
   // bags) per segment, so that small batches keep few partials
   const int64_t tiles = ((int64_t)p.B + kHbBags - 1) / kHbBags;
-  int64_t nseg = (256 + p.T - 1) / p.T;
-  const int64_t by_tiles = (tiles + 15) / 16;
+  int64_t nseg = (kHotBwdWorkgroups + p.T - 1) / p.T;
+  const int64_t by_tiles = (tiles + 31) / 32;
   if (nseg > by_tiles) nseg = by_tiles;
   return (int32_t)(nseg < 1 ? 1 : nseg);
 }
@@ -340,7 +441,7 @@ hipError_t launch_bwd_hot(const Problem& p, const float* grad, const int32_t* in
   const dim3 grid((unsigned)nseg, (unsigned)p.T);
 #define TBE_HOT(WGT, NTT)                                                                   \
   hipLaunchKernelGGL((bwd_hot_kernel<WGT, NTT>), grid, dim3(kHbThreads), 0, s, grad, indices, \
-                     offsets, psw, hot_rows, tinfo, hot_parts, hot_flag, p.T, p.B, p.ld, seg_bags)
+                     offsets, psw, hot_rows, tinfo, hot_parts, hot_flag, p.T, p.B, p.ld, seg_bags, p.N)
 #define TBE_HOT_NT(WGT)                       \
   switch (p.D / 32) {                         \
     case 1: TBE_HOT(WGT, 1); break;           \

@@ -55,4 +55,45 @@ __device__ __forceinline__ int hot_hash_find(const int32_t* s_key, const uint8_t
   }
 }
 
+// Slots of two rows (-1: not hot, or `go` false), their probes interleaved
+// so that both searches wait on one LDS round trip per step.
+__device__ __forceinline__ void hot_hash_find2(const int32_t* s_key, const uint8_t* s_slotof,
+                                               int32_t r0, bool go0, int32_t r1, bool go1,
+                                               int& slot0, int& slot1) {
+  uint32_t b0 = hot_bucket(r0), b1 = hot_bucket(r1);
+  int32_t f0 = -1, f1 = -1;  // entries that hold the rows
+  auto match = [](const int4& q, int32_t x) {
+    return q.x == x ? 0 : q.y == x ? 1 : q.z == x ? 2 : q.w == x ? 3 : -1;
+  };
+  {  // the first probe of both, without branches: most searches end there
+    const int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
+    const int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
+    const int j0 = match(q0, r0), j1 = match(q1, r1);
+    f0 = go0 && j0 >= 0 ? (int32_t)(b0 * 4 + j0) : -1;
+    f1 = go1 && j1 >= 0 ? (int32_t)(b1 * 4 + j1) : -1;
+    go0 = go0 && j0 < 0 && q0.w >= 0;  // entries fill in order: an empty one ends the search
+    go1 = go1 && j1 < 0 && q1.w >= 0;
+  }
+  while (go0 || go1) {  // a full bucket: the search goes on in the next
+    if (go0) {
+      b0 = (b0 + 1) & (kHotBuckets - 1);
+      const int4 q = reinterpret_cast<const int4*>(s_key)[b0];
+      const int j = match(q, r0);
+      if (j >= 0) f0 = (int32_t)(b0 * 4 + j);
+      go0 = j < 0 && q.w >= 0;
+    }
+    if (go1) {
+      b1 = (b1 + 1) & (kHotBuckets - 1);
+      const int4 q = reinterpret_cast<const int4*>(s_key)[b1];
+      const int j = match(q, r1);
+      if (j >= 0) f1 = (int32_t)(b1 * 4 + j);
+      go1 = j < 0 && q.w >= 0;
+    }
+  }
+  const int32_t s0 = s_slotof[f0 < 0 ? 0 : f0];
+  const int32_t s1 = s_slotof[f1 < 0 ? 0 : f1];
+  slot0 = f0 < 0 ? -1 : s0;
+  slot1 = f1 < 0 ? -1 : s1;
+}
+
 }  // namespace tbe

@@ -109,11 +109,11 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
                                         reads every gradient row once (page
                                         1, the compensated f16 hi/lo
                                         contraction; f16/bf16 weights, D a
-                                        multiple of 32 up to 128), the other
-                                        long runs on the chunk path.
-                                        Opt-in: slower than the chunk path
-                                        alone at the Zipf-skewed batch on
-                                        gfx950 */
+                                        multiple of 32 up to 128, fewer than
+                                        2^29 lookups), the other long runs
+                                        on the chunk path. Opt-in: about as
+                                        fast as the chunk path alone at the
+                                        Zipf-skewed batch on gfx950 */
 
 /* Bits OR-ed into *tbe_desc.error_flags under TBE_FLAG_CHECK. */
 #define TBE_ERROR_INDEX 0x1u   /* some index was outside its table */

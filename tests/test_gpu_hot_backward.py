@@ -7,8 +7,9 @@ and 1 ulp of the rounded oracle, state within 1e-5), untouched rows stay
 bitwise unchanged, and the stage timer shows the contraction ran. Covered:
 weighted bf16 and unweighted f16, rows of 32, 64, 96 and 128, more long runs
 than the 256 hot slots, runs tied at the cut (no hot row), a ragged last
-segment, and the two ways back to the chunk path: a gradient far above its
-column's scale and a tile with more lookups than the kernel stages."""
+segment, bags longer than the lookups staged ahead, and scales moved by later
+tiles: one gradient far above its column's scale, and every segment's first
+tile 1e-6 times smaller than the rest."""
 import dataclasses
 
 import numpy as np
@@ -73,9 +74,9 @@ def test_large_skewed_reduced_batch():
 
 
 def test_ragged_last_segment():
-    """64 tables of 2080 bags (65 tiles of 32): 4 segments of 17 tiles per
-    table, the last one 14 tiles long."""
-    cfg = Config("hot_ragged_seg", T=64, B=2080, D=64, rows=(200,) * 64, dtype="bf16",
+    """64 tables of 2088 bags (131 tiles of 16, the last one of 8 bags): 5
+    segments of 27 tiles per table, the last one 23 tiles long."""
+    cfg = Config("hot_ragged_seg", T=64, B=2088, D=64, rows=(200,) * 64, dtype="bf16",
                  bag=("fixed", 20), index=("zipf", 1.2), weighted=True,
                  preprocess_in_forward=True, seed=85)
     _check(cfg, make_batch(cfg), S=16, C=16)
@@ -110,7 +111,8 @@ def test_hot_runs_above_a_tie():
     _check(cfg, batch, S=16, C=16)
 
 
-def test_gradient_far_above_its_column_scale_falls_back():
+def test_gradient_far_above_its_column_scale():
+    """One gradient 1e8 times its column's first tile: the column is rescaled."""
     batch = make_batch(LARGE, B=2048)
     cfg = batch.cfg
     grad = batch.grad.copy()
@@ -119,8 +121,28 @@ def test_gradient_far_above_its_column_scale_falls_back():
     _check(cfg, batch, label="large skewed, one gradient of 1e8")
 
 
-def test_tiles_with_more_lookups_than_staged_fall_back():
-    """Bags of 150 to 250 lookups: a 32-bag tile holds more than 4096."""
+def test_small_first_tiles_rescale_columns_and_slots():
+    """Gradients and weights of the first 16 bags of every 512 scaled by 1e-6:
+    each segment's first tile sets scales 2^20 too small, and the later
+    tiles move every column's and most hot slots' scales (and their
+    accumulated values)."""
+    batch = make_batch(LARGE, B=2048)
+    cfg = batch.cfg
+    grad = batch.grad.copy()
+    psw = batch.psw.copy()
+    small = (np.arange(cfg.B) % 512) < 16
+    grad[small] *= np.float32(1e-6)
+    for t in range(cfg.T):
+        for b in np.nonzero(small)[0]:
+            i = t * cfg.B + b
+            psw[batch.offsets[i]:batch.offsets[i + 1]] *= np.float32(1e-6)
+    batch = dataclasses.replace(batch, grad=grad, psw=psw)
+    _check(cfg, batch, label="large skewed, small first tiles")
+
+
+def test_bags_longer_than_staged():
+    """Bags of 150 to 250 lookups: most of each bag's lookups are loaded in
+    the build, and its H column is cleared whole afterwards."""
     cfg = Config("hot_long_bags", T=2, B=256, D=128, rows=(300, 300), dtype="bf16",
                  bag=("uniform", 150, 250), index=("zipf", 1.1), weighted=True,
                  preprocess_in_forward=True, seed=91)
