@@ -45,6 +45,10 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+PEAK_F16_TFLOPS = 2500.0        # MI355X dense f16 matrix-core peak, 2.5 PFLOP/s
+HOT_K = 256                     # hot rows per table in the backward's contraction
+HOT_WGS = 512                   # workgroups the contraction aims at over all tables
+HOT_TILE = 16                   # bags per tile of the contraction
 GATE = 0.6                      # target fraction of the HBM roofline
 FLUSH_BYTES = 1 << 30           # scratch written before each flushed step
 
@@ -90,12 +94,31 @@ def compulsory_bytes(cfg, st, weighted):
     D, nb, N, U = cfg.D, cfg.T * cfg.B, st["N"], st["U"]
     psw = 4 if weighted else 0
     fwd = U * D * w + N * (4 + psw) + 4 * (nb + 1) + 4 * nb * D
+    hot = st.get("hot_runs", 0) > 0
+    # with the hot rows' contraction, the chunk kernel takes only the other long runs
+    chunk_lookups = st["long_lookups"] - st.get("hot_lookups", 0)
+    chunks = st.get("chunk_chunks", st["n_chunks"]) if hot else st["n_chunks"]
+    bags_chunk = st.get("bags_chunk", st["bags_long"]) if hot else st["bags_long"]
+    hot_parts = 4 * cfg.T * st.get("hot_nseg", 0) * HOT_K * D if hot else 0
     bwd = (st["bags_touched"] * 4 * D + N * (4 + psw) + U * (2 * D * w + 8 + 8 + 4)
-           + 2 * st["n_chunks"] * D * a)
-    long_k = st["bags_long"] * 4 * D + st["long_lookups"] * (4 + psw) + st["n_chunks"] * (D * a + 12)
+           + 2 * chunks * D * a + 2 * hot_parts)
+    long_k = bags_chunk * 4 * D + chunk_lookups * (4 + psw) + chunks * (D * a + 12)
     short_k = (st["bags_short"] * 4 * D + (N - st["long_lookups"]) * (4 + psw)
                + st["n_short"] * (2 * D * w + 8 + 12))
-    return dict(fwd=fwd, bwd=bwd, fwd_pool=fwd, bwd_long=long_k, bwd_short=short_k)
+    out = dict(fwd=fwd, bwd=bwd, fwd_pool=fwd, bwd_long=long_k, bwd_short=short_k)
+    if hot:
+        # every gradient row and every lookup's index and weight once, the
+        # offsets, the segment partials written
+        out["bwd_hot"] = nb * 4 * D + N * (4 + psw) + 4 * (nb + 1) + hot_parts
+    return out
+
+
+def hot_flops(cfg, st, weighted):
+    """Matrix-core flops of the hot rows' contraction: per table and 16-bag
+    tile, 256 slots x 16 bags x D columns, two products (hi, lo), three when
+    weighted (the weight sums' residual too)."""
+    tiles = -(-cfg.B // HOT_TILE)
+    return 2 * cfg.T * tiles * HOT_TILE * HOT_K * cfg.D * (3 if weighted else 2)
 
 
 def small_table_bytes(cfg, N):
@@ -116,10 +139,11 @@ def small_table_bytes(cfg, N):
                 bwd_flop=2 * 2 * T * B * E * D)          # hi and lo products
 
 
-def run_structure(torch, meta, cfg, N, S=256):
+def run_structure(torch, meta, cfg, N, S=256, C=256, hot=False):
     """Counts of the transpose's output, read back from the metadata the
     library wrote: runs, routing, long-run lookups, and how many distinct
-    upstream-gradient rows the short and the long runs read."""
+    upstream-gradient rows the short and the long runs read; with the hot
+    rows' contraction, which long runs it takes and what is left to chunks."""
     counts = meta["counts"][:4].cpu().numpy()
     U, n_short, n_long, n_chunks = (int(x) for x in counts)
     nb = cfg.T * cfg.B
@@ -136,6 +160,35 @@ def run_structure(torch, meta, cfg, N, S=256):
     st.update(long_lookups=int(is_long.sum().item()), bags_long=int(bl.sum().item()),
               bags_short=int(bs.sum().item()), bags_touched=int((bl | bs).sum().item()),
               max_sl=int(sl.max().item()))
+    if hot:
+        # the hot-row plan's choice: per table, the long runs of the longest
+        # lengths while at most HOT_K of them reach that length (a tie at the
+        # cut leaves the tied runs out)
+        keys = meta["run_keys"][:U].long()
+        toff = torch.tensor(np.concatenate([[0], np.cumsum(cfg.rows)]), device=keys.device)
+        tab = torch.searchsorted(toff, keys, right=True) - 1
+        hot_run = torch.zeros(U, dtype=torch.bool, device=keys.device)
+        lr = torch.nonzero(sl >= S).flatten()
+        for t in range(cfg.T):
+            mine = lr[tab[lr] == t]
+            if mine.numel() == 0:
+                continue
+            lens = sl[mine]
+            if mine.numel() <= HOT_K:
+                hot_run[mine] = True
+                continue
+            srt = torch.sort(lens, descending=True).values
+            v = int(srt[HOT_K].item()) + 1      # the (K+1)-th longest is left out, with its ties
+            hot_run[mine[lens >= v]] = True
+        is_hot = torch.repeat_interleave(hot_run, sl)
+        chunk_run = (sl >= S) & ~hot_run
+        bc = torch.bincount(sb[is_long & ~is_hot], minlength=nb) > 0
+        tiles = -(-cfg.B // HOT_TILE)
+        st.update(hot_runs=int(hot_run.sum().item()), hot_lookups=int(is_hot.sum().item()),
+                  chunk_chunks=int(((sl[chunk_run] + C - 1) // C).sum().item()),
+                  bags_chunk=int(bc.sum().item()),
+                  hot_nseg=max(1, min(-(-HOT_WGS // cfg.T), -(-tiles // 32))))
+        del is_hot, bc
     del is_long, sb, bl, bs
     return st
 
@@ -281,13 +334,13 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
     m = init_state(cfg, dev)
     out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    flags = 0
+    # the long-run path applies to every generic workload (the library takes
+    # the hot rows' contraction only where it is eligible); the rest of the
+    # diagnostics only to the headline
+    flags = {"two_launch": 0, "fused": tbe.TBE_FLAG_FUSED_LONG,
+             "hot": tbe.TBE_FLAG_HOT_BACKWARD}[args.long]
     if headline:
-        flags = {"none": 0, "fused": tbe.TBE_FLAG_CHECK, "validate": tbe.TBE_FLAG_VALIDATE}[args.check]
-        if args.long == "fused":
-            flags |= tbe.TBE_FLAG_FUSED_LONG
-        elif args.long == "hot":
-            flags |= tbe.TBE_FLAG_HOT_BACKWARD
+        flags |= {"none": 0, "fused": tbe.TBE_FLAG_CHECK, "validate": tbe.TBE_FLAG_VALIDATE}[args.check]
         if args.hot_rows == "off":
             flags |= tbe.TBE_FLAG_NO_HOT_ROWS
     desc = tbe.Desc(cfg.T, cfg.D, cfg.B, cfg.rows, cfg.dtype, flags=flags, error_flags=err)
@@ -325,9 +378,9 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
         tbe.tbe_preprocess(desc, idx, off, psw, meta,
                            tbe.workspace(desc, N, weighted, tbe.TBE_OP_PREPROCESS))
     torch.cuda.synchronize()
-    st = run_structure(torch, meta, cfg, N)
     steps = args.steps if headline else max(3, args.steps // 2)
     wall_ms, avg, stages, flushed = time_steps(torch, tbe, desc, step, steps, scratch)
+    st = run_structure(torch, meta, cfg, N, hot="bwd_hot" in stages)
     g_ms = None
     if headline and not wide and args.check != "validate":
         g_ms = graph_ms(torch, step, steps)
@@ -366,6 +419,9 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
     gathered = {"fwd_pool": N * cfg.D * (2 if cfg.dtype != "f32" else 4),
                 "bwd_long": st["long_lookups"] * 4 * cfg.D,
                 "bwd_short": (N - st["long_lookups"]) * 4 * cfg.D}
+    if st.get("hot_runs", 0):
+        gathered["bwd_long"] = (st["long_lookups"] - st["hot_lookups"]) * 4 * cfg.D
+        gathered["bwd_short"] = (N - st["long_lookups"]) * 4 * cfg.D
     for k in ("fwd_pool", "bwd_short", "bwd_long"):
         ms = avg[k]
         if ms <= 0:
@@ -374,6 +430,17 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
         kernels[k] = {"ms": round(ms, 4), "compulsory_bytes": comp[k], "GBps": gb,
                       "frac_of_peak": fr, "gathered_bytes": gathered[k],
                       "gathered_GBps": round(gathered[k] / (ms * 1e6), 1)}
+    if avg.get("bwd_hot", 0.0) > 0 and "bwd_hot" in comp:
+        # the stage holds the hot-row plan (about 0.03 ms) and the contraction
+        ms = avg["bwd_hot"]
+        fl = hot_flops(cfg, st, weighted)
+        gb, fr = frac(comp["bwd_hot"], ms)
+        tf = fl / (ms * 1e9)
+        kernels["bwd_hot"] = {"ms": round(ms, 4), "bound": "mfma", "flops": fl,
+                              "TFLOPs": round(tf, 1), "peak_TFLOPs": PEAK_F16_TFLOPS,
+                              "frac_of_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                              "compulsory_bytes": comp["bwd_hot"], "GBps": gb,
+                              "frac_of_hbm_peak": fr}
     res["kernels"] = kernels
     del W, m, out, grad, idx, off, psw, ws_f, ws_b, meta
     if wide:
@@ -560,12 +627,12 @@ def main():
     ap.add_argument("--hot-rows", choices=["on", "off"], default="on",
                     help="the forward after the transpose reads each table's hottest rows from "
                          "LDS (on, default) or gathers every row (off: TBE_FLAG_NO_HOT_ROWS)")
-    ap.add_argument("--long", choices=["two_launch", "fused", "hot"], default="two_launch",
-                    help="long runs: chunk partials then a separate apply (default), one "
-                         "launch whose last chunk per run reduces and applies (fused: "
-                         "TBE_FLAG_FUSED_LONG), or the hottest rows' gradients as one "
-                         "matrix-core contraction and the rest as chunks (hot: "
-                         "TBE_FLAG_HOT_BACKWARD)")
+    ap.add_argument("--long", choices=["two_launch", "fused", "hot"], default="hot",
+                    help="long runs: each table's hottest rows' gradients as one matrix-core "
+                         "contraction and the rest as chunk partials then a separate apply "
+                         "(hot, default: TBE_FLAG_HOT_BACKWARD), every long run as chunks "
+                         "(two_launch: the library's default), or one launch whose last "
+                         "chunk per run reduces and applies (fused: TBE_FLAG_FUSED_LONG)")
     ap.add_argument("--rows", choices=["zipf", "uniform"], default="zipf",
                     help="row distribution of the large workload: Zipf-Mandelbrot (default) or "
                          "uniform (a diagnostic without reuse)")
@@ -595,7 +662,7 @@ def main():
 
     dev = torch.device("cuda")
     scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-    diagnostic = (args.check != "none" or args.preprocess != "forward" or args.long != "two_launch"
+    diagnostic = (args.check != "none" or args.preprocess != "forward" or args.long != "hot"
                   or args.rows != "zipf" or args.index != "int32" or args.tables != 32
                   or args.hot_rows != "on")
 
@@ -615,7 +682,7 @@ def main():
         log("generating the headline batch")
         batch = make_batch(cfg)
         head = measure_generic(torch, tbe, cfg, batch, args, scratch, headline=True)
-        dom_candidates = ("fwd_pool", "bwd_short", "bwd_long")
+        dom_candidates = ("fwd_pool", "bwd_short", "bwd_long", "bwd_hot")
         metric = "TBE fwd+bwd(Adagrad) ms and achieved HBM GB/s % peak, T=32 B=128K D=128"
         dtype = "bf16"
     log(f"headline {head['ms_per_step']} ms per step")
@@ -638,10 +705,18 @@ def main():
     name_for_counters = cfg.name if not diagnostic else None
     rec = counters_for(name_for_counters, dom) if name_for_counters else None
     traffic = rec["hbm_bytes_per_launch"] if rec else None
-    roofline = {"kernel": dom, "bound": "hbm", "bytes_model": "compulsory",
-                "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": dk["frac_of_peak"], "traffic": traffic,
-                "bytes_per_launch": dk["compulsory_bytes"], "avg_launch_ms": dk["ms"]}
+    if dk.get("bound") == "mfma":
+        # a dense contraction: its flops against the f16 matrix-core peak
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": dk["TFLOPs"],
+                    "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": dk["frac_of_peak"],
+                    "traffic": traffic, "flops_per_launch": dk["flops"],
+                    "avg_launch_ms": dk["ms"], "bytes_per_launch": dk["compulsory_bytes"],
+                    "hbm_GBps": dk["GBps"], "hbm_frac": dk["frac_of_hbm_peak"]}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "bytes_model": "compulsory",
+                    "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": dk["frac_of_peak"], "traffic": traffic,
+                    "bytes_per_launch": dk["compulsory_bytes"], "avg_launch_ms": dk["ms"]}
     if traffic:
         roofline["traffic_GBps"] = round(traffic / (dk["ms"] * 1e6), 1)
         roofline["traffic_counters"] = rec.get("counters", "FETCH_SIZE + WRITE_SIZE")
@@ -711,8 +786,9 @@ def main():
         "config": {"workload": cfg.name + (f" ({args.rows} rows)" if args.rows != "zipf" else "")
                    + ("" if args.preprocess == "forward" else ", preprocessing in the backward")
                    + ("" if args.check == "none" else f", index check {args.check}")
-                   + {"two_launch": "", "fused": ", long runs in one launch",
-                      "hot": ", hot rows' backward on the matrix cores"}[args.long]
+                   + {"two_launch": ", every long run on the chunk path",
+                      "fused": ", long runs in one launch",
+                      "hot": ""}[args.long]
                    + ("" if args.hot_rows == "on" else ", no hot rows in the forward")
                    + ("" if args.index == "int32" else ", int64 indices")
                    + ("" if args.tables == 32 else f", {args.tables} tables"),

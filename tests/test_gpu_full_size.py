@@ -13,7 +13,8 @@ The oracle cannot redo 84M lookups in seconds, so:
   of the GPU's run lengths compared element by element;
 - the forward is checked on 50,000 random bags spread over all tables;
 - the backward is checked on every long run (segment length >= 256: the
-  chunk path, its per-XCD schedule and work queue, and the apply) and on
+  hot rows' contraction where the benchmark takes it, the chunk path, its
+  per-XCD schedule and work queue, and the apply) and on
   short runs sampled evenly from each segment-length band (1, 2-4, 5-255),
   each row with every one of its lookups, against the oracle."""
 import numpy as np
@@ -75,12 +76,17 @@ def _backward_sample(counts, uk, rng, per_band=3000):
     return long_keys, bands
 
 
-@pytest.mark.parametrize("rows", ["zipf", "uniform"])
-def test_large_workload_full_size(rows):
-    """The benchmark's skewed batch, and the same shapes with uniform rows:
-    46.7M short runs, more than one round of the short-run kernel's grid
-    (65536 workgroups of four waves, 64 runs each), so its waves stride."""
+@pytest.mark.parametrize("rows,hot", [("zipf", True), ("zipf", False), ("uniform", True)],
+                         ids=["zipf_hot_backward", "zipf_chunks_only", "uniform"])
+def test_large_workload_full_size(rows, hot):
+    """The benchmark's skewed batch (with the hot rows' backward on the
+    matrix cores, as the benchmark runs it, and with every long run on the
+    chunk path, the library's default), and the same shapes with uniform
+    rows: 46.7M short runs, more than one round of the short-run kernel's
+    grid (65536 workgroups of four waves, 64 runs each), so its waves
+    stride."""
     import dataclasses
+    import bwd_tbe_pooled_amd as tbe
     cfg = LARGE if rows == "zipf" else dataclasses.replace(LARGE, index=("uniform",))
     print(f"\n[full] generating the T=32 B=131072 workload, {rows} rows", flush=True)
     batch = make_batch(cfg)
@@ -97,8 +103,12 @@ def test_large_workload_full_size(rows):
     assert np.unique(sample_bags // cfg.B).size == cfg.T
     need = np.unique(np.concatenate([sample_keys, keys[_mask(cfg.T * cfg.B, sample_bags)[bags]]]))
     Wrows, mrows = host_rows(W0, m0, need)
-    print("[full] running the library", flush=True)
-    r = run_library(cfg, batch, W, m, meta_in_forward=True, backward_meta=True, with_pos=False)
+    print(f"[full] running the library, hot rows' backward {'on' if hot else 'off'}", flush=True)
+    timer = tbe.Timer(4)
+    r = run_library(cfg, batch, W, m, meta_in_forward=True, backward_meta=True, with_pos=False,
+                    flags=tbe.TBE_FLAG_HOT_BACKWARD if hot else 0, timer=timer)
+    if hot and rows == "zipf":
+        assert timer.read()["bwd_hot"][1] == 1, "the hot rows' contraction did not run"
 
     # forward on sampled bags
     ob = oracle.forward_bags(cfg.D, cfg.dtype, batch.offsets, keys, batch.psw, Wrows, sample_bags,
