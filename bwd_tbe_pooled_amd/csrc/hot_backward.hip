@@ -233,21 +233,22 @@ void bwd_hot_kernel(
       }
       mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, 1));  // the column's other eight bags
       bad |= mbits >= 0x7f800000u;                             // Inf or NaN
-      if (mbits != 0u && mbits < 0x7f800000u) {
+      {
+        // the column's first nonzero tile sets its scale (largest then in
+        // [2^4, 2^5)); a later tile 2^12 above the scale moves it, and its
+        // accumulators follow before this tile's products. Selects, no branch
+        // but the rare rescale's.
         const int e = __builtin_amdgcn_frexp_expf(__uint_as_float(mbits));  // max in [2^(e-1), 2^e)
-        if (!gset) {
-          gsc = 5 - e;  // the column's first nonzero tile: largest in [2^4, 2^5)
-          gset = true;
-        } else if (e + gsc > 12) {
-          // a value 2^12 above the scale: the column is rescaled (its
-          // accumulators too, before this tile's products)
-          if (gh == 0) {
-            s_gdelta[gc] = (5 - e) - gsc;
-            s_resc[par] = 1;
-            gdirty = true;
-          }
-          gsc = 5 - e;
+        const bool nz = mbits != 0u && mbits < 0x7f800000u;
+        const bool resc = nz && gset && e + gsc > 12;
+        const int nsc = 5 - e;
+        if (resc && gh == 0) {
+          s_gdelta[gc] = nsc - gsc;
+          s_resc[par] = 1;
+          gdirty = true;
         }
+        gsc = nz && (!gset || resc) ? nsc : gsc;
+        gset = gset || nz;
       }
       if (gthr) {
         half8 h, l;
@@ -320,17 +321,17 @@ void bwd_hot_kernel(
 #pragma unroll
           for (int j = 0; j < 8; ++j) hm = fmaxf(hm, __builtin_fabsf(hx[mb][j]));
           hm = fmaxf(hm, __shfl_xor(hm, 32));
-          if (hm > 0.f) {
-            const int e = __builtin_amdgcn_frexp_expf(hm);
-            if (!(hm <= 3.402823466e38f)) bad = true;
-            else if (!hset[mb]) {
-              hsc[mb] = 1 - e;  // the slot's first nonzero tile: largest sum in [1, 2)
-              hset[mb] = true;
-            } else if (e + hsc[mb] > 12) {  // 2^12 above the scale: the slot is rescaled
-              dsc[mb] = (1 - e) - hsc[mb];
-              hsc[mb] = 1 - e;
-            }
-          }
+          // the slot's first nonzero tile sets its scale (largest sum then in
+          // [1, 2)); a later tile 2^12 above it moves the scale
+          const int e = __builtin_amdgcn_frexp_expf(hm);
+          const bool fin = hm <= 3.402823466e38f;
+          bad |= !fin;
+          const bool nz = hm > 0.f && fin;
+          const bool resc = nz && hset[mb] && e + hsc[mb] > 12;
+          const int nsc = 1 - e;
+          dsc[mb] = resc ? nsc - hsc[mb] : 0;
+          hsc[mb] = nz && (!hset[mb] || resc) ? nsc : hsc[mb];
+          hset[mb] = hset[mb] || nz;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
