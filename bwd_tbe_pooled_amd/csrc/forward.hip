@@ -380,8 +380,12 @@ void fwd_pool_hot_kernel(
         else if (q.w < 0) go = false;  // entries fill in order: an empty one ends the search
       };
       {  // the first probe of both, outside the loop: most searches end there
-        const int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
-        const int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
+        int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
+        int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
+        // all eight words as loaded, so that the compares are not turned
+        // into a second, dependent read of the words past the first
+        asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w));
+        asm volatile("" : "+v"(q1.x), "+v"(q1.y), "+v"(q1.z), "+v"(q1.w));
         look(q0, id[0], b0, go0, f0);
         look(q1, id[1], b1, go1, f1);
         b0 = (b0 + 1) & (kHotBuckets - 1);

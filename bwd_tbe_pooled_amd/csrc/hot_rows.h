@@ -66,8 +66,12 @@ __device__ __forceinline__ void hot_hash_find2(const int32_t* s_key, const uint8
     return q.x == x ? 0 : q.y == x ? 1 : q.z == x ? 2 : q.w == x ? 3 : -1;
   };
   {  // the first probe of both, without branches: most searches end there
-    const int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
-    const int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
+    int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
+    int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
+    // all eight words as loaded, so that the compares are not turned into a
+    // second, dependent read of the words past the first
+    asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w));
+    asm volatile("" : "+v"(q1.x), "+v"(q1.y), "+v"(q1.z), "+v"(q1.w));
     const int j0 = match(q0, r0), j1 = match(q1, r1);
     f0 = go0 && j0 >= 0 ? (int32_t)(b0 * 4 + j0) : -1;
     f1 = go1 && j1 >= 0 ? (int32_t)(b1 * 4 + j1) : -1;
