@@ -3,13 +3,14 @@ tbe_backward_adagrad with a caller workspace: the same metadata, weights,
 state and upstream gradient must give the same updated weights and state, bit
 for bit (the two run the same kernels). Two calls in a row on each path, the
 second on a smaller batch, so the second runs on scratch the first left
-behind; plus the refusal of a problem whose scratch would not fit."""
+behind; the same with the hot rows' contraction on; plus the refusal of a
+problem whose scratch would not fit."""
 import numpy as np
 import pytest
 import torch
 
 from tests.gpu_common import device_batch, fresh_params, make_desc
-from workloads import DEMO3, MEDIUM, SMALL_TABLE, make_batch
+from workloads import DEMO3, LARGE, MEDIUM, SMALL_TABLE, make_batch
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +26,7 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-def _step_pair(cfg, B, flags=0):
+def _step_pair(cfg, B, flags=0, timer=None):
     """Forward with metadata, then the backward through both entry points on
     copies of the same weights and state."""
     import bwd_tbe_pooled_amd as tbe
@@ -34,7 +35,7 @@ def _step_pair(cfg, B, flags=0):
     dev = device_batch(batch)
     N = batch.indices.size
     weighted = batch.psw is not None
-    desc = make_desc(c, flags=flags)
+    desc = make_desc(c, flags=flags, timer=timer)
     need = tbe.tbe_workspace_bytes(desc, N, weighted, tbe.TBE_OP_BACKWARD)
     assert 0 < need <= tbe.TBE_NOALLOC_SCRATCH_BYTES, (c.name, B, need)
     W, m = fresh_params(c, m0="uniform")
@@ -70,6 +71,22 @@ def test_noalloc_fused_long_matches():
     import bwd_tbe_pooled_amd as tbe
     print("\n[noalloc] fused long path", flush=True)
     _step_pair(MEDIUM, 2048, flags=tbe.TBE_FLAG_FUSED_LONG)
+
+
+@pytest.mark.parametrize("cfg,B1,B2", [
+    (MEDIUM, 4096, 1024),        # f16 weights, unweighted
+    (LARGE, 2048, 1024),         # the benchmark's tables: bf16, weighted
+], ids=["f16_unweighted", "bf16_weighted"])
+def test_noalloc_hot_backward_matches(cfg, B1, B2):
+    """The hot rows' contraction (TBE_FLAG_HOT_BACKWARD, the benchmark's
+    configuration): its plan, segment partials and flags come from the
+    scratch too."""
+    import bwd_tbe_pooled_amd as tbe
+    print(f"\n[noalloc] hot rows' backward, {cfg.name} B={B1} then B={B2}", flush=True)
+    for B in (B1, B2):
+        timer = tbe.Timer(4)
+        _step_pair(cfg, B, flags=tbe.TBE_FLAG_HOT_BACKWARD, timer=timer)
+        assert timer.read()["bwd_hot"][1] == 2, "the contraction did not run in both calls"
 
 
 def test_noalloc_refuses_a_problem_beyond_its_scratch():
