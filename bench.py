@@ -47,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 PEAK_F16_TFLOPS = 2500.0        # MI355X dense f16 matrix-core peak, 2.5 PFLOP/s
 HOT_K = 256                     # hot rows per table in the backward's contraction
-HOT_WGS = 512                   # workgroups the contraction aims at over all tables
+HOT_WGS = 512                   # workgroups the contraction runs over all tables (at most)
 HOT_TILE = 16                   # bags per tile of the contraction
 GATE = 0.6                      # target fraction of the HBM roofline
 FLUSH_BYTES = 1 << 30           # scratch written before each flushed step
@@ -187,7 +187,7 @@ def run_structure(torch, meta, cfg, N, S=256, C=256, hot=False):
         st.update(hot_runs=int(hot_run.sum().item()), hot_lookups=int(is_hot.sum().item()),
                   chunk_chunks=int(((sl[chunk_run] + C - 1) // C).sum().item()),
                   bags_chunk=int(bc.sum().item()),
-                  hot_nseg=max(1, min(-(-HOT_WGS // cfg.T), -(-tiles // 32))))
+                  hot_nseg=max(1, min(HOT_WGS // cfg.T, -(-tiles // 32))))
         del is_hot, bc
     del is_long, sb, bl, bs
     return st

@@ -513,8 +513,8 @@ Problem bound_problem(const tbe_desc* d, int64_t N, int weighted, int64_t sum, i
   p.hot_bwd_asked = (d->flags & TBE_FLAG_HOT_BACKWARD) != 0;
   derive_sizes(&p);
   p.sort_bits = 7;  // a group with fewer rows can take fewer, wider digits
-  // a group of T_g tables takes T_g * ceil(W / T_g) <= T + W - 1 segments in
-  // all (W = kHotBwdWorkgroups)
+  // a group of T_g tables takes T_g * max(1, floor(W / T_g)) <= T + W - 1
+  // segments in all (W = kHotBwdWorkgroups)
   if (p.hot_bwd) p.hot_nseg = (int32_t)((p.T + kHotBwdWorkgroups - 1 + p.T - 1) / p.T);
   if (path == TBE_PATH_SMALL_TABLE) {  // split partials: T_g * splits(T_g) at most
     int64_t parts = 0;

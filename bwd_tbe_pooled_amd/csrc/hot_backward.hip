@@ -423,10 +423,12 @@ bool hot_backward_eligible(const Problem& p) {
 }
 
 int32_t hot_backward_segments(const Problem& p) {
-  // about two workgroups per CU over all tables, and at least 32 tiles (512
-  // bags) per segment, so that small batches keep few partials
+  // two workgroups per CU over all tables, never more (a workgroup past the
+  // ones that fit at once would start only when others end, and double the
+  // time), and at least 32 tiles (512 bags) per segment, so that small
+  // batches keep few partials
   const int64_t tiles = ((int64_t)p.B + kHbBags - 1) / kHbBags;
-  int64_t nseg = (kHotBwdWorkgroups + p.T - 1) / p.T;
+  int64_t nseg = kHotBwdWorkgroups / p.T;
   const int64_t by_tiles = (tiles + 31) / 32;
   if (nseg > by_tiles) nseg = by_tiles;
   return (int32_t)(nseg < 1 ? 1 : nseg);

@@ -126,8 +126,8 @@ hipError_t launch_hot_plan(const Problem& p, const tbe_meta& meta, const int32_t
                            int32_t* hot_rows, int32_t* run_slot, int32_t* hot_min,
                            int32_t* hot_flag, hipStream_t s);
 bool hot_backward_eligible(const Problem& p);
-// workgroups the hot rows' contraction aims at over all tables: T * segments
-// <= T + kHotBwdWorkgroups - 1
+// workgroups the hot rows' contraction runs over all tables (two per CU of
+// an MI355X): T * segments <= max(T, kHotBwdWorkgroups)
 constexpr int kHotBwdWorkgroups = 512;
 int32_t hot_backward_segments(const Problem& p);
 hipError_t launch_bwd_hot(const Problem& p, const float* grad, const int32_t* indices,
