@@ -24,18 +24,22 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-@pytest.mark.parametrize("name,B", [("t16_e1m_d128_f16_b16k", 2048),
-                                    ("t32_e2m_d128_bf16_b128k", 1024),
-                                    ("small_t64_e64_d128_f16_b32k", 512)])
-def test_step_replayed_from_a_graph_matches_eager(name, B):
+@pytest.mark.parametrize("name,B,hot", [("t16_e1m_d128_f16_b16k", 2048, False),
+                                        ("t32_e2m_d128_bf16_b128k", 1024, False),
+                                        ("t32_e2m_d128_bf16_b128k", 1024, True),
+                                        ("small_t64_e64_d128_f16_b32k", 512, False)],
+                         ids=["f16", "bf16_weighted", "bf16_weighted_hot_backward", "small_table"])
+def test_step_replayed_from_a_graph_matches_eager(name, B, hot):
+    """With hot: the benchmark's configuration (TBE_FLAG_HOT_BACKWARD), whose
+    hot-row plan and contraction run inside the captured backward."""
     tbe = lib()
     batch = make_batch(WORKLOADS[name], B=B)
     cfg = batch.cfg
-    print(f"\n[graph] {cfg.name} B={cfg.B} N={batch.indices.size}", flush=True)
+    print(f"\n[graph] {cfg.name} B={cfg.B} N={batch.indices.size} hot={hot}", flush=True)
     dev = device_batch(batch)
     N = batch.indices.size
     weighted = dev["psw"] is not None
-    desc = make_desc(cfg)
+    desc = make_desc(cfg, flags=tbe.TBE_FLAG_HOT_BACKWARD if hot else 0)
     W, m = fresh_params(cfg)
     W0, m0 = W.clone(), m.clone()
     out = torch.empty((cfg.B, cfg.T * cfg.D), dtype=torch.float32, device="cuda")
