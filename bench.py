@@ -387,8 +387,8 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
 
     fwd_ms = avg["fwd_pool"] + avg.get("hot_plan", 0.0)   # the gather, and its hot-row plan
     pre_ms = avg["linearize"] + avg["sort"] + avg["rle_route"]
-    bwd_ms = (avg["bwd_short"] + avg.get("bwd_hot", 0.0) + avg["long_schedule"] + avg["bwd_long"]
-              + avg["bwd_apply"])
+    bwd_ms = (avg["bwd_short"] + avg.get("bwd_hot_plan", 0.0) + avg.get("bwd_hot", 0.0)
+              + avg["long_schedule"] + avg["bwd_long"] + avg["bwd_apply"])
     eff = effective_bytes(cfg, N, st["U"], st["n_chunks"], st["long_lookups"], weighted, st["n_long"])
     comp = compulsory_bytes(cfg, st, weighted)
     res = {
@@ -431,7 +431,7 @@ def measure_generic(torch, tbe, cfg, batch, args, scratch, *, headline=False):
                       "frac_of_peak": fr, "gathered_bytes": gathered[k],
                       "gathered_GBps": round(gathered[k] / (ms * 1e6), 1)}
     if avg.get("bwd_hot", 0.0) > 0 and "bwd_hot" in comp:
-        # the stage holds the hot-row plan (about 0.03 ms) and the contraction
+        # the contraction alone (its plan is the bwd_hot_plan stage)
         ms = avg["bwd_hot"]
         fl = hot_flops(cfg, st, weighted)
         gb, fr = frac(comp["bwd_hot"], ms)

@@ -38,7 +38,7 @@ TBE_PATH_GENERIC, TBE_PATH_SMALL_TABLE = 0, 1
  TBE_OP_BACKWARD_SELF) = range(5)
 STAGES = ["fwd_pool", "linearize", "sort", "rle_route", "bwd_short", "bwd_long", "bwd_apply",
           "small_fwd", "small_bwd", "small_apply", "validate", "long_schedule", "small_count",
-          "bwd_hot", "hot_plan"]
+          "bwd_hot", "hot_plan", "bwd_hot_plan"]
 TBE_NUM_STAGES = len(STAGES)
 TBE_NOALLOC_SCRATCH_BYTES = 64 << 20   # built-in scratch of tbe_backward_adagrad_noalloc
 META_FIELDS = ["counts", "run_keys", "run_offsets", "sorted_pos", "sorted_bag", "sorted_psw",

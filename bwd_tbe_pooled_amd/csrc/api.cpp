@@ -444,9 +444,11 @@ tbe_status backward_impl(const tbe_desc* desc, const Problem& p, void* W, float*
     hot.hot_flag = hb_flag;
     hot.parts = hb_parts;
     hot.nseg = p.hot_nseg;
-    timer_begin(desc->timer, TBE_STAGE_BWD_HOT, s);
+    timer_begin(desc->timer, TBE_STAGE_BWD_HOT_PLAN, s);
     TBE_TRY_HIP(launch_hot_plan(p, m, tinfo, 256, hb_rows, at<int32_t>(ws, L.hb_run_slot),
                                 at<int32_t>(ws, L.hb_min), hb_flag, s));
+    timer_end(desc->timer, TBE_STAGE_BWD_HOT_PLAN, s);
+    timer_begin(desc->timer, TBE_STAGE_BWD_HOT, s);
     TBE_TRY_HIP(launch_bwd_hot(p, grad_out, indices, offsets, psw, hb_rows, tinfo, hb_parts,
                                hb_flag, s));
     timer_end(desc->timer, TBE_STAGE_BWD_HOT, s);

@@ -142,10 +142,12 @@ typedef enum {
     TBE_STAGE_VALIDATE = 10,    /* TBE_FLAG_VALIDATE check                    */
     TBE_STAGE_LONG_SCHEDULE = 11, /* per-XCD order of the long-run chunks     */
     TBE_STAGE_SMALL_COUNT = 12, /* small-table per-bag row counts             */
-    TBE_STAGE_BWD_HOT = 13,     /* hot rows: plan + matrix-core contraction   */
+    TBE_STAGE_BWD_HOT = 13,     /* hot rows: the matrix-core contraction      */
     TBE_STAGE_HOT_PLAN = 14,    /* the forward's hot-row plan (after the
                                    transpose, when the hot rows are on)       */
-    TBE_NUM_STAGES = 15
+    TBE_STAGE_BWD_HOT_PLAN = 15, /* the backward's hot-row plan (under
+                                   TBE_FLAG_HOT_BACKWARD)                     */
+    TBE_NUM_STAGES = 16
 } tbe_stage;
 
 typedef struct tbe_timer tbe_timer;   /* opaque; see tbe_timer_create */
