@@ -260,8 +260,7 @@ void fwd_pool_hot_kernel(
   constexpr int HU = kHotUnroll<(int)sizeof(HRAW)>;
   // hot rows in slots 0..K-1, then slot K, a row of zeros that padded lanes read
   __shared__ __align__(16) unsigned char s_rows[kHotBytes];
-  __shared__ __align__(16) int32_t s_key[kHotHash];
-  __shared__ uint8_t s_slotof[kHotHash];
+  __shared__ __align__(16) int32_t s_key[kHotHash];  // packed hash: row << 8 | slot
   __shared__ int32_t s_cidx[kHotWaves][kHotStage];   // cold lookups' rows, in lookup order
   __shared__ uint8_t s_hslot[kHotWaves][kHotStage];  // hot lookups' LDS slots, in lookup order
   // weights: cold lookups from the front, hot lookups from the back
@@ -300,7 +299,7 @@ void fwd_pool_hot_kernel(
   // hash of the table's hot rows, then the rows themselves
   for (int i = threadIdx.x; i < kHotHash; i += kHotThreads) s_key[i] = -1;
   __syncthreads();
-  hot_hash_insert(s_key, s_slotof, hot_rows + (int64_t)t * K, K);
+  hot_hash_insert_packed(s_key, hot_rows + (int64_t)t * K, K);
   {
     const int n16 = K * row_bytes / 16;  // 16-byte pieces of the hot rows in memory
     for (int q = threadIdx.x; q < n16; q += kHotThreads) {
@@ -369,45 +368,9 @@ void fwd_pool_hot_kernel(
       }
       id[r] = idx;
     }
-    // both lookups probe the hash together, a bucket per LDS read
-    {
-      uint32_t b0 = hot_bucket(id[0]), b1 = hot_bucket(id[1]);
-      bool go0 = valid[0], go1 = valid[1];
-      int32_t f0 = -1, f1 = -1;
-      auto look = [](const int4& q, int32_t x, uint32_t b, bool& go, int32_t& f) {
-        const int j = q.x == x ? 0 : q.y == x ? 1 : q.z == x ? 2 : q.w == x ? 3 : -1;
-        if (j >= 0) { f = (int32_t)(b * 4 + j); go = false; }
-        else if (q.w < 0) go = false;  // entries fill in order: an empty one ends the search
-      };
-      {  // the first probe of both, outside the loop: most searches end there
-        int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
-        int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
-        // all eight words as loaded, so that the compares are not turned
-        // into a second, dependent read of the words past the first
-        asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w));
-        asm volatile("" : "+v"(q1.x), "+v"(q1.y), "+v"(q1.z), "+v"(q1.w));
-        look(q0, id[0], b0, go0, f0);
-        look(q1, id[1], b1, go1, f1);
-        b0 = (b0 + 1) & (kHotBuckets - 1);
-        b1 = (b1 + 1) & (kHotBuckets - 1);
-      }
-      while (go0 || go1) {  // a full bucket: the search goes on in the next
-        const int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
-        const int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
-        if (go0) {
-          look(q0, id[0], b0, go0, f0);
-          b0 = (b0 + 1) & (kHotBuckets - 1);
-        }
-        if (go1) {
-          look(q1, id[1], b1, go1, f1);
-          b1 = (b1 + 1) & (kHotBuckets - 1);
-        }
-      }
-      const int32_t q0 = s_slotof[f0 < 0 ? 0 : f0];
-      const int32_t q1 = s_slotof[f1 < 0 ? 0 : f1];
-      hs[0] = f0 < 0 ? -1 : q0;
-      hs[1] = f1 < 0 ? -1 : q1;
-    }
+    // both lookups probe the hash together, a bucket per LDS read that also
+    // holds the slot
+    hot_hash_find2_packed(s_key, id[0], valid[0], id[1], valid[1], hs[0], hs[1]);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       cm[r] = __ballot(valid[r] && hs[r] < 0);
@@ -702,7 +665,8 @@ void choose_hot(Problem* p) {
   if (p->no_hot || p->path != TBE_PATH_GENERIC || row % 16 != 0 || row_shape(p->D, hot_max_v(wbytes)).P != 1)
     return;
   // cold rows are read at 32-bit offsets below 2^31, rows numbered in 24 bits
-  if (p->max_rows >= (int64_t(1) << 24) || p->max_rows * row >= (int64_t(1) << 31)) return;
+  // (below 2^24 - 1: the hash packs row << 8 | slot in 32 bits)
+  if (p->max_rows >= (int64_t(1) << 24) - 1 || p->max_rows * row >= (int64_t(1) << 31)) return;
   const int64_t lrow = p->D * (p->wdtype == TBE_BF16 ? kHotLdsElem<bf16_t> : wbytes);
   const int64_t k = std::min<int64_t>(256, kHotBytes / lrow - 1);  // and the zero row
   if (k < 16 || p->B < 1) return;

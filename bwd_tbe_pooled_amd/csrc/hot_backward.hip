@@ -79,8 +79,7 @@ void bwd_hot_kernel(
     float* __restrict__ hot_parts, int32_t* __restrict__ hot_flag, int32_t T, int32_t B,
     int64_t ld, int32_t seg_bags, int64_t N) {
   constexpr int D = NT * 32;
-  __shared__ __align__(16) int32_t s_key[kHotHash];
-  __shared__ uint8_t s_slotof[kHotHash];
+  __shared__ __align__(16) int32_t s_key[kHotHash];  // packed hash: row << 8 | slot
   __shared__ __align__(16) float s_H[kHotMaxK][kHbHStride];   // weight sums
   __shared__ __align__(16) _Float16 s_gb[2][NT][kWave][8];    // [hi, lo][nt][lane][j]
   __shared__ int32_t s_gsc[D];    // per column: scale exponent, for the unscaling
@@ -108,7 +107,7 @@ void bwd_hot_kernel(
   }
   for (int d = threadIdx.x; d < D; d += kHbThreads) s_gdelta[d] = 0;
   __syncthreads();
-  hot_hash_insert(s_key, s_slotof, hr, kHotMaxK);
+  hot_hash_insert_packed(s_key, hr, kHotMaxK);
   if (threadIdx.x < kHotMaxK && hr[threadIdx.x] >= 0) atomicMax(&s_nhot, (int)threadIdx.x + 1);
   __syncthreads();
   const int n_hot = s_nhot;  // slots 0..n_hot-1 are taken
@@ -187,7 +186,9 @@ void bwd_hot_kernel(
     }
   };
   auto slot_of = [&](int32_t idx) {
-    return hot_hash_find(s_key, s_slotof, (uint32_t)idx < Et ? idx : 0);
+    int s0, s1;
+    hot_hash_find2_packed(s_key, (uint32_t)idx < Et ? idx : 0, true, 0, false, s0, s1);
+    return s0;
   };
 
   // H cells this thread added to in the last tile, cleared before the next
@@ -220,8 +221,8 @@ void bwd_hot_kernel(
     static_assert(kHbAhead == 2, "two staged lookups per thread");
     {
       const bool v0 = o_cur.q0 + lk < o_cur.q1, v1 = o_cur.q0 + lk + 16 < o_cur.q1;
-      hot_hash_find2(s_key, s_slotof, (uint32_t)dat.idx[0] < Et ? dat.idx[0] : 0, v0,
-                     (uint32_t)dat.idx[1] < Et ? dat.idx[1] : 0, v1, zslot[0], zslot[1]);
+      hot_hash_find2_packed(s_key, (uint32_t)dat.idx[0] < Et ? dat.idx[0] : 0, v0,
+                            (uint32_t)dat.idx[1] < Et ? dat.idx[1] : 0, v1, zslot[0], zslot[1]);
     }
     {
       // the largest |g| as the largest bit pattern (finite values only)
@@ -416,10 +417,11 @@ void bwd_hot_kernel(
 // MI355X the plan and the contraction take 1.46 ms and the remaining long
 // runs' chunks 0.43 ms, against 2.04 ms for the chunk path alone.
 bool hot_backward_eligible(const Problem& p) {
-  // 32-bit byte offsets: the lookups below 2^29, a 16-row gradient tile below 2^31 bytes
+  // 32-bit byte offsets: the lookups below 2^29, a 16-row gradient tile below 2^31 bytes;
+  // the packed hash: tables of fewer than 2^24 - 1 rows
   return p.hot_bwd_asked && !p.no_hot && p.path == TBE_PATH_GENERIC && p.wdtype != TBE_F32 &&
          p.D % 32 == 0 && p.D <= 128 && p.B >= 1 && p.cap_long > 0 && p.N < (int64_t(1) << 29) &&
-         p.ld < (int64_t(1) << 25);
+         p.ld < (int64_t(1) << 25) && p.max_rows < (int64_t(1) << 24) - 1;
 }
 
 int32_t hot_backward_segments(const Problem& p) {

@@ -9,7 +9,9 @@ weighted bf16 and unweighted f16, rows of 32, 64, 96 and 128, more long runs
 than the 256 hot slots, runs tied at the cut (no hot row), a ragged last
 segment, bags longer than the lookups staged ahead, and scales moved by later
 tiles: one gradient far above its column's scale, and every segment's first
-tile 1e-6 times smaller than the rest."""
+tile 1e-6 times smaller than the rest; hot rows above 2^23 in a table of
+2^24 - 2 rows (the largest the packed row-and-slot hash takes), and a table
+of 2^24 - 1 rows, which leaves every hot run to the chunk path."""
 import dataclasses
 
 import numpy as np
@@ -31,7 +33,7 @@ def _need_gpu():
     import bwd_tbe_pooled_amd  # noqa: F401
 
 
-def _check(cfg, batch, S=0, C=0, label=""):
+def _check(cfg, batch, S=0, C=0, label="", hot=True):
     import bwd_tbe_pooled_amd as tbe
     print(f"\n[hotbwd] {label or cfg.name} T={cfg.T} B={cfg.B} D={cfg.D} {cfg.dtype} "
           f"N={batch.indices.size} S={S or 256}", flush=True)
@@ -46,7 +48,10 @@ def _check(cfg, batch, S=0, C=0, label=""):
     pre, _, bw = oracle_all(cfg, batch, Wrows, mrows, uk, S or 256, C or 256)
     assert_rows_match(cfg, W, m, pre["run_keys"], bw["w_new"], bw["m_new"], label or cfg.name)
     assert_untouched_unchanged(W0, W, m0, m, uk)
-    assert timer.read()["bwd_hot"][1] == 1, "the hot rows' contraction did not run"
+    if hot:
+        assert timer.read()["bwd_hot"][1] == 1, "the hot rows' contraction did not run"
+    else:
+        assert timer.read()["bwd_hot"][1] == 0, "the hot rows' contraction ran"
     return pre
 
 
@@ -147,3 +152,27 @@ def test_bags_longer_than_staged():
                  bag=("uniform", 150, 250), index=("zipf", 1.1), weighted=True,
                  preprocess_in_forward=True, seed=91)
     _check(cfg, make_batch(cfg), S=16, C=64)
+
+
+def test_hot_rows_near_the_packed_hash_limit():
+    """A table of 2^24 - 2 rows (its hot rows' packed entries row << 8 | slot
+    reach the sign bit) beside a small one: the contraction runs."""
+    cfg = Config("hot_rows_2p24m2", T=2, B=4096, D=32, rows=((1 << 24) - 2, 3000), dtype="bf16",
+                 bag=("poisson", 20.0), index=("zipf", 1.2), weighted=True,
+                 preprocess_in_forward=True, seed=97)
+    batch = make_batch(cfg)
+    pre = _check(cfg, batch, S=32, C=64)
+    keys = pre["run_keys"].astype(np.int64)
+    sl = np.diff(pre["run_offsets"].astype(np.int64))
+    long_t0 = keys[(sl >= 32) & (keys < cfg.rows[0])]
+    assert (long_t0 >= (1 << 23)).any(), "no long run of table 0 above 2^23"
+    assert long_t0.size <= 256  # every one of them hot
+
+
+def test_table_too_large_for_the_packed_hash_falls_back():
+    """A table of 2^24 - 1 rows: the flag is ignored and the chunk path takes
+    every long run, with the same result."""
+    cfg = Config("hot_rows_2p24m1", T=2, B=4096, D=32, rows=((1 << 24) - 1, 3000), dtype="bf16",
+                 bag=("poisson", 20.0), index=("zipf", 1.2), weighted=True,
+                 preprocess_in_forward=True, seed=98)
+    _check(cfg, make_batch(cfg), S=32, C=64, hot=False)
