@@ -101,8 +101,9 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
                                         transpose gathers every row through
                                         the plain gather (by default it reads
                                         the rows of each table's longest runs
-                                        from LDS), and TBE_FLAG_HOT_BACKWARD
-                                        is ignored */
+                                        from LDS, when every table has fewer
+                                        than 2^24 - 1 rows), and
+                                        TBE_FLAG_HOT_BACKWARD is ignored */
 #define TBE_FLAG_HOT_BACKWARD  0x20u /* the backward sums the gradients of
                                         each table's up to 256 longest runs
                                         as one matrix-core contraction that
@@ -110,11 +111,12 @@ typedef enum { TBE_F32 = 0, TBE_F16 = 1, TBE_BF16 = 2 } tbe_dtype;
                                         1, the compensated f16 hi/lo
                                         contraction; f16/bf16 weights, D a
                                         multiple of 32 up to 128, fewer than
-                                        2^29 lookups), the other long runs
-                                        on the chunk path. Opt-in; at the
-                                        Zipf-skewed batch on gfx950 the
-                                        faster of the two (0.2 ms a step at
-                                        32 tables) */
+                                        2^29 lookups, every table fewer than
+                                        2^24 - 1 rows; otherwise ignored),
+                                        the other long runs on the chunk
+                                        path. Opt-in; at the Zipf-skewed
+                                        batch on gfx950 the faster of the
+                                        two (0.3 ms a step at 32 tables) */
 
 /* Bits OR-ed into *tbe_desc.error_flags under TBE_FLAG_CHECK. */
 #define TBE_ERROR_INDEX 0x1u   /* some index was outside its table */
