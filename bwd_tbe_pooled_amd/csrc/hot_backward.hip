@@ -205,6 +205,12 @@ void bwd_hot_kernel(
   load_data(b_begin, o_cur, dat);
   load_off(b_begin + kHbBags, o_nxt);
   for (int32_t b0 = b_begin; b0 < b_end; b0 += kHbBags, par ^= 1) {
+    // The build issues before the contraction on a SIMD that holds waves of
+    // both phases (the two workgroups of a CU drift apart): the next tile's
+    // loads and the LDS atomics start sooner, and the matrix-core work of the
+    // other workgroup fills the gaps (1.36 -> 1.30 ms on the Zipf-skewed
+    // batch; raising the contraction instead gave 1.31 ms).
+    __builtin_amdgcn_s_setprio(1);
     // --- build: the last tile's H cells cleared, H[slot][bag] += weight of
     //     each hot lookup, the gradients scaled and split into the B operands
     if (zcol) {
@@ -292,6 +298,7 @@ void bwd_hot_kernel(
     __syncthreads();
 
     // --- the contraction ----------------------------------------------------
+    __builtin_amdgcn_s_setprio(0);
     if (mine) {
       float hx[2][8];
 #pragma unroll
