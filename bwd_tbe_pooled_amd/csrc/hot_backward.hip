@@ -421,7 +421,7 @@ void bwd_hot_kernel(
 }  // namespace
 
 // Opt-in (TBE_FLAG_HOT_BACKWARD): at T=32, B=131072, D=128 bf16 on one
-// MI355X the plan and the contraction take 1.36 ms and the remaining long
+// MI355X the plan and the contraction take about 1.3 ms and the remaining long
 // runs' chunks 0.43 ms, against 2.03 ms for the chunk path alone.
 bool hot_backward_eligible(const Problem& p) {
   // 32-bit byte offsets: the lookups below 2^29, a 16-row gradient tile below 2^31 bytes;
