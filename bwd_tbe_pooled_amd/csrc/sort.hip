@@ -236,6 +236,9 @@ __global__ __launch_bounds__(kThreads, WITH_POS ? 3 : 4) void sort_downsweep_ker
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 
   for (int d = threadIdx.x; d < 4 * 256; d += kThreads) (&wave_hist[0][0])[d] = 0;
+  // The tile's loads issue ahead of the ranking of the workgroups already
+  // resident (1.596 -> 1.582 ms for the three passes at T=32, B=131072).
+  __builtin_amdgcn_s_setprio(1);
 
   int32_t key[kItems], pos[kItems], bag[kItems], rank[kItems];
   float w[kItems];
@@ -249,6 +252,7 @@ __global__ __launch_bounds__(kThreads, WITH_POS ? 3 : 4) void sort_downsweep_ker
     if constexpr (!FIRST) bag[r] = ok ? bag_in[j] : 0;
     if constexpr (WEIGHTED) w[r] = ok ? psw_in[j] : 0.f;
   }
+  __builtin_amdgcn_s_setprio(0);
   if (clamp_rows) {
     // Bounds check fused into the first pass: a row outside its table sorts
     // (and is later read and updated) as row 0, and the call reports it.
