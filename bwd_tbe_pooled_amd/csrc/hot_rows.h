@@ -21,93 +21,16 @@ __device__ __forceinline__ uint32_t hot_bucket(int32_t row) {
   return ((uint32_t)row * 0x9E3779B1u) >> 24;
 }
 
-// Fill the hash (s_key[kHotHash], 16-byte aligned, and s_slotof) from
-// rows[0..K), entries < 0 being empty slots. Called by every thread of the
-// workgroup between two barriers: s_key must be all -1 before (the caller
-// clears it and synchronises), and is complete after the caller's next
-// barrier.
-__device__ __forceinline__ void hot_hash_insert(int32_t* s_key, uint8_t* s_slotof,
-                                                const int32_t* __restrict__ rows, int K) {
-  for (int k = threadIdx.x; k < K; k += blockDim.x) {
-    const int32_t r = rows[k];
-    if (r < 0) continue;
-    uint32_t h = hot_bucket(r) * 4;
-    for (;;) {  // at most 256 rows in 1024 entries: a free entry exists
-      if (atomicCAS(&s_key[h], -1, r) == -1) {
-        s_slotof[h] = (uint8_t)k;
-        break;
-      }
-      h = (h + 1) & (kHotHash - 1);
-    }
-  }
-}
-
-// Slot of `row` among the hot rows, or -1.
-__device__ __forceinline__ int hot_hash_find(const int32_t* s_key, const uint8_t* s_slotof,
-                                             int32_t row) {
-  uint32_t b = hot_bucket(row);
-  for (;;) {
-    const int4 q = reinterpret_cast<const int4*>(s_key)[b];
-    const int j = q.x == row ? 0 : q.y == row ? 1 : q.z == row ? 2 : q.w == row ? 3 : -1;
-    if (j >= 0) return s_slotof[b * 4 + j];
-    if (q.w < 0) return -1;  // entries fill in order: an empty one ends the search
-    b = (b + 1) & (kHotBuckets - 1);
-  }
-}
-
-// Slots of two rows (-1: not hot, or `go` false), their probes interleaved
-// so that both searches wait on one LDS round trip per step.
-__device__ __forceinline__ void hot_hash_find2(const int32_t* s_key, const uint8_t* s_slotof,
-                                               int32_t r0, bool go0, int32_t r1, bool go1,
-                                               int& slot0, int& slot1) {
-  uint32_t b0 = hot_bucket(r0), b1 = hot_bucket(r1);
-  int32_t f0 = -1, f1 = -1;  // entries that hold the rows
-  auto match = [](const int4& q, int32_t x) {
-    return q.x == x ? 0 : q.y == x ? 1 : q.z == x ? 2 : q.w == x ? 3 : -1;
-  };
-  {  // the first probe of both, without branches: most searches end there
-    int4 q0 = reinterpret_cast<const int4*>(s_key)[b0];
-    int4 q1 = reinterpret_cast<const int4*>(s_key)[b1];
-    // all eight words as loaded, so that the compares are not turned into a
-    // second, dependent read of the words past the first
-    asm volatile("" : "+v"(q0.x), "+v"(q0.y), "+v"(q0.z), "+v"(q0.w));
-    asm volatile("" : "+v"(q1.x), "+v"(q1.y), "+v"(q1.z), "+v"(q1.w));
-    const int j0 = match(q0, r0), j1 = match(q1, r1);
-    f0 = go0 && j0 >= 0 ? (int32_t)(b0 * 4 + j0) : -1;
-    f1 = go1 && j1 >= 0 ? (int32_t)(b1 * 4 + j1) : -1;
-    go0 = go0 && j0 < 0 && q0.w >= 0;  // entries fill in order: an empty one ends the search
-    go1 = go1 && j1 < 0 && q1.w >= 0;
-  }
-  while (go0 || go1) {  // a full bucket: the search goes on in the next
-    if (go0) {
-      b0 = (b0 + 1) & (kHotBuckets - 1);
-      const int4 q = reinterpret_cast<const int4*>(s_key)[b0];
-      const int j = match(q, r0);
-      if (j >= 0) f0 = (int32_t)(b0 * 4 + j);
-      go0 = j < 0 && q.w >= 0;
-    }
-    if (go1) {
-      b1 = (b1 + 1) & (kHotBuckets - 1);
-      const int4 q = reinterpret_cast<const int4*>(s_key)[b1];
-      const int j = match(q, r1);
-      if (j >= 0) f1 = (int32_t)(b1 * 4 + j);
-      go1 = j < 0 && q.w >= 0;
-    }
-  }
-  const int32_t s0 = s_slotof[f0 < 0 ? 0 : f0];
-  const int32_t s1 = s_slotof[f1 < 0 ? 0 : f1];
-  slot0 = f0 < 0 ? -1 : s0;
-  slot1 = f1 < 0 ? -1 : s1;
-}
-
-// Packed form, for tables of fewer than 2^24 - 1 rows: an entry is
-// row << 8 | slot, so the read of a bucket yields the slot as well, with no
-// second, dependent read. With rk = row << 8, the entry minus rk (mod 2^32) is
-// the slot (below 256) for the row's own entry, and at least 256 for another
-// row's entry (rows differ by a nonzero multiple of 256 below 2^32) and for an
-// empty one (-1 minus rk is at least 511 when row <= 2^24 - 2). Rows of
-// rows[0..K) must be below 2^24 - 1; the entries are filled like the unpacked
-// hash's.
+// The hash (s_key[kHotHash], 16-byte aligned) packs each entry as
+// row << 8 | slot, for tables of fewer than 2^24 - 1 rows, so the read of a
+// bucket yields the slot as well, with no second, dependent read. With
+// rk = row << 8, the entry minus rk (mod 2^32) is the slot (below 256) for the
+// row's own entry, and at least 256 for another row's entry (rows differ by a
+// nonzero multiple of 256 below 2^32) and for an empty one (-1 minus rk is at
+// least 511 when row <= 2^24 - 2). Filled from rows[0..K) (entries < 0 being
+// empty slots, the others below 2^24 - 1) by every thread of the workgroup
+// between two barriers: s_key must be all -1 before (the caller clears it and
+// synchronises), and is complete after the caller's next barrier.
 __device__ __forceinline__ void hot_hash_insert_packed(int32_t* s_key,
                                                        const int32_t* __restrict__ rows, int K) {
   for (int k = threadIdx.x; k < K; k += blockDim.x) {
